@@ -1,0 +1,287 @@
+#!/usr/bin/env python3
+"""Benchmark of the linear-attention hot path on one MI355X.
+
+Default workload (the headline): causal linear attention, bf16 inputs with fp32
+accumulation and state, B=2 H=16 N=32768 D=M=64 — one step is one full
+``linattn_causal_fwd`` over the batch (every kernel of the causal path).
+Other workloads (``--workload``): noncausal_long, decode (prefill + 1024
+single-token steps on 256x16 states), deltanet, causal_mid.
+
+Prints ONE JSON line.  Inputs are synthetic (seeded N(0,1), the recipe of the
+synth module), copied to the GPU before the timed region.  Timing: W untimed
+warm-up steps, then K timed steps bracketed by a device synchronisation;
+per-launch kernel time comes from HIP events recorded on the stream the library
+launches on (torch's current stream, passed to the C ABI).  The CPU baseline is
+the oracle timed on the host cores on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector / matrix, TFLOP/s
+METRIC = "causal linear-attn B·H·N tokens/s at N=32k, D=64; % of HBM/MFMA roofline"
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def source_hash() -> str:
+    """Hash of the kernel sources: counter figures taken from another source are stale."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "weight_recurrences_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp", ".cpp")):
+            h.update(name.encode())
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str):
+    """HBM bytes per launch from a committed counter summary, if it matches the
+    current kernel sources (else None).  The summary states FETCH/WRITE bytes per
+    path launch already scaled by the copy-kernel calibration factor."""
+    path = os.path.join(PROFILE_DIR, f"{workload}_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"source_hash:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def time_oracle(workload, inputs, budget_s: float = 20.0):
+    """The oracle as it stands, on the host cores, on a bounded sample."""
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    oracle.set_threads(threads)
+    w = workload
+    if w.name == "decode":
+        q, k, v, sq, sk, sv = inputs
+        nh = w.B * w.H
+        # sample: all states, prefill + the first T steps
+        t0 = time.perf_counter()
+        _, S, z = oracle.causal(q, k, v, want_output=False)
+        T = 0
+        while T < w.steps:
+            oracle.decode_step(sq[T], sk[T], sv[T], S, z)
+            T += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+        # prefill work counts as nh*N head-tokens, each step as nh head-tokens
+        return {"value": nh * (w.N + T) / dt, "unit": "head-tokens/s", "cores": threads, "kind": "oracle",
+                "sample": f"prefill {w.N} tokens + {T} of {w.steps} steps on all {nh} states, {dt:.1f} s, "
+                          f"{cpu_model()}"}
+    heads = w.B * w.H
+    if w.name == "deltanet":
+        q, k, v, beta = inputs
+    else:
+        q, k, v = inputs[:3]
+    # time one head first, then choose the sample size from it
+    t0 = time.perf_counter()
+    if w.name == "deltanet":
+        oracle.deltanet(q[:1, :1], k[:1, :1], v[:1, :1], beta[:1, :1])
+    elif w.name.startswith("noncausal"):
+        oracle.noncausal(q[:1, :1], k[:1, :1], v[:1, :1])
+    else:
+        oracle.causal(q[:1, :1], k[:1, :1], v[:1, :1])
+    one = time.perf_counter() - t0
+    nb = max(1, min(w.B, int(budget_s / max(one * w.H / threads, 1e-6))))
+    t0 = time.perf_counter()
+    if w.name == "deltanet":
+        oracle.deltanet(q[:nb], k[:nb], v[:nb], beta[:nb])
+    elif w.name.startswith("noncausal"):
+        oracle.noncausal(q[:nb], k[:nb], v[:nb])
+    else:
+        oracle.causal(q[:nb], k[:nb], v[:nb])
+    dt = time.perf_counter() - t0
+    toks = nb * w.H * w.N
+    return {"value": toks / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{nb} of {w.B} batch entries ({nb * w.H} of {heads} heads, all {w.N} tokens), "
+                      f"{dt:.1f} s, {cpu_model()}"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="causal_long",
+                    choices=["causal_long", "noncausal_long", "decode", "deltanet", "causal_mid"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--oracle-budget", type=float, default=20.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the per-(batch, head) problems shard across GPUs without communication; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import weight_recurrences_amd as la
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(3)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    wname = "causal_long" if args.workload == "noncausal_long" else args.workload
+    w = synth.WORKLOADS[wname]
+    inputs = synth.workload_inputs(w)
+    K, Wm = args.steps, args.warmup
+
+    def events(n):
+        return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+    if args.workload in ("causal_long", "causal_mid", "noncausal_long"):
+        q, k, v = (t.to(dev) for t in inputs)
+        o = torch.empty(w.B, w.H, w.N, w.M, dtype=w.dtype, device=dev)
+        if args.workload == "noncausal_long":
+            ws = torch.empty(max(1, la.noncausal_workspace_bytes(w.B, w.H, w.N, w.D, w.M, w.dtype)),
+                             dtype=torch.uint8, device=dev)
+            step = lambda: la.noncausal(q, k, v, out=o, workspace=ws)
+            kernel = "linattn_noncausal_fwd (block_state + state_scan + noncausal_apply)"
+        else:
+            ws = torch.empty(max(1, la.causal_workspace_bytes(w.B, w.H, w.N, w.D, w.M, w.dtype)),
+                             dtype=torch.uint8, device=dev)
+            step = lambda: la.causal(q, k, v, out=o, workspace=ws)
+            kernel = "linattn_causal_fwd (block_state + state_scan + causal_sweep)"
+        units = w.B * w.H * w.N                      # tokens per step
+        es = torch.tensor([], dtype=w.dtype).element_size()
+        alg_bytes = units * (2 * w.D + 2 * w.M) * es  # read q, k, v; write o
+        unit = "tokens/s"
+        launches_per_step = 1
+    elif args.workload == "decode":
+        pq, pk, pv, sq, sk, sv = inputs
+        pq, pk, pv = pq.to(dev), pk.to(dev), pv.to(dev)
+        sq, sk, sv = sq.to(dev), sk.to(dev), sv.to(dev)
+        S0, z0 = la.causal(pq, pk, pv, output=False)
+        S, z = S0.clone(), z0.clone()
+        o = torch.empty(w.steps, w.B, w.H, w.M, dtype=w.dtype, device=dev)
+
+        def step():
+            for t in range(w.steps):
+                la.decode_step(sq[t], sk[t], sv[t], S, z, out=o[t])
+        kernel = "linattn_decode_step (decode_step_kernel)"
+        units = w.B * w.H * w.steps                  # head-tokens per step (1024 decode steps)
+        es = 2
+        per_head_token = 2 * w.D * w.M * 4 + 2 * w.D * 4 + (2 * w.D + 2 * w.M) * es
+        alg_bytes = w.B * w.H * per_head_token       # per launch (one decode step)
+        unit = "head-tokens/s"
+        launches_per_step = w.steps
+    else:  # deltanet
+        q, k, v, beta = (t.to(dev) for t in inputs)
+        o = torch.empty(w.B, w.H, w.N, w.M, dtype=w.dtype, device=dev)
+        step = lambda: la.deltanet(q, k, v, beta, out=o)
+        kernel = "deltanet_fwd (deltanet_kernel)"
+        units = w.B * w.H * w.N
+        alg_bytes = units * ((2 * w.D + 2 * w.M) * 4 + 4)
+        unit = "tokens/s"
+        launches_per_step = 1
+
+    for _ in range(Wm):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: K steps; HIP events around every launch of the measured path.
+    ev = events(2 * K * launches_per_step) if launches_per_step == 1 else None
+    t_start, t_end = events(2)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    if launches_per_step == 1:
+        for i in range(K):
+            ev[2 * i].record(stream)
+            step()
+            ev[2 * i + 1].record(stream)
+    else:
+        # decode: per-launch events on a sample of the steps inside the loop
+        per = []
+        for i in range(K):
+            for t in range(w.steps):
+                if t % 64 == 0:
+                    a, b = events(2)
+                    a.record(stream)
+                    la.decode_step(sq[t], sk[t], sv[t], S, z, out=o[t])
+                    b.record(stream)
+                    per.append((a, b))
+                else:
+                    la.decode_step(sq[t], sk[t], sv[t], S, z, out=o[t])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    if launches_per_step == 1:
+        launch_ms = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(K)) / K
+    else:
+        launch_ms = sum(a.elapsed_time(b) for a, b in per) / len(per)
+
+    ms_per_step = total_ms / K
+    value = units * K / (total_ms / 1e3)
+    achieved = alg_bytes / (launch_ms / 1e3) / 1e9
+    traffic = traffic_from_profiles(args.workload)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel,
+                "algorithmic_bytes_per_launch": alg_bytes, "launch_ms": round(launch_ms, 5)}
+    if args.workload == "deltanet":
+        flops = units * (6 * w.D * w.M + 6 * w.D)
+        roofline["alu"] = {"achieved_tflops": round(flops / (launch_ms / 1e3) / 1e12, 3),
+                           "peak_tflops": FP32_PEAK_TFLOPS}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = time_oracle(w, inputs, args.oracle_budget)
+
+    names = {
+        "causal_long": f"causal_long: causal linear attention (phi=elu+1), bf16 in/out, fp32 state, "
+                       f"B={w.B} H={w.H} N={w.N} D=M={w.D}",
+        "noncausal_long": f"noncausal_long: non-causal linear attention, bf16, B={w.B} H={w.H} N={w.N} D=M={w.D}",
+        "causal_mid": f"causal_mid: causal linear attention, fp32, B={w.B} H={w.H} N={w.N} D=M={w.D}",
+        "decode": f"decode: RNN-form decode, {w.B}x{w.H} states D=M={w.D}, {w.steps} single-token bf16 steps "
+                  f"after a {w.N}-token prefill",
+        "deltanet": f"deltanet: delta-rule fast weights, fp32, B={w.B} H={w.H} N={w.N} D=M={w.D}",
+    }
+    dtype = {"causal_long": "bf16", "noncausal_long": "bf16", "decode": "bf16", "causal_mid": "f32",
+             "deltanet": "f32"}[args.workload]
+    line = {
+        "metric": METRIC if args.workload == "causal_long" else f"{args.workload} {unit}",
+        "value": value, "unit": unit, "n_gpus": 1, "steps": K, "warmup": Wm,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": dtype,
+        "data": "synthetic (seeded N(0,1) inputs; no datasets or trained weights)",
+        "config": {"workload": names[args.workload], "B": w.B, "H": w.H, "N": w.N, "D": w.D, "M": w.M,
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "wall_s": round(wall, 4),
+        "source_hash": source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,143 @@
+/*
+ * linattn.h — C ABI of the MI355X (gfx950) causal linear-attention library.
+ *
+ * The library computes linear attention with the feature map
+ *   phi(x) = elu(x) + 1            ("Transformers are RNNs", Katharopoulos et
+ *                                   al. 2020, translated page "線性變換器",
+ *                                   §3.2.1 eq.(7); alpha = 1)
+ * in four forms:
+ *   - causal:      o_i = phi(q_i)^T S_i / phi(q_i)^T z_i,
+ *                  S_i = sum_{j<=i} phi(k_j) v_j^T,  z_i = sum_{j<=i} phi(k_j)
+ *                  (same page, §3.3 eq.(9)-(12); the mask j <= i is inclusive);
+ *   - non-causal:  the same with the sums over every j = 1..N (§3.2 eq.(5)-(6));
+ *   - decode step: one step of the RNN form, state updated first and then read
+ *                  (§3.4 eq.(16)-(20), without f_l and the residual);
+ *   - delta rule:  the fast-weight memory W (M x D) of "Linear Transformers Are
+ *                  Secretly Fast Weight Programmers" (Schlag et al. 2021; news
+ *                  summary, paragraphs on the update rule and normalisation):
+ *                  kh = phi(k)/sum(phi(k)), qh = phi(q)/sum(phi(q)),
+ *                  vbar = W kh, W += beta (v - vbar) kh^T, o = W qh.
+ * No 1/sqrt(D) scaling and no epsilon is applied (the pages apply none to these
+ * forms; phi > 0 keeps every denominator positive).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Tensors are DEVICE pointers, contiguous and row-major, owned by the caller:
+ *   q, k : [B, H, N, D]    v, o : [B, H, N, M]     (element type = dtype)
+ *   S    : [B, H, D, M]    z    : [B, H, D]         (always float32)
+ *   W    : [B, H, M, D]    beta : [B, H, N]         (W float32; beta = dtype)
+ * dtype is LINATTN_F32 (float) or LINATTN_BF16 (bfloat16 bits, uint16).
+ * bf16 inputs are read exactly; accumulation and state are float32; a bf16
+ * output is rounded to nearest even once, from float32.
+ * (D, M) must be one of {32, 64} x {32, 64}.  B, H, N may be 0 (nothing to
+ * compute); negative sizes are rejected.
+ * stream: a hipStream_t passed as void* (NULL = the default stream).  All work
+ * is enqueued on it asynchronously; the library never synchronises, never
+ * allocates device memory and keeps no pointer after returning.
+ *
+ * Error behaviour: every call validates its arguments before enqueuing
+ * anything and returns a linattn_status_t:
+ *   LINATTN_ERR_NULL        a required pointer is NULL, or a pair that must be
+ *                           given together (S0/z0, S_out/z_out) is half given;
+ *   LINATTN_ERR_SHAPE       a size is negative or an element count overflows;
+ *   LINATTN_ERR_DTYPE       dtype is not LINATTN_F32 / LINATTN_BF16;
+ *   LINATTN_ERR_UNSUPPORTED (D, M) is outside the built set;
+ *   LINATTN_ERR_ALIGN       a pointer is not 16-byte aligned;
+ *   LINATTN_ERR_ALIAS       an output overlaps an input it must not overlap
+ *                           (a state output identical to its input is allowed);
+ *   LINATTN_ERR_WORKSPACE   the workspace is NULL or smaller than required;
+ *   LINATTN_ERR_HIP         a kernel launch failed (hipGetLastError).
+ * Values are not checked: NaN/Inf propagate, beta outside [0,1] follows the
+ * formula.  Device faults surface at the caller's next synchronisation.
+ */
+#ifndef LINATTN_H
+#define LINATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LINATTN_ABI_VERSION 1
+
+typedef enum { LINATTN_F32 = 0, LINATTN_BF16 = 1 } linattn_dtype_t;
+
+typedef enum {
+  LINATTN_OK = 0,
+  LINATTN_ERR_NULL = 1,
+  LINATTN_ERR_SHAPE = 2,
+  LINATTN_ERR_DTYPE = 3,
+  LINATTN_ERR_UNSUPPORTED = 4,
+  LINATTN_ERR_ALIGN = 5,
+  LINATTN_ERR_ALIAS = 6,
+  LINATTN_ERR_WORKSPACE = 7,
+  LINATTN_ERR_HIP = 8
+} linattn_status_t;
+
+/* Bytes of device workspace linattn_causal_fwd needs for this problem (0 when
+ * none is needed).  Returns 0 also for invalid arguments, which the forward
+ * call then rejects. */
+size_t linattn_causal_workspace_bytes(int B, int H, int N, int D, int M, int dtype);
+
+/* Causal linear attention, eq.(9)-(12): for every (b, h) and i = 1..N,
+ *   S_i = S0 + sum_{j<=i} phi(k_j) v_j^T,  z_i = z0 + sum_{j<=i} phi(k_j),
+ *   o_i = phi(q_i)^T S_i / phi(q_i)^T z_i.
+ * o:            [B,H,N,M] output, or NULL to compute the final state only.
+ * S0, z0:       initial state (both NULL means zero, as eq.(16)-(17)); read only.
+ * S_out, z_out: final state S_N, z_N (both NULL: not written).  S_out may be
+ *               the same pointer as S0 (and z_out as z0) for an in-place carry.
+ * ws, ws_bytes: device workspace of at least linattn_causal_workspace_bytes();
+ *               contents need no initialisation and are clobbered.
+ * o must not overlap q, k, v, S0, z0, S_out, z_out or ws. */
+int linattn_causal_fwd(const void* q, const void* k, const void* v, void* o,
+                       int B, int H, int N, int D, int M, int dtype,
+                       const float* S0, const float* z0, float* S_out, float* z_out,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of device workspace linattn_noncausal_fwd needs (0 when none). */
+size_t linattn_noncausal_workspace_bytes(int B, int H, int N, int D, int M, int dtype);
+
+/* Non-causal (encoder) linear attention, eq.(5)-(6): with
+ *   S = sum_{j=1..N} phi(k_j) v_j^T and z = sum_{j=1..N} phi(k_j),
+ *   o_i = phi(q_i)^T S / phi(q_i)^T z for every i.
+ * Self-attention only: queries and keys share the length N.
+ * o must not overlap q, k, v or ws. */
+int linattn_noncausal_fwd(const void* q, const void* k, const void* v, void* o,
+                          int B, int H, int N, int D, int M, int dtype,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* One autoregressive step of the RNN form, eq.(18)-(20), for B*H independent
+ * states, in place:
+ *   S <- S + phi(k) v^T,  z <- z + phi(k),  o = phi(q)^T S / phi(q)^T z
+ * (the output reads the state that already holds this step's token).
+ * q, k: [B,H,D]; v, o: [B,H,M] (dtype); S: [B,H,D,M], z: [B,H,D] float32,
+ * read and written in place.  o must not overlap q, k, v, S or z. */
+int linattn_decode_step(const void* q, const void* k, const void* v, void* o,
+                        float* S, float* z, int B, int H, int D, int M, int dtype,
+                        void* stream);
+
+/* Delta-rule fast-weight memory over a sequence, for every (b, h), i = 1..N:
+ *   kh = phi(k_i)/sum_c phi(k_i)_c,  qh = phi(q_i)/sum_c phi(q_i)_c,
+ *   vbar = W kh,  W <- W + beta_i (v_i - vbar) kh^T,  o_i = W qh
+ * (retrieve the value bound to the key, then store the convex combination
+ * beta_i v_i + (1 - beta_i) vbar in its place; the output reads the updated W).
+ * beta: [B,H,N] in dtype, used as given (no squashing).
+ * W0: [B,H,M,D] float32 initial memory, NULL means zero.
+ * W_out: [B,H,M,D] float32 final memory, or NULL; may equal W0.
+ * o must not overlap q, k, v, beta, W0 or W_out. */
+int deltanet_fwd(const void* q, const void* k, const void* v, const void* beta, void* o,
+                 int B, int H, int N, int D, int M, int dtype,
+                 const float* W0, float* W_out, void* stream);
+
+/* Static, human-readable name of a status code ("LINATTN_OK", ...). */
+const char* linattn_status_str(int status);
+
+/* LINATTN_ABI_VERSION of the built library. */
+int linattn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINATTN_H */

@@ -1,0 +1,305 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Both sides read the same seeded host tensors.  Errors are row-wise relative
+(max over rows of ||y - r||_inf / ||r||_inf); tolerances: 1e-4 for float32
+inputs, 2e-2 for bfloat16 inputs with float32 accumulation.  States are float32
+in every mode and are held to 1e-4 (per matrix, max |err| / max |ref|), also
+in bf16 runs: the state update multiplies the exact bf16 values by phi(k)
+split into a bf16 head and tail, so the state carries float32-level error.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import weight_recurrences_amd as la
+from oracle.metrics import mat_rel_err, row_rel_err
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
+STATE_TOL = {torch.float32: 1e-4, torch.bfloat16: 1e-4}
+DEV = "cuda:0"
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def gpu(*ts):
+    return [None if t is None else t.to(DEV) for t in ts]
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.detach().to("cpu")
+
+
+# ---------------------------------------------------------------- causal
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("D,M", [(32, 32), (32, 64), (64, 32), (64, 64)])
+@pytest.mark.parametrize("N", [1, 3, 63, 64, 65, 200, 1000, 2500])
+def test_causal_ragged(dtype, D, M, N):
+    say("causal", dtype, D, M, N)
+    q, k, v = synth.qkv(2, 3, N, D, M, dtype=dtype, seed=N * 7 + D + M)
+    o, (S, z) = la.causal(*gpu(q, k, v), return_state=True)
+    ro, rS, rz = oracle.causal(q, k, v)
+    assert row_rel_err(host(o), ro) < TOL[dtype]
+    assert mat_rel_err(host(S), rS) < STATE_TOL[dtype]
+    assert mat_rel_err(host(z), rz, 1) < STATE_TOL[dtype]
+
+
+def test_causal_small_workload_all_rows_explicit():
+    w = synth.WORKLOADS["causal_small"]
+    say(w)
+    q, k, v = synth.workload_inputs(w)
+    o = la.causal(*gpu(q, k, v))
+    assert row_rel_err(host(o), oracle.causal_explicit(q, k, v)) < 1e-4
+
+
+def test_causal_mid_workload():
+    w = synth.WORKLOADS["causal_mid"]
+    say(w)
+    q, k, v = synth.workload_inputs(w)
+    o, (S, z) = la.causal(*gpu(q, k, v), return_state=True)
+    o = host(o)
+    ro, rS, rz = oracle.causal(q, k, v)
+    assert row_rel_err(o, ro) < 1e-4
+    assert mat_rel_err(host(S), rS) < 1e-4 and mat_rel_err(host(z), rz, 1) < 1e-4
+    rows = synth.sample_rows(w.N, w.B * w.H, n_random=16)
+    ex = oracle.causal_explicit(q, k, v, rows=rows)
+    got = torch.gather(o.reshape(w.B * w.H, w.N, w.M), 1, rows[..., None].expand(-1, -1, w.M))
+    assert row_rel_err(got.reshape(ex.shape), ex) < 1e-4
+
+
+@pytest.fixture(scope="module")
+def long_inputs():
+    w = synth.WORKLOADS["causal_long"]
+    return w, synth.workload_inputs(w)
+
+
+def test_causal_long_workload(long_inputs):
+    w, (q, k, v) = long_inputs
+    say(w)
+    o, (S, z) = la.causal(*gpu(q, k, v), return_state=True)
+    o = host(o)
+    ro, rS, rz = oracle.causal(q, k, v)
+    assert row_rel_err(o, ro) < 2e-2
+    assert mat_rel_err(host(S), rS) < 1e-4 and mat_rel_err(host(z), rz, 1) < 1e-4
+    rows = synth.sample_rows(w.N, w.B * w.H, n_random=32)
+    ex = oracle.causal_explicit(q, k, v, rows=rows)
+    got = torch.gather(o.reshape(w.B * w.H, w.N, w.M), 1, rows[..., None].expand(-1, -1, w.M))
+    assert row_rel_err(got.reshape(ex.shape), ex) < 2e-2
+
+
+def test_causal_long_repeatable(long_inputs):
+    w, (q, k, v) = long_inputs
+    say("repeat", w)
+    qg, kg, vg = gpu(q, k, v)
+    a = host(la.causal(qg, kg, vg))
+    b = host(la.causal(qg, kg, vg))
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_noncausal_long_workload(long_inputs):
+    w, (q, k, v) = long_inputs
+    say("noncausal", w)
+    o = host(la.noncausal(*gpu(q, k, v)))
+    ro, _, _ = oracle.noncausal(q, k, v)
+    assert row_rel_err(o, ro) < 2e-2
+    rows = synth.sample_rows(w.N, w.B * w.H, n_random=4)[:, :6]
+    ex = oracle.noncausal_explicit(q, k, v, rows=rows)
+    got = torch.gather(o.reshape(w.B * w.H, w.N, w.M), 1, rows[..., None].expand(-1, -1, w.M))
+    assert row_rel_err(got.reshape(ex.shape), ex) < 2e-2
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("D,M", [(32, 32), (32, 64), (64, 32), (64, 64)])
+@pytest.mark.parametrize("N", [1, 65, 1000, 2500])
+def test_noncausal_ragged(dtype, D, M, N):
+    say("noncausal", dtype, D, M, N)
+    q, k, v = synth.qkv(2, 2, N, D, M, dtype=dtype, seed=N + 3 * D + M)
+    o = host(la.noncausal(*gpu(q, k, v)))
+    ro, _, _ = oracle.noncausal(q, k, v)
+    assert row_rel_err(o, ro) < TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_state_carry_split_sequence(dtype):
+    N, D, M = 3000, 64, 64
+    say("carry", dtype)
+    q, k, v = synth.qkv(1, 4, N, D, M, dtype=dtype, seed=11)
+    ro, rS, rz = oracle.causal(q, k, v)
+    qg, kg, vg = gpu(q, k, v)
+    for P in (1, 700, 2048, 2999):
+        S, z = la.causal(qg[:, :, :P].contiguous(), kg[:, :, :P].contiguous(), vg[:, :, :P].contiguous(),
+                         output=False)
+        # in-place carry: S_out is the same buffer as S0
+        S1, z1 = S.clone(), z.clone()
+        lib = la._lib.load()
+        rest = [t[:, :, P:].contiguous() for t in (qg, kg, vg)]
+        o2 = torch.empty_like(rest[2])
+        need = la.causal_workspace_bytes(1, 4, N - P, D, M, dtype)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=DEV)
+        rc = lib.linattn_causal_fwd(rest[0].data_ptr(), rest[1].data_ptr(), rest[2].data_ptr(), o2.data_ptr(),
+                                    1, 4, N - P, D, M, 0 if dtype == torch.float32 else 1,
+                                    S1.data_ptr(), z1.data_ptr(), S1.data_ptr(), z1.data_ptr(),
+                                    ws.data_ptr(), need, torch.cuda.current_stream().cuda_stream)
+        assert rc == 0
+        assert row_rel_err(host(o2), ro[:, :, P:]) < TOL[dtype]
+        assert mat_rel_err(host(S1), rS) < STATE_TOL[dtype]
+        assert mat_rel_err(host(z1), rz, 1) < STATE_TOL[dtype]
+
+
+def test_state_only_and_empty_sequences():
+    say("state-only / empty")
+    q, k, v = synth.qkv(3, 2, 777, 32, 64, dtype=torch.bfloat16, seed=5)
+    S0 = torch.randn(3, 2, 32, 64, dtype=torch.float64)
+    z0 = torch.rand(3, 2, 32, dtype=torch.float64) * 10
+    S0f, z0f = S0.float(), z0.float()
+    S, z = la.causal(*gpu(q, k, v), state=(S0f.to(DEV), z0f.to(DEV)), output=False)
+    _, rS, rz = oracle.causal(q, k, v, S0=S0f, z0=z0f, want_output=False)
+    assert mat_rel_err(host(S), rS) < 1e-4 and mat_rel_err(host(z), rz, 1) < 1e-4
+    # N = 0: the final state is the initial state
+    e = torch.empty(3, 2, 0, 32, dtype=torch.bfloat16, device=DEV)
+    ev = torch.empty(3, 2, 0, 64, dtype=torch.bfloat16, device=DEV)
+    o, (S, z) = la.causal(e, e, ev, state=(S0f.to(DEV), z0f.to(DEV)), return_state=True)
+    assert o.shape == (3, 2, 0, 64)
+    assert torch.equal(host(S), S0f) and torch.equal(host(z), z0f)
+    o, (S, z) = la.causal(e, e, ev, return_state=True)
+    assert torch.count_nonzero(host(S)) == 0 and torch.count_nonzero(host(z)) == 0
+
+
+def test_causal_one_hot_slots_exact():
+    """Keys that select one slot each (phi = e_c exactly in float32): every output
+    row is the mean of the small-integer values stored in the query's slot."""
+    N, D, M = 300, 32, 32
+    say("one-hot")
+    g = torch.Generator().manual_seed(3)
+    slots = torch.randint(0, D, (N,), generator=g)
+    k = torch.full((1, 1, N, D), -200.0)
+    k[0, 0, torch.arange(N), slots] = 0.0
+    q = torch.full((1, 1, N, D), -200.0)
+    q[..., int(slots[0])] = 0.0
+    v = torch.randint(-8, 9, (1, 1, N, M), generator=g).float()
+    o = host(la.causal(*gpu(q, k, v)))
+    want = np.zeros((N, M))
+    sel = []
+    for i in range(N):
+        if slots[i] == slots[0]:
+            sel.append(i)
+        want[i] = v[0, 0, sel].numpy().mean(axis=0)
+    np.testing.assert_allclose(o[0, 0].numpy(), want, rtol=0, atol=1e-5)
+
+
+# ---------------------------------------------------------------- decode
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("D,M", [(32, 32), (32, 64), (64, 32), (64, 64)])
+def test_decode_steps_small(dtype, D, M):
+    B, H, P, T = 3, 5, 40, 6
+    say("decode", dtype, D, M)
+    q, k, v = synth.qkv(B, H, P, D, M, dtype=dtype, seed=D * M)
+    sq, sk, sv = synth.decode_steps(B, H, D, M, T, dtype=dtype, seed=D + M)
+    S, z = la.causal(*gpu(q, k, v), output=False)
+    _, rS, rz = oracle.causal(q, k, v, want_output=False)
+    gq, gk, gv = gpu(sq, sk, sv)
+    for t in range(T):
+        o = la.decode_step(gq[t], gk[t], gv[t], S, z)
+        ro, rS, rz = oracle.decode_step(sq[t], sk[t], sv[t], rS, rz)
+        assert row_rel_err(host(o), ro) < TOL[dtype]
+    assert mat_rel_err(host(S), rS) < 1e-4 and mat_rel_err(host(z), rz, 1) < 1e-4
+
+
+def test_decode_workload_sampled_heads():
+    """Full decode workload (prefill 512 + 1024 steps on 256 x 16 states, the
+    launch sequence the benchmark times): every head for the first steps, 64
+    sampled heads through all 1024 steps, and the final fp32 states of the
+    sampled heads."""
+    w = synth.WORKLOADS["decode"]
+    say(w)
+    q, k, v, sq, sk, sv = synth.workload_inputs(w)
+    S, z = la.causal(*gpu(q, k, v), output=False)
+    _, rS, rz = oracle.causal(q, k, v, want_output=False)
+    assert mat_rel_err(host(S), rS) < 1e-4
+    gq, gk, gv = gpu(sq, sk, sv)
+    outs = torch.empty(w.steps, w.B, w.H, w.M, dtype=w.dtype, device=DEV)
+    for t in range(w.steps):
+        la.decode_step(gq[t], gk[t], gv[t], S, z, out=outs[t])
+        if t < 2:  # every head
+            ro, rS, rz = oracle.decode_step(sq[t], sk[t], sv[t], rS, rz)
+            assert row_rel_err(host(outs[t]), ro) < 2e-2
+    outs = host(outs)
+    hs = torch.randperm(w.B * w.H, generator=torch.Generator().manual_seed(9))[:64]
+    bi, hi = hs // w.H, hs % w.H
+    _, rS_s, rz_s = oracle.causal(q[bi, hi][None], k[bi, hi][None], v[bi, hi][None], want_output=False)
+    for t in range(w.steps):
+        ro, rS_s, rz_s = oracle.decode_step(sq[t][bi, hi][None], sk[t][bi, hi][None], sv[t][bi, hi][None],
+                                            rS_s, rz_s)
+        assert row_rel_err(outs[t][bi, hi][None], ro) < 2e-2, t
+    assert mat_rel_err(host(S)[bi, hi][None], rS_s) < 1e-4
+    assert mat_rel_err(host(z)[bi, hi][None], rz_s, 1) < 1e-4
+
+
+# ---------------------------------------------------------------- delta rule
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("D,M", [(32, 32), (32, 64), (64, 32), (64, 64)])
+@pytest.mark.parametrize("N", [1, 5, 64, 65, 130])
+def test_deltanet_ragged(dtype, D, M, N):
+    say("deltanet", dtype, D, M, N)
+    q, k, v, beta = synth.qkv_beta(2, 3, N, D, M, dtype=dtype, seed=N + D * M)
+    W0 = torch.randn(2, 3, M, D) * 0.1
+    o, W = la.deltanet(*gpu(q, k, v, beta), W0=W0.to(DEV), return_state=True)
+    ro, rW = oracle.deltanet(q, k, v, beta, W0=W0)
+    assert row_rel_err(host(o), ro) < TOL[dtype]
+    assert mat_rel_err(host(W), rW) < 1e-4
+
+
+def test_deltanet_workload():
+    w = synth.WORKLOADS["deltanet"]
+    say(w)
+    q, k, v, beta = synth.workload_inputs(w)
+    o, W = la.deltanet(*gpu(q, k, v, beta), return_state=True)
+    ro, rW = oracle.deltanet(q, k, v, beta)
+    assert row_rel_err(host(o), ro) < 1e-4
+    assert mat_rel_err(host(W), rW) < 1e-4
+
+
+def test_deltanet_exact_recall_and_inplace_memory():
+    """One-hot keys at beta = 1 store and overwrite slots exactly; W_out may be W0."""
+    D, M, N = 64, 64, 200
+    say("deltanet recall")
+    g = torch.Generator().manual_seed(4)
+    slots = torch.randint(0, D, (N,), generator=g)
+    k = torch.full((1, 1, N, D), -200.0)
+    k[0, 0, torch.arange(N), slots] = 0.0
+    v = torch.randint(-8, 9, (1, 1, N, M), generator=g).float()
+    q = k.clone()
+    beta = torch.ones(1, 1, N)
+    Wg = torch.zeros(1, 1, M, D, device=DEV)
+    lib = la._lib.load()
+    qg, kg, vg, bg = gpu(q, k, v, beta)
+    o = torch.empty(1, 1, N, M, device=DEV)
+    rc = lib.deltanet_fwd(qg.data_ptr(), kg.data_ptr(), vg.data_ptr(), bg.data_ptr(), o.data_ptr(), 1, 1, N, D, M,
+                          0, Wg.data_ptr(), Wg.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+    # reading the slot just written returns exactly the value written
+    np.testing.assert_allclose(host(o)[0, 0].numpy(), v[0, 0].numpy(), rtol=0, atol=1e-5)
+    W = host(Wg)[0, 0]
+    for c in range(D):
+        last = [i for i in range(N) if slots[i] == c]
+        want = v[0, 0, last[-1]] if last else torch.zeros(M)
+        np.testing.assert_allclose(W[:, c].numpy(), want.numpy(), rtol=0, atol=1e-5)
+
+
+def test_deltanet_empty_sequence_copies_memory():
+    say("deltanet empty")
+    W0 = torch.randn(2, 2, 32, 32, device=DEV)
+    e = torch.empty(2, 2, 0, 32, device=DEV)
+    o, W = la.deltanet(e, e, e, torch.empty(2, 2, 0, device=DEV), W0=W0, return_state=True)
+    assert torch.equal(host(W), host(W0))

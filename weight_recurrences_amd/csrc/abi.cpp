@@ -1,0 +1,182 @@
+// C ABI of the library (declared in include/linattn.h): argument validation,
+// workspace sizing and dispatch to the gfx950 kernels.  Every check runs on
+// the host before anything is enqueued, so an invalid call leaves the device
+// untouched and never calls into the HIP runtime.
+#include <stdint.h>
+
+#include <algorithm>
+#include <initializer_list>
+
+#include "linattn.h"
+#include "kernels.hpp"
+
+namespace {
+
+struct Span {
+  uintptr_t lo = 0, hi = 0;  // [lo, hi); empty when hi == lo
+  Span() = default;
+  Span(const void* p, long long bytes) : lo((uintptr_t)p), hi((uintptr_t)p + (uintptr_t)(p ? bytes : 0)) {}
+  bool empty() const { return hi <= lo; }
+  bool overlaps(const Span& o) const { return !empty() && !o.empty() && lo < o.hi && o.lo < hi; }
+  bool same(const Span& o) const { return lo == o.lo && hi == o.hi; }
+};
+
+bool dm_supported(int D, int M) { return (D == 32 || D == 64) && (M == 32 || M == 64); }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int esize(int dtype) { return dtype == LINATTN_BF16 ? 2 : 4; }
+
+// Shape checks shared by the sequence entry points.  Sizes fit int64 element
+// counts and the kernels' 32-bit grid and index arithmetic.
+int check_shape(int B, int H, int N, int D, int M, int dtype) {
+  if (dtype != LINATTN_F32 && dtype != LINATTN_BF16) return LINATTN_ERR_DTYPE;
+  if (B < 0 || H < 0 || N < 0 || D <= 0 || M <= 0) return LINATTN_ERR_SHAPE;
+  if (!dm_supported(D, M)) return LINATTN_ERR_UNSUPPORTED;
+  const long long BH = (long long)B * H;
+  if (BH > (1LL << 30)) return LINATTN_ERR_SHAPE;
+  const long long rows = BH * N;
+  if (N > 0 && rows / N != BH) return LINATTN_ERR_SHAPE;
+  if (rows > (1LL << 46) / 64) return LINATTN_ERR_SHAPE;  // bytes of q stay far below 2^63
+  if (BH > 0 && N > 0) {
+    const int tb = la::causal_block_tokens((int)BH, N);
+    const long long nblk = (N + tb - 1) / tb;
+    if (nblk * BH > (long long)INT32_MAX) return LINATTN_ERR_SHAPE;
+  }
+  return LINATTN_OK;
+}
+
+int check_align(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return LINATTN_ERR_ALIGN;
+  return LINATTN_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? LINATTN_OK : LINATTN_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+size_t linattn_causal_workspace_bytes(int B, int H, int N, int D, int M, int dtype) {
+  if (check_shape(B, H, N, D, M, dtype) != LINATTN_OK) return 0;
+  return la::causal_ws_bytes(B * H, N, D, M, dtype == LINATTN_BF16);
+}
+
+size_t linattn_noncausal_workspace_bytes(int B, int H, int N, int D, int M, int dtype) {
+  if (check_shape(B, H, N, D, M, dtype) != LINATTN_OK) return 0;
+  return la::noncausal_ws_bytes(B * H, N, D, M);
+}
+
+int linattn_causal_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int D, int M,
+                       int dtype, const float* S0, const float* z0, float* S_out, float* z_out, void* ws,
+                       size_t ws_bytes, void* stream) {
+  int st = check_shape(B, H, N, D, M, dtype);
+  if (st) return st;
+  const long long BH = (long long)B * H, es = esize(dtype);
+  const long long nq = BH * N * D * es, nv = BH * N * M * es;
+  if ((S0 == nullptr) != (z0 == nullptr)) return LINATTN_ERR_NULL;
+  if ((S_out == nullptr) != (z_out == nullptr)) return LINATTN_ERR_NULL;
+  if (BH * N > 0 && (!q || !k || !v)) return LINATTN_ERR_NULL;
+  if ((st = check_align({q, k, v, o, S0, z0, S_out, z_out, ws}))) return st;
+  const size_t need = la::causal_ws_bytes((int)BH, N, D, M, dtype == LINATTN_BF16);
+  const bool uses_ws = need > 0;
+  if (uses_ws && (!ws || ws_bytes < need)) return LINATTN_ERR_WORKSPACE;
+
+  const Span sq(q, nq), sk(k, nq), sv(v, nv), so(o, o ? nv : 0);
+  const Span sS0(S0, BH * D * M * 4), sz0(z0, BH * D * 4), sSo(S_out, BH * D * M * 4), szo(z_out, BH * D * 4);
+  const Span sws(ws, uses_ws ? (long long)need : 0);
+  for (const Span& x : {sq, sk, sv, sS0, sz0, sSo, szo, sws})
+    if (so.overlaps(x)) return LINATTN_ERR_ALIAS;
+  for (const Span& out : {sSo, szo})
+    for (const Span& x : {sq, sk, sv, sws})
+      if (out.overlaps(x)) return LINATTN_ERR_ALIAS;
+  if (sSo.overlaps(szo)) return LINATTN_ERR_ALIAS;
+  if ((sSo.overlaps(sS0) && !sSo.same(sS0)) || (szo.overlaps(sz0) && !szo.same(sz0))) return LINATTN_ERR_ALIAS;
+  if (sSo.overlaps(sz0) || szo.overlaps(sS0)) return LINATTN_ERR_ALIAS;
+  for (const Span& x : {sq, sk, sv, sS0, sz0})
+    if (sws.overlaps(x)) return LINATTN_ERR_ALIAS;
+
+  if (BH == 0) return LINATTN_OK;
+  if (N == 0 && !S_out) return LINATTN_OK;
+  return hip_status(la::launch_causal(q, k, v, o, (int)BH, N, D, M, dtype == LINATTN_BF16, S0, z0, S_out, z_out,
+                                      uses_ws ? ws : nullptr, (hipStream_t)stream));
+}
+
+int linattn_noncausal_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int D, int M,
+                          int dtype, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_shape(B, H, N, D, M, dtype);
+  if (st) return st;
+  const long long BH = (long long)B * H, es = esize(dtype);
+  if (BH * N == 0) return LINATTN_OK;
+  const long long nq = BH * N * D * es, nv = BH * N * M * es;
+  if (!q || !k || !v || !o) return LINATTN_ERR_NULL;
+  if ((st = check_align({q, k, v, o, ws}))) return st;
+  const size_t need = la::noncausal_ws_bytes((int)BH, N, D, M);
+  if (!ws || ws_bytes < need) return LINATTN_ERR_WORKSPACE;
+  const Span sq(q, nq), sk(k, nq), sv(v, nv), so(o, nv), sws(ws, (long long)need);
+  for (const Span& x : {sq, sk, sv, sws})
+    if (so.overlaps(x)) return LINATTN_ERR_ALIAS;
+  for (const Span& x : {sq, sk, sv})
+    if (sws.overlaps(x)) return LINATTN_ERR_ALIAS;
+  return hip_status(
+      la::launch_noncausal(q, k, v, o, (int)BH, N, D, M, dtype == LINATTN_BF16, ws, (hipStream_t)stream));
+}
+
+int linattn_decode_step(const void* q, const void* k, const void* v, void* o, float* S, float* z, int B, int H,
+                        int D, int M, int dtype, void* stream) {
+  int st = check_shape(B, H, 1, D, M, dtype);
+  if (st) return st;
+  const long long BH = (long long)B * H, es = esize(dtype);
+  if (BH == 0) return LINATTN_OK;
+  if (!q || !k || !v || !o || !S || !z) return LINATTN_ERR_NULL;
+  if ((st = check_align({q, k, v, o, S, z}))) return st;
+  const Span sq(q, BH * D * es), sk(k, BH * D * es), sv(v, BH * M * es), so(o, BH * M * es);
+  const Span sS(S, BH * D * M * 4), sz(z, BH * D * 4);
+  for (const Span& x : {sq, sk, sv, sS, sz})
+    if (so.overlaps(x)) return LINATTN_ERR_ALIAS;
+  for (const Span& x : {sq, sk, sv, sz})
+    if (sS.overlaps(x)) return LINATTN_ERR_ALIAS;
+  for (const Span& x : {sq, sk, sv})
+    if (sz.overlaps(x)) return LINATTN_ERR_ALIAS;
+  return hip_status(la::launch_decode(q, k, v, o, S, z, (int)BH, D, M, dtype == LINATTN_BF16, (hipStream_t)stream));
+}
+
+int deltanet_fwd(const void* q, const void* k, const void* v, const void* beta, void* o, int B, int H, int N, int D,
+                 int M, int dtype, const float* W0, float* W_out, void* stream) {
+  int st = check_shape(B, H, N, D, M, dtype);
+  if (st) return st;
+  const long long BH = (long long)B * H, es = esize(dtype);
+  if (BH * N > 0 && (!q || !k || !v || !beta || !o)) return LINATTN_ERR_NULL;
+  if ((st = check_align({q, k, v, beta, o, W0, W_out}))) return st;
+  const long long nq = BH * N * D * es, nv = BH * N * M * es;
+  const Span sq(q, nq), sk(k, nq), sv(v, nv), sb(beta, BH * N * es), so(o, nv);
+  const Span sW0(W0, BH * M * D * 4), sWo(W_out, BH * M * D * 4);
+  for (const Span& x : {sq, sk, sv, sb, sW0, sWo})
+    if (so.overlaps(x)) return LINATTN_ERR_ALIAS;
+  for (const Span& x : {sq, sk, sv, sb})
+    if (sWo.overlaps(x)) return LINATTN_ERR_ALIAS;
+  if (sWo.overlaps(sW0) && !sWo.same(sW0)) return LINATTN_ERR_ALIAS;
+  if (BH == 0 || (N == 0 && !W_out)) return LINATTN_OK;
+  return hip_status(la::launch_deltanet(q, k, v, beta, o, (int)BH, N, D, M, dtype == LINATTN_BF16, W0, W_out,
+                                        (hipStream_t)stream));
+}
+
+const char* linattn_status_str(int status) {
+  switch (status) {
+    case LINATTN_OK: return "LINATTN_OK";
+    case LINATTN_ERR_NULL: return "LINATTN_ERR_NULL";
+    case LINATTN_ERR_SHAPE: return "LINATTN_ERR_SHAPE";
+    case LINATTN_ERR_DTYPE: return "LINATTN_ERR_DTYPE";
+    case LINATTN_ERR_UNSUPPORTED: return "LINATTN_ERR_UNSUPPORTED";
+    case LINATTN_ERR_ALIGN: return "LINATTN_ERR_ALIGN";
+    case LINATTN_ERR_ALIAS: return "LINATTN_ERR_ALIAS";
+    case LINATTN_ERR_WORKSPACE: return "LINATTN_ERR_WORKSPACE";
+    case LINATTN_ERR_HIP: return "LINATTN_ERR_HIP";
+    default: return "LINATTN_ERR_UNKNOWN";
+  }
+}
+
+int linattn_abi_version(void) { return LINATTN_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,690 @@
+// Single-pass causal linear attention for bf16 inputs on gfx950 (MI355X).
+//
+// Method: "Transformers are RNNs" (Katharopoulos et al., 2020), translated page
+// "線性變換器", §3.3 eq.(9)-(12): o_i = phi(q_i)^T S_i / phi(q_i)^T z_i with the
+// prefix states S_i = sum_{j<=i} phi(k_j) v_j^T, z_i = sum_{j<=i} phi(k_j).
+//
+// One workgroup owns a block of T = 256 tokens of one (batch, head) and reads
+// each input byte from HBM exactly once:
+//   phase 1  K and V of the block are loaded, phi(K) is applied, and phi(K)
+//            (bf16) and V stay resident in LDS.  The block's state increment
+//            dS = phi(K_b)^T V_b, dz = colsum phi(K_b) is accumulated in
+//            float32 (phi(K) split into a bf16 head and tail so that the state
+//            keeps float32-level error), with a snapshot of the running local
+//            prefix at every chunk boundary.
+//   phase 2  decoupled look-back: the exclusive prefix P_b of the block is
+//            S0 + sum of the increments of all earlier blocks of the head
+//            (eq.(10)-(11) are plain sums, so blocks combine by addition).  The
+//            block publishes its increment, sums the increments of its
+//            predecessors until it meets one that has published its inclusive
+//            prefix, then publishes its own inclusive prefix.
+//   phase 3  outputs chunk by chunk from LDS: for chunk c with state
+//            S = P_b + (local prefix at c):
+//              num_i = phi(q_i)^T S + sum_{j in c, j<=i} (phi(q_i).phi(k_j)) v_j
+//              den_i = phi(q_i)^T z + sum_{j in c, j<=i}  phi(q_i).phi(k_j)
+//            with every product a 16x16x32 bf16 MFMA tile.
+//
+// Synchronisation between workgroups uses one 64-bit flag per block holding
+// (epoch << 2 | status); the epoch is new for every launch, so the workspace
+// never needs clearing.  A workgroup only waits on blocks with a smaller
+// workgroup index, and a bounded spin falls back to computing the missing
+// increment itself from global memory, so no wait can hang.
+//
+// Operand layouts (lane l = 16 g + n of a 64-lane wavefront):
+//  * d-contraction: lane group g holds d = 32 s + 8 g + e (e < 8) of slab s.
+//  * j-contraction: lane group g holds j = 32 s + 16 h + 4 g + r (e = 4h + r),
+//    the rows an accumulator tile keeps in the lane, read from the row-major
+//    LDS tiles with ds_read_b64_tr_b16 (within a 16-lane group the
+//    instruction returns out[i][e] = in[4e + i/4][i % 4]).
+//  * B-operand column n of tile t is column 16 t + n.
+// LDS rows are 16-byte units XOR-swizzled by (row ^ row >> 3) & 7, which keeps
+// the row-major stores, the score-operand reads and the transposed reads free
+// of bank conflicts.
+#include <atomic>
+#include <chrono>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace la {
+namespace fused {
+
+constexpr int CH = 64;    // chunk length
+constexpr int NT = 256;   // threads per workgroup (4 wavefronts)
+constexpr int TBLK = 256; // tokens per block
+constexpr int NCH = TBLK / CH;
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+template <int D, int M>
+struct G {
+  static constexpr int TD = D / 16, TM = M / 16;
+  static constexpr int WPT = 4 / TD;    // waves sharing a d-tile of S
+  static constexpr int TMW = TM / WPT;  // m-tiles of S per wave
+  static constexpr int UK = D / 8;      // 16-byte units per K row
+  static constexpr int UV = M / 8;      // 16-byte units per V row
+  // A published state is the register image of the block's tiles: for every
+  // (wave, tile, pair of accumulator rows) 64 lane-consecutive float pairs,
+  // followed by z [D].  Producer and consumers own the same tiles.
+  static constexpr int SIMG = 4 * TMW * 4 * 64;                        // floats of the S image
+  static constexpr int SLOT = ((SIMG + D) * 4 + 255) / 256 * 256;      // bytes per published state
+};
+
+template <int D, int M>
+struct Smem {
+  bf16_t K[TBLK * D];   // phi(K) head, row-major, swizzled
+  bf16_t V[TBLK * M];   // V, row-major, swizzled
+  union {
+    bf16_t Kl[CH * D];  // phase 1: phi(K) tail of the current chunk
+    bf16_t St[M * D];   // phase 3: S^T operand of the current chunk
+  } u;
+  float Zs[D];
+  int status;
+};
+
+// Swizzled element offset of (row, col) in a row-major bf16 tile with U units per row.
+template <int U>
+__device__ __forceinline__ int swz(int row, int col) {
+  const int unit = (col >> 3) ^ ((row ^ (row >> 3)) & (U - 1));
+  return row * U * 8 + unit * 8 + (col & 7);
+}
+
+__device__ __forceinline__ uint32_t cvt_pk(float lo, float hi) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{lo, hi}, b2));
+}
+
+__device__ __forceinline__ float lo_of(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_of(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Transposed fragment: lane (n, g) gets rows row0 + 4g + e (e < 4) of column col0 + n
+// from a row-major swizzled tile.
+template <int U>
+__device__ __forceinline__ u32x2 tr_read(const bf16_t* tile, int row0, int col0, int g, int sl) {
+  const int row = row0 + 4 * g + (sl >> 2);
+  const int col = col0 + 4 * (sl & 3);
+  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(tile + swz<U>(row, col)));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// j-slot fragment (8 rows 32s + 16h + 4g + r of column col0 + n) from a row-major tile.
+template <int U>
+__device__ __forceinline__ bf16x8 jfrag(const bf16_t* tile, int rbase, int col0, int g, int sl) {
+  const u32x2 a = tr_read<U>(tile, rbase, col0, g, sl);
+  const u32x2 b = tr_read<U>(tile, rbase + 16, col0, g, sl);
+  return as_bf16x8(u32x4{a[0], a[1], b[0], b[1]});
+}
+
+__device__ __forceinline__ bf16x8 ones8() {
+  const uint32_t one2 = 0x3F803F80u;
+  return as_bf16x8(u32x4{one2, one2, one2, one2});
+}
+
+// Publish / read a block state in the workspace: S [D][M] then z [D] (float32).
+template <int D, int M>
+struct Tiles {
+  f32x4 S[G<D, M>::TMW];
+  f32x4 Z;
+};
+
+template <int D, int M>
+__device__ __forceinline__ void tiles_zero(Tiles<D, M>& t) {
+#pragma unroll
+  for (int u = 0; u < G<D, M>::TMW; ++u) t.S[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  t.Z = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+template <int D, int M>
+__device__ __forceinline__ void tile_coords(int w, int u, int& td, int& tm) {
+  td = w % G<D, M>::TD;
+  tm = (w / G<D, M>::TD) + G<D, M>::WPT * u;
+}
+
+// Published states are written and read with relaxed agent-scope atomics
+// (write-through, coherent across the XCDs' L2 caches), so publishing needs no
+// cache-wide writeback or invalidate: the producer waits for its stores to
+// complete before its flag store, the consumer reads after seeing the flag.
+__device__ __forceinline__ unsigned long long f2_bits(float a, float b) {
+  return (unsigned long long)__float_as_uint(a) | ((unsigned long long)__float_as_uint(b) << 32);
+}
+
+template <int D, int M>
+__device__ __forceinline__ void slot_store(char* slot, const Tiles<D, M>& t, int w, int lane, int n, int g) {
+  using GG = G<D, M>;
+  unsigned long long* s = reinterpret_cast<unsigned long long*>(slot);
+#pragma unroll
+  for (int u = 0; u < GG::TMW; ++u)
+#pragma unroll
+    for (int rp = 0; rp < 2; ++rp)
+      __hip_atomic_store(&s[((w * GG::TMW + u) * 2 + rp) * 64 + lane], f2_bits(t.S[u][2 * rp], t.S[u][2 * rp + 1]),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (w < GG::TD && n == 0) {
+    unsigned* z = reinterpret_cast<unsigned*>(slot) + GG::SIMG;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      __hip_atomic_store(&z[16 * w + 4 * g + r], __float_as_uint(t.Z[r]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+template <int D, int M>
+__device__ __forceinline__ void slot_load(Tiles<D, M>& t, const char* slot, int w, int lane, int g) {
+  using GG = G<D, M>;
+  unsigned long long* s = reinterpret_cast<unsigned long long*>(const_cast<char*>(slot));
+#pragma unroll
+  for (int u = 0; u < GG::TMW; ++u)
+#pragma unroll
+    for (int rp = 0; rp < 2; ++rp) {
+      const unsigned long long x =
+          __hip_atomic_load(&s[((w * GG::TMW + u) * 2 + rp) * 64 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      t.S[u][2 * rp] = __uint_as_float((unsigned)x);
+      t.S[u][2 * rp + 1] = __uint_as_float((unsigned)(x >> 32));
+    }
+  t.Z = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (w < GG::TD) {
+    unsigned* z = reinterpret_cast<unsigned*>(const_cast<char*>(slot)) + GG::SIMG;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      t.Z[r] = __uint_as_float(__hip_atomic_load(&z[16 * w + 4 * g + r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  }
+}
+
+template <int D, int M>
+__device__ __forceinline__ void tiles_acc(Tiles<D, M>& a, const Tiles<D, M>& b) {
+#pragma unroll
+  for (int u = 0; u < G<D, M>::TMW; ++u) a.S[u] += b.S[u];
+  a.Z += b.Z;
+}
+
+// Adds this wave's elements of a caller state (S [D][M], z [D]).
+template <int D, int M>
+__device__ __forceinline__ void tiles_add_from_state(Tiles<D, M>& t, const float* S, const float* z, int w, int n,
+                                                     int g) {
+#pragma unroll
+  for (int u = 0; u < G<D, M>::TMW; ++u) {
+    int td, tm;
+    tile_coords<D, M>(w, u, td, tm);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) t.S[u][r] += S[(16 * td + 4 * g + r) * M + 16 * tm + n];
+  }
+  if (w < G<D, M>::TD) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) t.Z[r] += z[16 * w + 4 * g + r];
+  }
+}
+
+template <int D, int M>
+__device__ __forceinline__ void tiles_store(const Tiles<D, M>& t, float* S, float* z, int w, int n, int g) {
+#pragma unroll
+  for (int u = 0; u < G<D, M>::TMW; ++u) {
+    int td, tm;
+    tile_coords<D, M>(w, u, td, tm);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) S[(16 * td + 4 * g + r) * M + 16 * tm + n] = t.S[u][r];
+  }
+  if (w < G<D, M>::TD && n == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) z[16 * w + 4 * g + r] = t.Z[r];
+  }
+}
+
+// Exact float32 increment of block p computed straight from global memory
+// (the look-back fallback; never needed when predecessors make progress).
+template <int D, int M>
+__device__ void block_increment_direct(Tiles<D, M>& acc, const bf16_t* kh, const bf16_t* vh, int t0, int t1, int w,
+                                       int n, int g) {
+  for (int j = t0; j < t1; ++j) {
+#pragma unroll
+    for (int u = 0; u < G<D, M>::TMW; ++u) {
+      int td, tm;
+      tile_coords<D, M>(w, u, td, tm);
+      const float vm = bf2f(vh[(size_t)j * M + 16 * tm + n]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc.S[u][r] += phi(bf2f(kh[(size_t)j * D + 16 * td + 4 * g + r])) * vm;
+    }
+    if (w < G<D, M>::TD) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc.Z[r] += phi(bf2f(kh[(size_t)j * D + 16 * w + 4 * g + r]));
+    }
+  }
+}
+
+__device__ __forceinline__ unsigned long long rt_clock() { return __builtin_amdgcn_s_memrealtime(); }
+
+template <int D, int M>
+__global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, bf16_t* __restrict__ o,
+    int N, int nblk, int BH, const float* S0, const float* z0, float* S_out, float* z_out,
+    unsigned long long* flags, char* agg_ws, char* incl_ws, unsigned long long epoch, unsigned long long spin_ticks) {
+  using GG = G<D, M>;
+  __shared__ Smem<D, M> sm;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
+  // Block-major order: all heads' block 0 first; a block's predecessor has a
+  // smaller workgroup index (and, with BH a multiple of 8, runs on the same XCD).
+  const int b = blockIdx.x / BH, bh = blockIdx.x % BH;
+  const int t0 = b * TBLK, t1 = min(N, t0 + TBLK);
+  const int ntok = t1 - t0;
+  const int nch = (ntok + CH - 1) / CH;
+  const bf16_t* kh = k + (size_t)bh * N * D;
+  const bf16_t* vh = v + (size_t)bh * N * M;
+  const bf16_t* qh = q + (size_t)bh * N * D;
+
+  // ---------------- phase 1: load K, V of the whole block ----------------
+  constexpr int KV = CH * D * 2 / 16 / NT;  // 16-byte vectors per thread per chunk
+  constexpr int VV = CH * M * 2 / 16 / NT;
+  u32x4 rk[NCH][KV], rv[NCH][VV];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+    for (int i = 0; i < KV; ++i) {
+      const int p = tid + NT * i, row = p / GG::UK, cu = p % GG::UK;
+      const int t = c * CH + row;
+      rk[c][i] = t < ntok ? *reinterpret_cast<const u32x4*>(kh + (size_t)(t0 + t) * D + cu * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < VV; ++i) {
+      const int p = tid + NT * i, row = p / GG::UV, cu = p % GG::UV;
+      const int t = c * CH + row;
+      rv[c][i] = t < ntok ? *reinterpret_cast<const u32x4*>(vh + (size_t)(t0 + t) * M + cu * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  Tiles<D, M> L;  // running local state of the block (float32)
+  tiles_zero<D, M>(L);
+  Tiles<D, M> snap[NCH];  // exclusive local prefix at every chunk start
+  const bf16x8 ones = ones8();
+  const int td = w % GG::TD;
+
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    snap[c] = L;
+    if (c < nch) {
+      // phi(K): head into the resident tile, tail into the staging tile.
+#pragma unroll
+      for (int i = 0; i < KV; ++i) {
+        const int p = tid + NT * i, row = p / GG::UK, cu = p % GG::UK;
+        const int t = c * CH + row;
+        const bool ok = t < ntok;
+        u32x4 hv, lv;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const uint32_t wd = rk[c][i][h];
+          const float a = ok ? phi(lo_of(wd)) : 0.f, bb = ok ? phi(hi_of(wd)) : 0.f;
+          const uint32_t hp = cvt_pk(a, bb);
+          hv[h] = hp;
+          lv[h] = cvt_pk(a - lo_of(hp), bb - hi_of(hp));
+        }
+        *reinterpret_cast<u32x4*>(&sm.K[swz<GG::UK>(t, cu * 8)]) = hv;
+        *reinterpret_cast<u32x4*>(&sm.u.Kl[swz<GG::UK>(row, cu * 8)]) = lv;
+      }
+#pragma unroll
+      for (int i = 0; i < VV; ++i) {
+        const int p = tid + NT * i, row = p / GG::UV, cu = p % GG::UV;
+        *reinterpret_cast<u32x4*>(&sm.V[swz<GG::UV>(c * CH + row, cu * 8)]) = rv[c][i];
+      }
+      __syncthreads();
+      // L += phi(K_c)^T V_c (head and tail), z += colsum phi(K_c).
+#pragma unroll
+      for (int s = 0; s < CH / 32; ++s) {
+        const bf16x8 ah = jfrag<GG::UK>(sm.K, c * CH + 32 * s, 16 * td, g, n);
+        const bf16x8 al = jfrag<GG::UK>(sm.u.Kl, 32 * s, 16 * td, g, n);
+#pragma unroll
+        for (int u = 0; u < GG::TMW; ++u) {
+          int tdd, tm;
+          tile_coords<D, M>(w, u, tdd, tm);
+          const bf16x8 bv = jfrag<GG::UV>(sm.V, c * CH + 32 * s, 16 * tm, g, n);
+          L.S[u] = mma(ah, bv, L.S[u]);
+          L.S[u] = mma(al, bv, L.S[u]);
+        }
+        if (w < GG::TD) {
+          L.Z = mma(ah, ones, L.Z);
+          L.Z = mma(al, ones, L.Z);
+        }
+      }
+      __syncthreads();  // the staging tile is rewritten by the next chunk
+    }
+  }
+
+  // Prefetch phase 3's queries (raw bits; phi is applied per chunk).
+  constexpr int QV = D / 32;
+  u32x4 rq[NCH][QV];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int i = c * CH + 16 * w + n;
+#pragma unroll
+    for (int s = 0; s < QV; ++s)
+      rq[c][s] = (o && i < ntok) ? *reinterpret_cast<const u32x4*>(qh + (size_t)(t0 + i) * D + 32 * s + 8 * g)
+                                 : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  // ---------------- phase 2: exclusive prefix of the block ----------------
+  // P_b is the left fold S0 + a_0 + a_1 + ... + a_{b-1} of the block
+  // increments a_j, evaluated in that order whatever the timing: the block
+  // starts from the nearest published inclusive prefix (itself such a fold)
+  // and adds the later increments in forward order.  Results are therefore
+  // bitwise repeatable; only the never-expected fallback (a predecessor that
+  // publishes nothing within the spin bound) computes increments differently.
+  Tiles<D, M> P;
+  tiles_zero<D, M>(P);
+  const size_t slot = (size_t)bh * nblk + b;
+  if (b > 0) {
+    slot_store<D, M>(agg_ws + slot * GG::SLOT, L, w, lane, n, g);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's stores are complete
+    __syncthreads();
+    if (tid == 0)
+      __hip_atomic_store(&flags[slot], (epoch << 2) | 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+    // Wave 0 polls up to 64 predecessors at once: it needs the nearest one
+    // with an inclusive prefix and every block after it with its increment.
+    if (w == 0) {
+      const int W = b < 64 ? b : 64;
+      const unsigned long long inwin = W >= 64 ? ~0ull : ((1ull << W) - 1);
+      int pstar = -4;  // -4: timeout, -3: no inclusive prefix within the window
+      const unsigned long long start = rt_clock();
+      for (int it = 0; it < (1 << 20); ++it) {
+        int st = 0;
+        if (lane < W) {
+          const unsigned long long f =
+              __hip_atomic_load(&flags[(size_t)bh * nblk + (b - 1 - lane)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          st = (f >> 2) == epoch ? (int)(f & 3ull) : 0;
+        }
+        const unsigned long long incl = __ballot(st == 2) & inwin;
+        const unsigned long long ready = __ballot(st >= 1) & inwin;
+        const int first = incl ? __builtin_ctzll(incl) : W;
+        const unsigned long long need = first >= 64 ? inwin : ((1ull << first) - 1);
+        if ((ready & need) == need) {
+          pstar = first < W ? b - 1 - first : -3;
+          break;
+        }
+        if (rt_clock() - start > spin_ticks) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      if (lane == 0) sm.status = pstar;
+    }
+    __syncthreads();
+    const int pstar = sm.status;
+    if (pstar >= 0) {
+      slot_load<D, M>(P, incl_ws + ((size_t)bh * nblk + pstar) * GG::SLOT, w, lane, g);
+      int j = pstar + 1;
+      for (; j + 4 <= b; j += 4) {  // four loads in flight, added in order
+        Tiles<D, M> a0, a1, a2, a3;
+        slot_load<D, M>(a0, agg_ws + ((size_t)bh * nblk + j) * GG::SLOT, w, lane, g);
+        slot_load<D, M>(a1, agg_ws + ((size_t)bh * nblk + j + 1) * GG::SLOT, w, lane, g);
+        slot_load<D, M>(a2, agg_ws + ((size_t)bh * nblk + j + 2) * GG::SLOT, w, lane, g);
+        slot_load<D, M>(a3, agg_ws + ((size_t)bh * nblk + j + 3) * GG::SLOT, w, lane, g);
+        tiles_acc<D, M>(P, a0);
+        tiles_acc<D, M>(P, a1);
+        tiles_acc<D, M>(P, a2);
+        tiles_acc<D, M>(P, a3);
+      }
+      for (; j < b; ++j) {
+        Tiles<D, M> a0;
+        slot_load<D, M>(a0, agg_ws + ((size_t)bh * nblk + j) * GG::SLOT, w, lane, g);
+        tiles_acc<D, M>(P, a0);
+      }
+    } else {
+      // Slow path: walk back one block at a time with a bounded wait each,
+      // computing an increment directly when its block has published nothing.
+      bool done = false;
+      for (int p = b - 1; p >= 0 && !done; --p) {
+        __syncthreads();  // everyone has read sm.status
+        if (tid == 0) {
+          int st = 0;
+          const unsigned long long start = rt_clock();
+          for (int it = 0; it < (1 << 20); ++it) {
+            const unsigned long long f =
+                __hip_atomic_load(&flags[(size_t)bh * nblk + p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if ((f >> 2) == epoch && (f & 3ull) != 0) {
+              st = (int)(f & 3ull);
+              break;
+            }
+            if (rt_clock() - start > spin_ticks) break;
+            __builtin_amdgcn_s_sleep(2);
+          }
+          sm.status = st;
+        }
+        __syncthreads();
+        const int st = sm.status;
+        const size_t ps = (size_t)bh * nblk + p;
+        Tiles<D, M> a0;
+        if (st == 2) {
+          slot_load<D, M>(a0, incl_ws + ps * GG::SLOT, w, lane, g);
+          done = true;
+        } else if (st == 1) {
+          slot_load<D, M>(a0, agg_ws + ps * GG::SLOT, w, lane, g);
+        } else {
+          tiles_zero<D, M>(a0);
+          block_increment_direct<D, M>(a0, kh, vh, p * TBLK, min(N, (p + 1) * TBLK), w, n, g);
+        }
+        tiles_acc<D, M>(P, a0);
+      }
+      if (!done && S0) tiles_add_from_state<D, M>(P, S0 + (size_t)bh * D * M, z0 + (size_t)bh * D, w, n, g);
+    }
+  } else if (S0) {
+    tiles_add_from_state<D, M>(P, S0 + (size_t)bh * D * M, z0 + (size_t)bh * D, w, n, g);
+  }
+
+  {
+    Tiles<D, M> inc;
+#pragma unroll
+    for (int u = 0; u < GG::TMW; ++u) inc.S[u] = P.S[u] + L.S[u];
+    inc.Z = P.Z + L.Z;
+    if (b == nblk - 1) {
+      if (S_out) tiles_store<D, M>(inc, S_out + (size_t)bh * D * M, z_out + (size_t)bh * D, w, n, g);
+    } else {
+      slot_store<D, M>(incl_ws + slot * GG::SLOT, inc, w, lane, n, g);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tid == 0)
+        __hip_atomic_store(&flags[slot], (epoch << 2) | 2ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  if (!o) return;
+
+  // ---------------- phase 3: outputs ----------------
+  bf16_t* oh = o + (size_t)bh * N * M;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    if (c >= nch) break;
+    __syncthreads();  // previous readers of St / Zs are done
+    // state at the chunk start: P + local prefix, published as the S^T operand
+#pragma unroll
+    for (int u = 0; u < GG::TMW; ++u) {
+      int tdd, tm;
+      tile_coords<D, M>(w, u, tdd, tm);
+      const f32x4 x = P.S[u] + snap[c].S[u];
+      *reinterpret_cast<u32x2*>(&sm.u.St[swz<GG::UK>(16 * tm + n, 16 * tdd + 4 * g)]) =
+          u32x2{cvt_pk(x[0], x[1]), cvt_pk(x[2], x[3])};
+    }
+    if (w < GG::TD && n == 0) *reinterpret_cast<f32x4*>(&sm.Zs[16 * w + 4 * g]) = P.Z + snap[c].Z;
+    __syncthreads();
+
+    // phi(Q) fragments of this wave's 16 rows.
+    bf16x8 qf[QV];
+#pragma unroll
+    for (int s = 0; s < QV; ++s) {
+      u32x4 pk;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const uint32_t wd = rq[c][s][h];
+        pk[h] = cvt_pk(phi(lo_of(wd)), phi(hi_of(wd)));
+      }
+      qf[s] = as_bf16x8(pk);
+    }
+
+    f32x4 num[GG::TM];
+#pragma unroll
+    for (int tm = 0; tm < GG::TM; ++tm) num[tm] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 den{0.f, 0.f, 0.f, 0.f};
+
+    // Scores A^T[j][i] = phi(k_j).phi(q_i), j-tiles t <= w, masked on the diagonal.
+    f32x4 at[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      at[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (t <= w) {
+#pragma unroll
+        for (int s = 0; s < QV; ++s) {
+          const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.K[swz<GG::UK>(c * CH + 16 * t + n, 32 * s + 8 * g)]));
+          at[t] = mma(a, qf[s], at[t]);
+        }
+        if (t == w) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (4 * g + r > n) at[t][r] = 0.f;
+        }
+      }
+    }
+    // Intra-chunk: num += P V, den += P 1.
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if (2 * s <= w) {
+        const bf16x8 pf = as_bf16x8(u32x4{cvt_pk(at[2 * s][0], at[2 * s][1]), cvt_pk(at[2 * s][2], at[2 * s][3]),
+                                          cvt_pk(at[2 * s + 1][0], at[2 * s + 1][1]),
+                                          cvt_pk(at[2 * s + 1][2], at[2 * s + 1][3])});
+#pragma unroll
+        for (int tm = 0; tm < GG::TM; ++tm) {
+          const bf16x8 bv = jfrag<GG::UV>(sm.V, c * CH + 32 * s, 16 * tm, g, n);
+          num[tm] = mma(pf, bv, num[tm]);
+        }
+        den = mma(pf, ones, den);
+      }
+    }
+    // Inter-chunk: num += phi(Q) S, den += phi(Q) z (z as a bf16 head + tail).
+#pragma unroll
+    for (int s = 0; s < QV; ++s) {
+#pragma unroll
+      for (int tm = 0; tm < GG::TM; ++tm) {
+        const bf16x8 bs = as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.u.St[swz<GG::UK>(16 * tm + n, 32 * s + 8 * g)]));
+        num[tm] = mma(qf[s], bs, num[tm]);
+      }
+      const f32x4 za = *reinterpret_cast<const f32x4*>(&sm.Zs[32 * s + 8 * g]);
+      const f32x4 zb = *reinterpret_cast<const f32x4*>(&sm.Zs[32 * s + 8 * g + 4]);
+      uint32_t zh[4], zl[4];
+      zh[0] = cvt_pk(za[0], za[1]);
+      zh[1] = cvt_pk(za[2], za[3]);
+      zh[2] = cvt_pk(zb[0], zb[1]);
+      zh[3] = cvt_pk(zb[2], zb[3]);
+      zl[0] = cvt_pk(za[0] - lo_of(zh[0]), za[1] - hi_of(zh[0]));
+      zl[1] = cvt_pk(za[2] - lo_of(zh[1]), za[3] - hi_of(zh[1]));
+      zl[2] = cvt_pk(zb[0] - lo_of(zh[2]), zb[1] - hi_of(zh[2]));
+      zl[3] = cvt_pk(zb[2] - lo_of(zh[3]), zb[3] - hi_of(zh[3]));
+      den = mma(qf[s], as_bf16x8(u32x4{zh[0], zh[1], zh[2], zh[3]}), den);
+      den = mma(qf[s], as_bf16x8(u32x4{zl[0], zl[1], zl[2], zl[3]}), den);
+    }
+    // o_i = num_i / den_i: lane (n, g) holds rows 16w + 4g + r, columns 16 tm + n.
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = c * CH + 16 * w + 4 * g + r;
+      if (i < ntok) {
+        const float inv = 1.f / den[r];
+        bf16_t* dst = oh + (size_t)(t0 + i) * M + n;
+#pragma unroll
+        for (int tm = 0; tm < GG::TM; ++tm) dst[16 * tm] = (bf16_t)(cvt_pk(num[tm][r] * inv, 0.f) & 0xffffu);
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Host side.
+struct WsLayout {
+  size_t flags_bytes, slot_bytes, init_bytes, total;
+};
+
+template <int D, int M>
+static WsLayout layout(long long BH, int N) {
+  const long long nblk = (N + TBLK - 1) / TBLK;
+  WsLayout l;
+  l.flags_bytes = (size_t)((BH * nblk * 8 + 255) / 256 * 256);
+  l.slot_bytes = (size_t)G<D, M>::SLOT;
+  // private copy of an initial state that the call overwrites in place
+  l.init_bytes = (size_t)((BH * (D * M + D) * 4 + 255) / 256 * 256);
+  l.total = l.flags_bytes + 2 * (size_t)(BH * nblk) * l.slot_bytes + l.init_bytes;
+  return l;
+}
+
+// Launch epochs: strictly increasing across calls and, being seeded from the
+// wall clock, across processes, so flags left in a reused workspace by any
+// earlier launch never match the current one.
+static std::atomic<unsigned long long> g_epoch{0};
+
+static unsigned long long next_epoch() {
+  unsigned long long e = g_epoch.load();
+  if (e == 0) {
+    const unsigned long long seed =
+        (unsigned long long)std::chrono::duration_cast<std::chrono::nanoseconds>(
+            std::chrono::system_clock::now().time_since_epoch()).count();
+    unsigned long long expect = 0;
+    g_epoch.compare_exchange_strong(expect, seed & ((1ull << 61) - 1));
+  }
+  return g_epoch.fetch_add(1) + 1;
+}
+
+__global__ __launch_bounds__(256) void copy_state_kernel(const float* S, const float* z, float* S2, float* z2,
+                                                        long long nS, long long nz) {
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (e < nS) S2[e] = S[e];
+  if (e < nz) z2[e] = z[e];
+}
+
+template <int D, int M>
+static hipError_t fused_impl(const void* q, const void* k, const void* v, void* o, int BH, int N, const float* S0,
+                             const float* z0, float* S_out, float* z_out, void* ws, hipStream_t stream) {
+  const int nblk = (N + TBLK - 1) / TBLK;
+  const WsLayout l = layout<D, M>(BH, N);
+  char* base = (char*)ws;
+  unsigned long long* flags = (unsigned long long*)base;
+  char* agg = base + l.flags_bytes;
+  char* incl = agg + (size_t)BH * nblk * l.slot_bytes;
+  if (S0 && nblk > 1 && (S0 == S_out || z0 == z_out)) {
+    // An in-place carry: block 0 reads the initial state while the last block
+    // writes the final one; give the kernel a private copy to read.
+    float* S0c = (float*)(incl + (size_t)BH * nblk * l.slot_bytes);
+    float* z0c = S0c + (size_t)BH * D * M;
+    const long long nS = (long long)BH * D * M, nz = (long long)BH * D;
+    hipLaunchKernelGGL(copy_state_kernel, dim3((unsigned)((nS + 255) / 256)), dim3(256), 0, stream, S0, z0, S0c, z0c,
+                       nS, nz);
+    S0 = S0c;
+    z0 = z0c;
+  }
+  const unsigned long long spin_ticks = 20000;  // 200 us of the 100 MHz real-time counter
+  hipLaunchKernelGGL((causal_fused_kernel<D, M>), dim3((unsigned)nblk * (unsigned)BH), dim3(NT), 0, stream,
+                     (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (bf16_t*)o, N, nblk, BH, S0, z0, S_out,
+                     z_out, flags, agg, incl, next_epoch(), spin_ticks);
+  return hipGetLastError();
+}
+
+template <int D, int M>
+static size_t fused_ws(int BH, int N) {
+  return layout<D, M>(BH, N).total;
+}
+
+}  // namespace fused
+
+size_t causal_fused_ws_bytes(int BH, int N, int D, int M) {
+  if (BH <= 0 || N <= 0) return 0;
+  switch (D * 100 + M) {
+    case 3232: return fused::fused_ws<32, 32>(BH, N);
+    case 3264: return fused::fused_ws<32, 64>(BH, N);
+    case 6432: return fused::fused_ws<64, 32>(BH, N);
+    case 6464: return fused::fused_ws<64, 64>(BH, N);
+    default: return 0;
+  }
+}
+
+hipError_t launch_causal_fused(const void* q, const void* k, const void* v, void* o, int BH, int N, int D, int M,
+                               const float* S0, const float* z0, float* S_out, float* z_out, void* ws,
+                               hipStream_t stream) {
+  using namespace fused;
+  switch (D * 100 + M) {
+    case 3232: return fused_impl<32, 32>(q, k, v, o, BH, N, S0, z0, S_out, z_out, ws, stream);
+    case 3264: return fused_impl<32, 64>(q, k, v, o, BH, N, S0, z0, S_out, z_out, ws, stream);
+    case 6432: return fused_impl<64, 32>(q, k, v, o, BH, N, S0, z0, S_out, z_out, ws, stream);
+    case 6464: return fused_impl<64, 64>(q, k, v, o, BH, N, S0, z0, S_out, z_out, ws, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace la

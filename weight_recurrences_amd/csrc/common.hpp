@@ -1,0 +1,92 @@
+// Device helpers shared by the gfx950 kernels: bf16 conversion, the feature
+// map, MFMA wrappers and wavefront reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace la {
+
+typedef uint16_t bf16_t;  // bfloat16 stored as its raw bits
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf2f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// float -> bfloat16 bits, round to nearest even (NaN stays a quiet NaN).
+// Branch-free: both results are formed and selected.
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t nan = (u >> 16) | 0x40u;
+  return ((u & 0x7fffffffu) > 0x7f800000u) ? nan : r;
+}
+
+// Two floats -> two bf16 packed in one dword (lo in the low half).
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) { return f2bf(lo) | (f2bf(hi) << 16); }
+
+// phi(x) = elu(x) + 1 with alpha = 1 ("Transformers are RNNs", §3.2.1 eq.(7)):
+// x + 1 for x > 0, exp(x) otherwise (the exp form keeps relative accuracy for
+// very negative x).
+__device__ __forceinline__ float phi(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+
+template <typename T> __device__ __forceinline__ float ld_scalar(const T* p);
+template <> __device__ __forceinline__ float ld_scalar<float>(const float* p) { return *p; }
+template <> __device__ __forceinline__ float ld_scalar<bf16_t>(const bf16_t* p) { return bf2f(*p); }
+
+template <typename T> __device__ __forceinline__ T to_elem(float f);
+template <> __device__ __forceinline__ float to_elem<float>(float f) { return f; }
+template <> __device__ __forceinline__ bf16_t to_elem<bf16_t>(float f) { return (bf16_t)f2bf(f); }
+
+// ---- MFMA (16x16 output tiles, 64 lanes: lane = 16*g + n) --------------------
+// A operand: lane (n, g) holds row n, k-slots of group g.  B operand: lane
+// (n, g) holds column n, the same k-slots.  Result: lane (n, g) holds rows
+// 4g..4g+3 of column n (element r of the f32x4).
+__device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// ---- cross-lane reductions ---------------------------------------------------
+// DPP controls (GFX9 encoding).
+constexpr int DPP_XOR1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141; // lane i <- lane 7-i within 8
+constexpr int DPP_MIRROR = 0x140;      // lane i <- lane 15-i within 16
+
+template <int CTRL> __device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each aligned group of 16 lanes; every lane of the group gets it.
+__device__ __forceinline__ float sum16(float x) {
+  x += dpp<DPP_XOR1>(x);
+  x += dpp<DPP_XOR2>(x);
+  x += dpp<DPP_HALF_MIRROR>(x);
+  x += dpp<DPP_MIRROR>(x);
+  return x;
+}
+
+// Sum over each aligned group of 8 lanes.
+__device__ __forceinline__ float sum8(float x) {
+  x += dpp<DPP_XOR1>(x);
+  x += dpp<DPP_XOR2>(x);
+  x += dpp<DPP_HALF_MIRROR>(x);
+  return x;
+}
+
+// Sum over the whole wavefront (all 64 lanes get it).
+__device__ __forceinline__ float wave_sum(float x) {
+  x = sum16(x);
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+}  // namespace la

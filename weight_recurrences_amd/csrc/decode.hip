@@ -1,0 +1,112 @@
+// RNN-form single-token decode step on gfx950.
+//
+// "Transformers are RNNs" (Katharopoulos et al., 2020), translated page
+// "線性變換器", §3.4 eq.(18)-(20): s <- s + phi(k) v^T, z <- z + phi(k),
+// o = phi(q)^T s / phi(q)^T z, the state updated before it is read.
+//
+// The step is a pure state stream: every (b, h) reads and writes its D x M
+// float32 matrix once (16 KiB each way at D = M = 64), so the kernel is bound
+// by HBM bandwidth.  One wavefront owns one (b, h) state; lane l covers the
+// four columns 4*(l % (M/4)) .. +3 of rows d = l / (M/4) + (256/M) * p, so each
+// load instruction of the wave reads 1 KiB of consecutive memory.  The
+// numerator is reduced across the lanes that share columns with cross-lane
+// shuffles; the denominator is a full-wave sum of phi(q)_d z_d.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace la {
+
+template <typename T> __device__ __forceinline__ float4 load4(const T* p);
+template <> __device__ __forceinline__ float4 load4<float>(const float* p) { return *reinterpret_cast<const float4*>(p); }
+template <> __device__ __forceinline__ float4 load4<bf16_t>(const bf16_t* p) {
+  const uint2 w = *reinterpret_cast<const uint2*>(p);
+  return float4{bf2f(w.x & 0xffffu), bf2f(w.x >> 16), bf2f(w.y & 0xffffu), bf2f(w.y >> 16)};
+}
+template <typename T> __device__ __forceinline__ void store4(T* p, float4 x);
+template <> __device__ __forceinline__ void store4<float>(float* p, float4 x) { *reinterpret_cast<float4*>(p) = x; }
+template <> __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, float4 x) {
+  *reinterpret_cast<uint2*>(p) = uint2{pack_bf2(x.x, x.y), pack_bf2(x.z, x.w)};
+}
+
+template <typename T, int D, int M>
+__global__ __launch_bounds__(256) void decode_step_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                          const T* __restrict__ v, T* __restrict__ o,
+                                                          float* __restrict__ S, float* __restrict__ z, int BH) {
+  constexpr int LPR = M / 4;     // lanes per state row
+  constexpr int RPP = 64 / LPR;  // rows per pass
+  constexpr int NP = D / RPP;    // passes
+  const int lane = threadIdx.x & 63;
+  const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (bh >= BH) return;  // whole wavefront; the kernel has no barrier
+  const int mc = lane % LPR, r0 = lane / LPR;
+
+  float pk = 0.f, pq = 0.f;
+  if (lane < D) {
+    pk = phi(ld_scalar<T>(k + (size_t)bh * D + lane));
+    pq = phi(ld_scalar<T>(q + (size_t)bh * D + lane));
+  }
+  const float4 vv = load4<T>(v + (size_t)bh * M + 4 * mc);
+
+  float* Sh = S + (size_t)bh * D * M + 4 * mc;
+  float4 s[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) s[p] = *reinterpret_cast<const float4*>(Sh + (size_t)(r0 + RPP * p) * M);
+
+  float4 acc{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int d = r0 + RPP * p;
+    const float kd = __shfl(pk, d);
+    const float qd = __shfl(pq, d);
+    s[p].x += kd * vv.x;
+    s[p].y += kd * vv.y;
+    s[p].z += kd * vv.z;
+    s[p].w += kd * vv.w;
+    acc.x += qd * s[p].x;
+    acc.y += qd * s[p].y;
+    acc.z += qd * s[p].z;
+    acc.w += qd * s[p].w;
+  }
+#pragma unroll
+  for (int p = 0; p < NP; ++p) *reinterpret_cast<float4*>(Sh + (size_t)(r0 + RPP * p) * M) = s[p];
+
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1) {
+    acc.x += __shfl_xor(acc.x, off);
+    acc.y += __shfl_xor(acc.y, off);
+    acc.z += __shfl_xor(acc.z, off);
+    acc.w += __shfl_xor(acc.w, off);
+  }
+
+  float zd = 0.f;
+  if (lane < D) {
+    zd = z[(size_t)bh * D + lane] + pk;
+    z[(size_t)bh * D + lane] = zd;
+  }
+  const float den = wave_sum(pq * zd);
+  if (r0 == 0) {
+    const float inv = 1.f / den;
+    store4<T>(o + (size_t)bh * M + 4 * mc, float4{acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv});
+  }
+}
+
+template <typename T, int D, int M>
+static hipError_t decode_impl(const void* q, const void* k, const void* v, void* o, float* S, float* z, int BH,
+                              hipStream_t stream) {
+  const unsigned nb = (unsigned)((BH + 3) / 4);
+  hipLaunchKernelGGL((decode_step_kernel<T, D, M>), dim3(nb), dim3(256), 0, stream, (const T*)q, (const T*)k,
+                     (const T*)v, (T*)o, S, z, BH);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const void* q, const void* k, const void* v, void* o, float* S, float* z, int BH, int D,
+                         int M, int bf16, hipStream_t stream) {
+  if (BH == 0) return hipSuccess;
+  if (bf16) {
+    LA_DISPATCH_DM(decode_impl, bf16_t, q, k, v, o, S, z, BH, stream)
+  } else {
+    LA_DISPATCH_DM(decode_impl, float, q, k, v, o, S, z, BH, stream)
+  }
+}
+
+}  // namespace la

@@ -1,0 +1,196 @@
+// Delta-rule fast-weight memory on gfx950.
+//
+// News summary of "Linear Transformers Are Secretly Fast Weight Programmers"
+// (Schlag, Irie, Schmidhuber, 2021), paragraphs on the new update rule and on
+// normalisation: for each token, retrieve the value currently bound to the
+// key, vbar = W kh, and replace it by the convex combination
+// beta v + (1 - beta) vbar, i.e. W += beta (v - vbar) kh^T; keys and queries
+// pass through phi = elu + 1 and are divided by the sum of their components;
+// the output reads the updated memory, o = W qh.
+//
+// Rows of W are independent chains (row m only ever sees v_m), so the memory of
+// a (b, h) is split over workgroups of 16 rows: 4 wavefronts x 4 rows, 16
+// lanes per row, D/16 consecutive elements of the row per lane, all in
+// registers.  The token loop is inherently sequential; what does not depend on
+// W (phi, the sum normalisation of k and q, the loads) is computed for a block
+// of 64 tokens at a time by the whole workgroup and staged in LDS, with the
+// next block's global loads in flight during the sequential phase.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace la {
+
+constexpr int DTB = 64;  // tokens per staged block
+
+template <typename T, int D, int M>
+__global__ __launch_bounds__(256) void deltanet_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                       const T* __restrict__ v, const T* __restrict__ beta,
+                                                       T* __restrict__ o, int N, const float* W0, float* W_out) {
+  constexpr int DPL = D / 16;   // elements of a row per lane
+  constexpr int UPT = D / 4;    // 4-element units per token row of k/q
+  constexpr int NU = DTB * UPT; // units per block
+  constexpr int KU = (NU + 255) / 256;
+  __shared__ float Kh[DTB][D + 4];
+  __shared__ float Qh[DTB][D + 4];
+  __shared__ float Vs[DTB][16];
+  __shared__ float Bs[DTB];
+  __shared__ float Os[DTB][17];
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, rl = lane >> 4;
+  const int rg = blockIdx.x % (M / 16), bh = blockIdx.x / (M / 16);
+  const int m = 16 * rg + 4 * w + rl;  // memory row owned by this lane group
+
+  const T* qh = q + (size_t)bh * N * D;
+  const T* kh = k + (size_t)bh * N * D;
+  const T* vh = v + (size_t)bh * N * M;
+  const T* bhp = beta + (size_t)bh * N;
+  T* oh = o + (size_t)bh * N * M;
+
+  float W[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) W[e] = W0 ? W0[((size_t)bh * M + m) * D + n * DPL + e] : 0.f;
+
+  // Register prefetch of one block: k, q units, one v unit, one beta.
+  float4 rk[KU], rq[KU], rv;
+  float rb;
+  auto prefetch = [&](int t0, int nt) {
+#pragma unroll
+    for (int i = 0; i < KU; ++i) {
+      const int u = tid + 256 * i;
+      const int tok = u / UPT, d4 = (u % UPT) * 4;
+      rk[i] = rq[i] = float4{0.f, 0.f, 0.f, 0.f};
+      if (u < NU && tok < nt) {
+        const size_t off = (size_t)(t0 + tok) * D + d4;
+        if constexpr (sizeof(T) == 2) {
+          const uint2 a = *reinterpret_cast<const uint2*>(kh + off);
+          const uint2 b = *reinterpret_cast<const uint2*>(qh + off);
+          rk[i] = float4{bf2f(a.x & 0xffffu), bf2f(a.x >> 16), bf2f(a.y & 0xffffu), bf2f(a.y >> 16)};
+          rq[i] = float4{bf2f(b.x & 0xffffu), bf2f(b.x >> 16), bf2f(b.y & 0xffffu), bf2f(b.y >> 16)};
+        } else {
+          rk[i] = *reinterpret_cast<const float4*>(kh + off);
+          rq[i] = *reinterpret_cast<const float4*>(qh + off);
+        }
+      }
+    }
+    {  // v: 64 tokens x 16 rows = 256 units of 4
+      const int tok = tid >> 2, c4 = (tid & 3) * 4;
+      rv = float4{0.f, 0.f, 0.f, 0.f};
+      if (tok < nt) {
+        const T* src = vh + (size_t)(t0 + tok) * M + 16 * rg + c4;
+        rv = float4{ld_scalar<T>(src), ld_scalar<T>(src + 1), ld_scalar<T>(src + 2), ld_scalar<T>(src + 3)};
+      }
+    }
+    rb = (tid < nt) ? ld_scalar<T>(bhp + t0 + tid) : 0.f;
+  };
+
+  prefetch(0, min(DTB, N));
+  for (int t0 = 0; t0 < N; t0 += DTB) {
+    const int nt = min(DTB, N - t0);
+    // Stage: kh = phi(k)/sum phi(k), qh likewise (lanes of one token row are an
+    // aligned group of UPT lanes).
+#pragma unroll
+    for (int i = 0; i < KU; ++i) {
+      const int u = tid + 256 * i;
+      if (u < NU) {  // uniform per group of UPT lanes
+        const int tok = u / UPT, d4 = (u % UPT) * 4;
+        float4 a{phi(rk[i].x), phi(rk[i].y), phi(rk[i].z), phi(rk[i].w)};
+        float4 b{phi(rq[i].x), phi(rq[i].y), phi(rq[i].z), phi(rq[i].w)};
+        float sa = a.x + a.y + a.z + a.w, sb = b.x + b.y + b.z + b.w;
+        if constexpr (UPT == 16) {
+          sa = sum16(sa);
+          sb = sum16(sb);
+        } else {
+          sa = sum8(sa);
+          sb = sum8(sb);
+        }
+        const float ia = 1.f / sa, ib = 1.f / sb;
+        *reinterpret_cast<float4*>(&Kh[tok][d4]) = float4{a.x * ia, a.y * ia, a.z * ia, a.w * ia};
+        *reinterpret_cast<float4*>(&Qh[tok][d4]) = float4{b.x * ib, b.y * ib, b.z * ib, b.w * ib};
+      }
+    }
+    {
+      const int tok = tid >> 2, c4 = (tid & 3) * 4;
+      Vs[tok][c4 + 0] = rv.x;
+      Vs[tok][c4 + 1] = rv.y;
+      Vs[tok][c4 + 2] = rv.z;
+      Vs[tok][c4 + 3] = rv.w;
+    }
+    if (tid < DTB) Bs[tid] = rb;
+    __syncthreads();
+    if (t0 + DTB < N) prefetch(t0 + DTB, min(DTB, N - t0 - DTB));
+
+    // Sequential phase: one memory row per 16-lane group.
+    for (int i = 0; i < nt; ++i) {
+      float kv[DPL], qv[DPL];
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) {
+        kv[e] = Kh[i][n * DPL + e];
+        qv[e] = Qh[i][n * DPL + e];
+      }
+      const float vm = Vs[i][4 * w + rl];
+      const float b = Bs[i];
+      float p = 0.f;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) p += W[e] * kv[e];
+      const float vbar = sum16(p);          // retrieve
+      const float c = b * (vm - vbar);      // beta (v - vbar)
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) W[e] += c * kv[e];  // write
+      float po = 0.f;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) po += W[e] * qv[e];
+      const float om = sum16(po);           // read with the updated memory
+      if (n == 0) Os[i][4 * w + rl] = om;
+    }
+    __syncthreads();
+    {  // coalesced output of the block's 16 columns
+      const int tok = tid >> 2, c4 = (tid & 3) * 4;
+      if (tok < nt) {
+        T* dst = oh + (size_t)(t0 + tok) * M + 16 * rg + c4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[e] = to_elem<T>(Os[tok][c4 + e]);
+      }
+    }
+    // The next staging writes Kh/Qh/Vs/Bs only after every wave has passed the
+    // barrier above, i.e. finished reading them; Os is rewritten only after the
+    // next block's sequential phase, behind the next barrier.
+    __syncthreads();
+  }
+  if (W_out) {
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) W_out[((size_t)bh * M + m) * D + n * DPL + e] = W[e];
+  }
+}
+
+template <typename T, int D, int M>
+static hipError_t deltanet_impl(const void* q, const void* k, const void* v, const void* beta, void* o, int BH,
+                                int N, const float* W0, float* W_out, hipStream_t stream) {
+  const unsigned nb = (unsigned)BH * (M / 16);
+  hipLaunchKernelGGL((deltanet_kernel<T, D, M>), dim3(nb), dim3(256), 0, stream, (const T*)q, (const T*)k,
+                     (const T*)v, (const T*)beta, (T*)o, N, W0, W_out);
+  return hipGetLastError();
+}
+
+// Copies W0 to W_out, or zero-fills it (empty sequence).
+__global__ __launch_bounds__(256) void memory_copy_kernel(const float* W0, float* W_out, long long n) {
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (e < n) W_out[e] = W0 ? W0[e] : 0.f;
+}
+
+hipError_t launch_deltanet(const void* q, const void* k, const void* v, const void* beta, void* o, int BH, int N,
+                           int D, int M, int bf16, const float* W0, float* W_out, hipStream_t stream) {
+  if (BH == 0) return hipSuccess;
+  if (N == 0) {
+    if (!W_out) return hipSuccess;
+    const long long n = (long long)BH * M * D;
+    hipLaunchKernelGGL(memory_copy_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, W0, W_out, n);
+    return hipGetLastError();
+  }
+  if (bf16) {
+    LA_DISPATCH_DM(deltanet_impl, bf16_t, q, k, v, beta, o, BH, N, W0, W_out, stream)
+  } else {
+    LA_DISPATCH_DM(deltanet_impl, float, q, k, v, beta, o, BH, N, W0, W_out, stream)
+  }
+}
+
+}  // namespace la

@@ -1,0 +1,40 @@
+// Internal launcher interface between the C ABI (abi.cpp) and the kernels.
+// Arguments are validated by the caller; these only enqueue work on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+// Instantiates FN<T, D, M> for the built (D, M) set {32, 64} x {32, 64}.
+#define LA_DISPATCH_DM(FN, T, ...)                \
+  switch (D * 100 + M) {                          \
+    case 3232: return FN<T, 32, 32>(__VA_ARGS__); \
+    case 3264: return FN<T, 32, 64>(__VA_ARGS__); \
+    case 6432: return FN<T, 64, 32>(__VA_ARGS__); \
+    case 6464: return FN<T, 64, 64>(__VA_ARGS__); \
+    default: return hipErrorInvalidValue;         \
+  }
+
+namespace la {
+
+// Tokens per sequence block of the causal / non-causal kernels.
+int causal_block_tokens(int BH, int N);
+size_t causal_ws_bytes(int BH, int N, int D, int M, int bf16);
+size_t noncausal_ws_bytes(int BH, int N, int D, int M);
+
+hipError_t launch_causal(const void* q, const void* k, const void* v, void* o, int BH, int N, int D, int M,
+                         int bf16, const float* S0, const float* z0, float* S_out, float* z_out, void* ws,
+                         hipStream_t stream);
+// Single-pass bf16 causal path (one launch).
+size_t causal_fused_ws_bytes(int BH, int N, int D, int M);
+hipError_t launch_causal_fused(const void* q, const void* k, const void* v, void* o, int BH, int N, int D, int M,
+                               const float* S0, const float* z0, float* S_out, float* z_out, void* ws,
+                               hipStream_t stream);
+hipError_t launch_noncausal(const void* q, const void* k, const void* v, void* o, int BH, int N, int D, int M,
+                            int bf16, void* ws, hipStream_t stream);
+hipError_t launch_decode(const void* q, const void* k, const void* v, void* o, float* S, float* z, int BH, int D,
+                         int M, int bf16, hipStream_t stream);
+hipError_t launch_deltanet(const void* q, const void* k, const void* v, const void* beta, void* o, int BH, int N,
+                           int D, int M, int bf16, const float* W0, float* W_out, hipStream_t stream);
+
+}  // namespace la
