@@ -169,7 +169,7 @@ def main():
             ws = torch.empty(max(1, la.causal_workspace_bytes(w.B, w.H, w.N, w.D, w.M, w.dtype)),
                              dtype=torch.uint8, device=dev)
             step = lambda: la.causal(q, k, v, out=o, workspace=ws)
-            kernel = "linattn_causal_fwd (block_state + state_scan + causal_sweep)"
+            kernel = ("causal_fused_kernel (single pass)" if w.dtype == torch.bfloat16 else "linattn_causal_fwd (block_state + state_scan + causal_sweep)")
         units = w.B * w.H * w.N                      # tokens per step
         es = torch.tensor([], dtype=w.dtype).element_size()
         alg_bytes = units * (2 * w.D + 2 * w.M) * es  # read q, k, v; write o

@@ -72,7 +72,7 @@ struct G {
 };
 
 template <int D, int M>
-struct Smem {
+struct alignas(16) Smem {
   bf16_t K[TBLK * D];   // phi(K) head, row-major, swizzled
   bf16_t V[TBLK * M];   // V, row-major, swizzled
   union {
@@ -88,6 +88,21 @@ template <int U>
 __device__ __forceinline__ int swz(int row, int col) {
   const int unit = (col >> 3) ^ ((row ^ (row >> 3)) & (U - 1));
   return row * U * 8 + unit * 8 + (col & 7);
+}
+
+// 16-byte unit (row, col..col+7) of a swizzled tile; col is a multiple of 8.
+template <int U>
+__device__ __forceinline__ u32x4& unit16(bf16_t* tile, int row, int col) {
+  return reinterpret_cast<u32x4*>(tile)[swz<U>(row, col) >> 3];
+}
+template <int U>
+__device__ __forceinline__ const u32x4& unit16(const bf16_t* tile, int row, int col) {
+  return reinterpret_cast<const u32x4*>(tile)[swz<U>(row, col) >> 3];
+}
+// 8-byte half unit (row, col..col+3); col is a multiple of 4.
+template <int U>
+__device__ __forceinline__ u32x2& unit8(bf16_t* tile, int row, int col) {
+  return reinterpret_cast<u32x2*>(tile)[swz<U>(row, col) >> 2];
 }
 
 __device__ __forceinline__ uint32_t cvt_pk(float lo, float hi) {
@@ -315,13 +330,13 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
           hv[h] = hp;
           lv[h] = cvt_pk(a - lo_of(hp), bb - hi_of(hp));
         }
-        *reinterpret_cast<u32x4*>(&sm.K[swz<GG::UK>(t, cu * 8)]) = hv;
-        *reinterpret_cast<u32x4*>(&sm.u.Kl[swz<GG::UK>(row, cu * 8)]) = lv;
+        unit16<GG::UK>(sm.K, t, cu * 8) = hv;
+        unit16<GG::UK>(sm.u.Kl, row, cu * 8) = lv;
       }
 #pragma unroll
       for (int i = 0; i < VV; ++i) {
         const int p = tid + NT * i, row = p / GG::UV, cu = p % GG::UV;
-        *reinterpret_cast<u32x4*>(&sm.V[swz<GG::UV>(c * CH + row, cu * 8)]) = rv[c][i];
+        unit16<GG::UV>(sm.V, c * CH + row, cu * 8) = rv[c][i];
       }
       __syncthreads();
       // L += phi(K_c)^T V_c (head and tail), z += colsum phi(K_c).
@@ -494,8 +509,7 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
       int tdd, tm;
       tile_coords<D, M>(w, u, tdd, tm);
       const f32x4 x = P.S[u] + snap[c].S[u];
-      *reinterpret_cast<u32x2*>(&sm.u.St[swz<GG::UK>(16 * tm + n, 16 * tdd + 4 * g)]) =
-          u32x2{cvt_pk(x[0], x[1]), cvt_pk(x[2], x[3])};
+      unit8<GG::UK>(sm.u.St, 16 * tm + n, 16 * tdd + 4 * g) = u32x2{cvt_pk(x[0], x[1]), cvt_pk(x[2], x[3])};
     }
     if (w < GG::TD && n == 0) *reinterpret_cast<f32x4*>(&sm.Zs[16 * w + 4 * g]) = P.Z + snap[c].Z;
     __syncthreads();
@@ -526,7 +540,7 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
       if (t <= w) {
 #pragma unroll
         for (int s = 0; s < QV; ++s) {
-          const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.K[swz<GG::UK>(c * CH + 16 * t + n, 32 * s + 8 * g)]));
+          const bf16x8 a = as_bf16x8(unit16<GG::UK>((const bf16_t*)sm.K, c * CH + 16 * t + n, 32 * s + 8 * g));
           at[t] = mma(a, qf[s], at[t]);
         }
         if (t == w) {
@@ -556,7 +570,7 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
     for (int s = 0; s < QV; ++s) {
 #pragma unroll
       for (int tm = 0; tm < GG::TM; ++tm) {
-        const bf16x8 bs = as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.u.St[swz<GG::UK>(16 * tm + n, 32 * s + 8 * g)]));
+        const bf16x8 bs = as_bf16x8(unit16<GG::UK>((const bf16_t*)sm.u.St, 16 * tm + n, 32 * s + 8 * g));
         num[tm] = mma(qf[s], bs, num[tm]);
       }
       const f32x4 za = *reinterpret_cast<const f32x4*>(&sm.Zs[32 * s + 8 * g]);
@@ -578,7 +592,7 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
     for (int r = 0; r < 4; ++r) {
       const int i = c * CH + 16 * w + 4 * g + r;
       if (i < ntok) {
-        const float inv = 1.f / den[r];
+        const float inv = __builtin_amdgcn_rcpf(den[r]);
         bf16_t* dst = oh + (size_t)(t0 + i) * M + n;
 #pragma unroll
         for (int tm = 0; tm < GG::TM; ++tm) dst[16 * tm] = (bf16_t)(cvt_pk(num[tm][r] * inv, 0.f) & 0xffffu);
