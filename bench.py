@@ -127,7 +127,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="causal_long",
-                    choices=["causal_long", "noncausal_long", "decode", "deltanet", "causal_mid"])
+                    choices=["causal_long", "noncausal_long", "decode", "deltanet", "causal_mid", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--oracle-budget", type=float, default=20.0)
     args = ap.parse_args()
@@ -148,6 +148,28 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
+
+    if args.workload == "copy":
+        # Calibration: a plain 1 GiB device copy (torch's copy kernel).  Its
+        # FETCH_SIZE / WRITE_SIZE counter readings against the known 1 GiB give
+        # the factors that turn those counters into HBM bytes.
+        nbytes = 1 << 30
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup):
+            dst.copy_(src)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / args.steps
+        print(json.dumps({"metric": "device copy GB/s (read + write)", "value": 2 * nbytes / (ms / 1e3) / 1e9,
+                          "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                          "ms_per_step": ms, "higher_is_better": True, "bytes_per_copy": nbytes}), flush=True)
+        return
 
     wname = "causal_long" if args.workload == "noncausal_long" else args.workload
     w = synth.WORKLOADS[wname]
