@@ -229,38 +229,21 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # Timed region: K steps; HIP events around every launch of the measured path.
-    ev = events(2 * K * launches_per_step) if launches_per_step == 1 else None
+    # Timed region: K steps launched back to back on the library's stream, HIP
+    # events at both ends.  The average launch duration is the region's time over
+    # the launches in it (the launches queue without host gaps, so this matches
+    # the kernel trace's per-dispatch average).
     t_start, t_end = events(2)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
-    if launches_per_step == 1:
-        for i in range(K):
-            ev[2 * i].record(stream)
-            step()
-            ev[2 * i + 1].record(stream)
-    else:
-        # decode: per-launch events on a sample of the steps inside the loop
-        per = []
-        for i in range(K):
-            for t in range(w.steps):
-                if t % 64 == 0:
-                    a, b = events(2)
-                    a.record(stream)
-                    la.decode_step(sq[t], sk[t], sv[t], S, z, out=o[t])
-                    b.record(stream)
-                    per.append((a, b))
-                else:
-                    la.decode_step(sq[t], sk[t], sv[t], S, z, out=o[t])
+    for _ in range(K):
+        step()
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
-    if launches_per_step == 1:
-        launch_ms = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(K)) / K
-    else:
-        launch_ms = sum(a.elapsed_time(b) for a, b in per) / len(per)
+    launch_ms = total_ms / (K * launches_per_step)
 
     ms_per_step = total_ms / K
     value = units * K / (total_ms / 1e3)

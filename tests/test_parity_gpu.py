@@ -53,6 +53,23 @@ def test_causal_ragged(dtype, D, M, N):
     assert mat_rel_err(host(z), rz, 1) < STATE_TOL[dtype]
 
 
+@pytest.mark.parametrize("B,H,N", [(1, 1, 40000), (1, 2, 20000), (3, 100, 700), (2, 5, 9000)])
+def test_causal_many_blocks_with_state(B, H, N):
+    """Long sequences over few heads (and many heads over short ones): the
+    single-pass kernel then spreads one head's blocks over several rounds of
+    its persistent grid, which exercises every look-back case."""
+    dtype, D, M = torch.bfloat16, 64, 64
+    say("causal many blocks", B, H, N)
+    q, k, v = synth.qkv(B, H, N, D, M, dtype=dtype, seed=B * 1000 + H * 10 + N)
+    S0 = torch.randn(B, H, D, M, generator=torch.Generator().manual_seed(N)) * 3
+    z0 = torch.rand(B, H, D, generator=torch.Generator().manual_seed(N + 1)) * 5
+    o, (S, z) = la.causal(*gpu(q, k, v), state=(S0.to(DEV), z0.to(DEV)), return_state=True)
+    ro, rS, rz = oracle.causal(q, k, v, S0=S0, z0=z0)
+    assert row_rel_err(host(o), ro) < TOL[dtype]
+    assert mat_rel_err(host(S), rS) < STATE_TOL[dtype]
+    assert mat_rel_err(host(z), rz, 1) < STATE_TOL[dtype]
+
+
 def test_causal_small_workload_all_rows_explicit():
     w = synth.WORKLOADS["causal_small"]
     say(w)
