@@ -186,7 +186,7 @@ def main():
             ws = torch.empty(max(1, la.noncausal_workspace_bytes(w.B, w.H, w.N, w.D, w.M, w.dtype)),
                              dtype=torch.uint8, device=dev)
             step = lambda: la.noncausal(q, k, v, out=o, workspace=ws)
-            kernel = "linattn_noncausal_fwd (block_state + state_scan + noncausal_apply)"
+            kernel = "linattn_noncausal_fwd (nc_state_kernel + nc_reduce_kernel + nc_apply_kernel)"
         else:
             ws = torch.empty(max(1, la.causal_workspace_bytes(w.B, w.H, w.N, w.D, w.M, w.dtype)),
                              dtype=torch.uint8, device=dev)

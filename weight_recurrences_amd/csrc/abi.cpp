@@ -65,7 +65,7 @@ size_t linattn_causal_workspace_bytes(int B, int H, int N, int D, int M, int dty
 
 size_t linattn_noncausal_workspace_bytes(int B, int H, int N, int D, int M, int dtype) {
   if (check_shape(B, H, N, D, M, dtype) != LINATTN_OK) return 0;
-  return la::noncausal_ws_bytes(B * H, N, D, M);
+  return la::noncausal_ws_bytes(B * H, N, D, M, dtype == LINATTN_BF16);
 }
 
 int linattn_causal_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int D, int M,
@@ -112,7 +112,7 @@ int linattn_noncausal_fwd(const void* q, const void* k, const void* v, void* o, 
   const long long nq = BH * N * D * es, nv = BH * N * M * es;
   if (!q || !k || !v || !o) return LINATTN_ERR_NULL;
   if ((st = check_align({q, k, v, o, ws}))) return st;
-  const size_t need = la::noncausal_ws_bytes((int)BH, N, D, M);
+  const size_t need = la::noncausal_ws_bytes((int)BH, N, D, M, dtype == LINATTN_BF16);
   if (!ws || ws_bytes < need) return LINATTN_ERR_WORKSPACE;
   const Span sq(q, nq), sk(k, nq), sv(v, nv), so(o, nv), sws(ws, (long long)need);
   for (const Span& x : {sq, sk, sv, sws})

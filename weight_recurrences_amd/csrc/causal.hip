@@ -788,8 +788,9 @@ size_t causal_ws_bytes(int BH, int N, int D, int M, int bf16) {
   return (size_t)BH * nblk * (size_t)(D * M + D) * sizeof(float);
 }
 
-size_t noncausal_ws_bytes(int BH, int N, int D, int M) {
+size_t noncausal_ws_bytes(int BH, int N, int D, int M, int bf16) {
   if (BH <= 0 || N <= 0) return 0;
+  if (bf16) return noncausal_bf16_ws_bytes(BH, N, D, M);
   const int tblk = causal_block_tokens(BH, N);
   const long long nblk = (N + tblk - 1) / tblk;
   return (size_t)BH * (nblk + 1) * (size_t)(D * M + D) * sizeof(float);
@@ -816,11 +817,8 @@ hipError_t launch_causal(const void* q, const void* k, const void* v, void* o, i
 
 hipError_t launch_noncausal(const void* q, const void* k, const void* v, void* o, int BH, int N, int D, int M,
                             int bf16, void* ws, hipStream_t stream) {
-  if (bf16) {
-    LA_DISPATCH_DM(noncausal_impl, bf16_t, q, k, v, o, BH, N, ws, stream)
-  } else {
-    LA_DISPATCH_DM(noncausal_impl, float, q, k, v, o, BH, N, ws, stream)
-  }
+  if (bf16) return launch_noncausal_bf16(q, k, v, o, BH, N, D, M, ws, stream);
+  LA_DISPATCH_DM(noncausal_impl, float, q, k, v, o, BH, N, ws, stream)
 }
 
 }  // namespace la

@@ -45,6 +45,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "lds_tiles.hpp"
 
 namespace la {
 namespace fused {
@@ -53,9 +54,6 @@ constexpr int CH = 64;    // chunk length
 constexpr int NT = 256;   // threads per workgroup (4 wavefronts)
 constexpr int TBLK = 256; // tokens per block
 constexpr int NCH = TBLK / CH;
-
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 template <int D, int M>
 struct G {
@@ -82,60 +80,6 @@ struct alignas(16) Smem {
   float Zs[D];
   int status;
 };
-
-// Swizzled element offset of (row, col) in a row-major bf16 tile with U units per row.
-template <int U>
-__device__ __forceinline__ int swz(int row, int col) {
-  const int unit = (col >> 3) ^ ((row ^ (row >> 3)) & (U - 1));
-  return row * U * 8 + unit * 8 + (col & 7);
-}
-
-// 16-byte unit (row, col..col+7) of a swizzled tile; col is a multiple of 8.
-template <int U>
-__device__ __forceinline__ u32x4& unit16(bf16_t* tile, int row, int col) {
-  return reinterpret_cast<u32x4*>(tile)[swz<U>(row, col) >> 3];
-}
-template <int U>
-__device__ __forceinline__ const u32x4& unit16(const bf16_t* tile, int row, int col) {
-  return reinterpret_cast<const u32x4*>(tile)[swz<U>(row, col) >> 3];
-}
-// 8-byte half unit (row, col..col+3); col is a multiple of 4.
-template <int U>
-__device__ __forceinline__ u32x2& unit8(bf16_t* tile, int row, int col) {
-  return reinterpret_cast<u32x2*>(tile)[swz<U>(row, col) >> 2];
-}
-
-__device__ __forceinline__ uint32_t cvt_pk(float lo, float hi) {
-  typedef float f2 __attribute__((ext_vector_type(2)));
-  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{lo, hi}, b2));
-}
-
-__device__ __forceinline__ float lo_of(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float hi_of(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// Transposed fragment: lane (n, g) gets rows row0 + 4g + e (e < 4) of column col0 + n
-// from a row-major swizzled tile.
-template <int U>
-__device__ __forceinline__ u32x2 tr_read(const bf16_t* tile, int row0, int col0, int g, int sl) {
-  const int row = row0 + 4 * g + (sl >> 2);
-  const int col = col0 + 4 * (sl & 3);
-  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(tile + swz<U>(row, col)));
-  return __builtin_bit_cast(u32x2, r);
-}
-
-// j-slot fragment (8 rows 32s + 16h + 4g + r of column col0 + n) from a row-major tile.
-template <int U>
-__device__ __forceinline__ bf16x8 jfrag(const bf16_t* tile, int rbase, int col0, int g, int sl) {
-  const u32x2 a = tr_read<U>(tile, rbase, col0, g, sl);
-  const u32x2 b = tr_read<U>(tile, rbase + 16, col0, g, sl);
-  return as_bf16x8(u32x4{a[0], a[1], b[0], b[1]});
-}
-
-__device__ __forceinline__ bf16x8 ones8() {
-  const uint32_t one2 = 0x3F803F80u;
-  return as_bf16x8(u32x4{one2, one2, one2, one2});
-}
 
 // Publish / read a block state in the workspace: S [D][M] then z [D] (float32).
 template <int D, int M>
@@ -361,7 +305,17 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
     }
   }
 
-  // Prefetch phase 3's queries (raw bits; phi is applied per chunk).
+  // ---------------- phase 2: exclusive prefix of the block ----------------
+  // P_b is the left fold S0 + a_0 + a_1 + ... + a_{b-1} of the block
+  // increments a_j, evaluated in that order whatever the timing: the block
+  // starts from the nearest published inclusive prefix (itself such a fold)
+  // and adds the later increments in forward order.  Results are therefore
+  // bitwise repeatable; only the never-expected fallback (a predecessor that
+  // publishes nothing within the spin bound) computes increments differently.
+  // Prefetch phase 3's queries (raw bits; phi is applied per chunk).  They are
+  // issued before the look-back on purpose: a workgroup's vector memory
+  // operations complete in issue order, so the flag polls and state loads of the
+  // look-back must not queue behind them.
   constexpr int QV = D / 32;
   u32x4 rq[NCH][QV];
 #pragma unroll
@@ -373,13 +327,6 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
                                  : u32x4{0u, 0u, 0u, 0u};
   }
 
-  // ---------------- phase 2: exclusive prefix of the block ----------------
-  // P_b is the left fold S0 + a_0 + a_1 + ... + a_{b-1} of the block
-  // increments a_j, evaluated in that order whatever the timing: the block
-  // starts from the nearest published inclusive prefix (itself such a fold)
-  // and adds the later increments in forward order.  Results are therefore
-  // bitwise repeatable; only the never-expected fallback (a predecessor that
-  // publishes nothing within the spin bound) computes increments differently.
   Tiles<D, M> P;
   tiles_zero<D, M>(P);
   const size_t slot = (size_t)bh * nblk + b;
@@ -527,9 +474,11 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
       qf[s] = as_bf16x8(pk);
     }
 
-    f32x4 num[GG::TM];
+    // Transposed accumulators: numT[tm] row m (16 tm + 4g + r), column i (16 w + n);
+    // every row of den holds the denominator of query column i.
+    f32x4 numT[GG::TM];
 #pragma unroll
-    for (int tm = 0; tm < GG::TM; ++tm) num[tm] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int tm = 0; tm < GG::TM; ++tm) numT[tm] = f32x4{0.f, 0.f, 0.f, 0.f};
     f32x4 den{0.f, 0.f, 0.f, 0.f};
 
     // Scores A^T[j][i] = phi(k_j).phi(q_i), j-tiles t <= w, masked on the diagonal.
@@ -550,7 +499,8 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
         }
       }
     }
-    // Intra-chunk: num += P V, den += P 1.
+    // Intra-chunk: num^T += V^T P^T, den += 1^T P^T (the score tiles are already
+    // the B operand: lane (n, g) holds column i = n at the j-slots of group g).
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       if (2 * s <= w) {
@@ -559,19 +509,19 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
                                           cvt_pk(at[2 * s + 1][2], at[2 * s + 1][3])});
 #pragma unroll
         for (int tm = 0; tm < GG::TM; ++tm) {
-          const bf16x8 bv = jfrag<GG::UV>(sm.V, c * CH + 32 * s, 16 * tm, g, n);
-          num[tm] = mma(pf, bv, num[tm]);
+          const bf16x8 av = jfrag<GG::UV>(sm.V, c * CH + 32 * s, 16 * tm, g, n);
+          numT[tm] = mma(av, pf, numT[tm]);
         }
-        den = mma(pf, ones, den);
+        den = mma(ones, pf, den);
       }
     }
-    // Inter-chunk: num += phi(Q) S, den += phi(Q) z (z as a bf16 head + tail).
+    // Inter-chunk: num^T += S^T phi(Q)^T, den += z^T phi(Q)^T (z as a bf16 head + tail).
 #pragma unroll
     for (int s = 0; s < QV; ++s) {
 #pragma unroll
       for (int tm = 0; tm < GG::TM; ++tm) {
-        const bf16x8 bs = as_bf16x8(unit16<GG::UK>((const bf16_t*)sm.u.St, 16 * tm + n, 32 * s + 8 * g));
-        num[tm] = mma(qf[s], bs, num[tm]);
+        const bf16x8 as = as_bf16x8(unit16<GG::UK>((const bf16_t*)sm.u.St, 16 * tm + n, 32 * s + 8 * g));
+        numT[tm] = mma(as, qf[s], numT[tm]);
       }
       const f32x4 za = *reinterpret_cast<const f32x4*>(&sm.Zs[32 * s + 8 * g]);
       const f32x4 zb = *reinterpret_cast<const f32x4*>(&sm.Zs[32 * s + 8 * g + 4]);
@@ -584,18 +534,22 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
       zl[1] = cvt_pk(za[2] - lo_of(zh[1]), za[3] - hi_of(zh[1]));
       zl[2] = cvt_pk(zb[0] - lo_of(zh[2]), zb[1] - hi_of(zh[2]));
       zl[3] = cvt_pk(zb[2] - lo_of(zh[3]), zb[3] - hi_of(zh[3]));
-      den = mma(qf[s], as_bf16x8(u32x4{zh[0], zh[1], zh[2], zh[3]}), den);
-      den = mma(qf[s], as_bf16x8(u32x4{zl[0], zl[1], zl[2], zl[3]}), den);
+      den = mma(as_bf16x8(u32x4{zh[0], zh[1], zh[2], zh[3]}), qf[s], den);
+      den = mma(as_bf16x8(u32x4{zl[0], zl[1], zl[2], zl[3]}), qf[s], den);
     }
-    // o_i = num_i / den_i: lane (n, g) holds rows 16w + 4g + r, columns 16 tm + n.
+    // o_i = num_i / den_i for query i = 16w + n: lane (n, g) holds the four
+    // consecutive columns 16 tm + 4g .. +3 of every m-tile, one 8-byte store each.
+    {
+      const int i = c * CH + 16 * w + n;
+      const float inv = __builtin_amdgcn_rcpf(den[0]);
+      u32x2 pk[GG::TM];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = c * CH + 16 * w + 4 * g + r;
+      for (int tm = 0; tm < GG::TM; ++tm)
+        pk[tm] = u32x2{cvt_pk(numT[tm][0] * inv, numT[tm][1] * inv), cvt_pk(numT[tm][2] * inv, numT[tm][3] * inv)};
       if (i < ntok) {
-        const float inv = __builtin_amdgcn_rcpf(den[r]);
-        bf16_t* dst = oh + (size_t)(t0 + i) * M + n;
+        bf16_t* dst = oh + (size_t)(t0 + i) * M + 4 * g;
 #pragma unroll
-        for (int tm = 0; tm < GG::TM; ++tm) dst[16 * tm] = (bf16_t)(cvt_pk(num[tm][r] * inv, 0.f) & 0xffffu);
+        for (int tm = 0; tm < GG::TM; ++tm) *reinterpret_cast<u32x2*>(dst + 16 * tm) = pk[tm];
       }
     }
   }

@@ -20,7 +20,7 @@ namespace la {
 // Tokens per sequence block of the causal / non-causal kernels.
 int causal_block_tokens(int BH, int N);
 size_t causal_ws_bytes(int BH, int N, int D, int M, int bf16);
-size_t noncausal_ws_bytes(int BH, int N, int D, int M);
+size_t noncausal_ws_bytes(int BH, int N, int D, int M, int bf16);
 
 hipError_t launch_causal(const void* q, const void* k, const void* v, void* o, int BH, int N, int D, int M,
                          int bf16, const float* S0, const float* z0, float* S_out, float* z_out, void* ws,
@@ -32,6 +32,10 @@ hipError_t launch_causal_fused(const void* q, const void* k, const void* v, void
                                hipStream_t stream);
 hipError_t launch_noncausal(const void* q, const void* k, const void* v, void* o, int BH, int N, int D, int M,
                             int bf16, void* ws, hipStream_t stream);
+// bf16 non-causal path (state, reduce and apply kernels).
+size_t noncausal_bf16_ws_bytes(int BH, int N, int D, int M);
+hipError_t launch_noncausal_bf16(const void* q, const void* k, const void* v, void* o, int BH, int N, int D, int M,
+                                 void* ws, hipStream_t stream);
 hipError_t launch_decode(const void* q, const void* k, const void* v, void* o, float* S, float* z, int BH, int D,
                          int M, int bf16, hipStream_t stream);
 hipError_t launch_deltanet(const void* q, const void* k, const void* v, const void* beta, void* o, int BH, int N,
