@@ -30,9 +30,9 @@ __global__ __launch_bounds__(256) void deltanet_kernel(const T* __restrict__ q, 
   constexpr int UPT = D / 4;    // 4-element units per token row of k/q
   constexpr int NU = DTB * UPT; // units per block
   constexpr int KU = (NU + 255) / 256;
-  __shared__ float Kh[DTB][D + 4];
-  __shared__ float Qh[DTB][D + 4];
-  __shared__ float Vs[DTB][16];
+  __shared__ __attribute__((aligned(16))) float Kh[DTB][D + 4];
+  __shared__ __attribute__((aligned(16))) float Qh[DTB][D + 4];
+  __shared__ __attribute__((aligned(16))) float Vs[DTB][16];
   __shared__ float Bs[DTB];
   __shared__ float Os[DTB][17];
 
@@ -87,12 +87,14 @@ __global__ __launch_bounds__(256) void deltanet_kernel(const T* __restrict__ q, 
   for (int t0 = 0; t0 < N; t0 += DTB) {
     const int nt = min(DTB, N - t0);
     // Stage: kh = phi(k)/sum phi(k), qh likewise (lanes of one token row are an
-    // aligned group of UPT lanes).
+    // aligned group of UPT lanes).  Tokens past the end are staged as zero k, q
+    // and beta, which leave W unchanged, so the sequential loop always runs 64.
 #pragma unroll
     for (int i = 0; i < KU; ++i) {
       const int u = tid + 256 * i;
       if (u < NU) {  // uniform per group of UPT lanes
         const int tok = u / UPT, d4 = (u % UPT) * 4;
+        const bool ok = tok < nt;
         float4 a{phi(rk[i].x), phi(rk[i].y), phi(rk[i].z), phi(rk[i].w)};
         float4 b{phi(rq[i].x), phi(rq[i].y), phi(rq[i].z), phi(rq[i].w)};
         float sa = a.x + a.y + a.z + a.w, sb = b.x + b.y + b.z + b.w;
@@ -103,45 +105,84 @@ __global__ __launch_bounds__(256) void deltanet_kernel(const T* __restrict__ q, 
           sa = sum8(sa);
           sb = sum8(sb);
         }
-        const float ia = 1.f / sa, ib = 1.f / sb;
+        const float ia = ok ? 1.f / sa : 0.f, ib = ok ? 1.f / sb : 0.f;
         *reinterpret_cast<float4*>(&Kh[tok][d4]) = float4{a.x * ia, a.y * ia, a.z * ia, a.w * ia};
         *reinterpret_cast<float4*>(&Qh[tok][d4]) = float4{b.x * ib, b.y * ib, b.z * ib, b.w * ib};
       }
     }
     {
       const int tok = tid >> 2, c4 = (tid & 3) * 4;
-      Vs[tok][c4 + 0] = rv.x;
-      Vs[tok][c4 + 1] = rv.y;
-      Vs[tok][c4 + 2] = rv.z;
-      Vs[tok][c4 + 3] = rv.w;
+      *reinterpret_cast<float4*>(&Vs[tok][c4]) = rv;
     }
     if (tid < DTB) Bs[tid] = rb;
     __syncthreads();
     if (t0 + DTB < N) prefetch(t0 + DTB, min(DTB, N - t0 - DTB));
 
-    // Sequential phase: one memory row per 16-lane group.
-    for (int i = 0; i < nt; ++i) {
-      float kv[DPL], qv[DPL];
+    // Sequential phase: one memory row per 16-lane group.  The chain from one
+    // token to the next is v̄ = W k, the row's sum16, c = beta (v - v̄) and the
+    // rank-1 write; the operands of token i + 1 are read from LDS while token
+    // i runs, and o = W q hangs off the chain.  Lane n keeps the outputs of the
+    // tokens i = n (mod 16) in registers until the block ends.
+    const int row = 4 * w + rl;
+    float kv[DPL], qv[DPL], vm, bt;
+    auto read_tok = [&](int i) __attribute__((always_inline)) {
+      if constexpr (DPL % 4 == 0) {
+        const float4* kp = reinterpret_cast<const float4*>(&Kh[i][n * DPL]);
+        const float4* qp = reinterpret_cast<const float4*>(&Qh[i][n * DPL]);
+#pragma unroll
+        for (int e4 = 0; e4 < DPL / 4; ++e4) {
+          const float4 x = kp[e4], y = qp[e4];
+          kv[4 * e4] = x.x; kv[4 * e4 + 1] = x.y; kv[4 * e4 + 2] = x.z; kv[4 * e4 + 3] = x.w;
+          qv[4 * e4] = y.x; qv[4 * e4 + 1] = y.y; qv[4 * e4 + 2] = y.z; qv[4 * e4 + 3] = y.w;
+        }
+      } else {
+        static_assert(DPL == 2, "rows hold 2 or a multiple of 4 elements per lane");
+        const float2 x = *reinterpret_cast<const float2*>(&Kh[i][n * DPL]);
+        const float2 y = *reinterpret_cast<const float2*>(&Qh[i][n * DPL]);
+        kv[0] = x.x; kv[1] = x.y;
+        qv[0] = y.x; qv[1] = y.y;
+      }
+      vm = Vs[i][row];
+      bt = Bs[i];
+    };
+    float oreg[DTB / 16];
+#pragma unroll
+    for (int j = 0; j < DTB / 16; ++j) oreg[j] = 0.f;
+    read_tok(0);
+#pragma unroll
+    for (int i = 0; i < DTB; ++i) {
+      float k_[DPL], q_[DPL];
 #pragma unroll
       for (int e = 0; e < DPL; ++e) {
-        kv[e] = Kh[i][n * DPL + e];
-        qv[e] = Qh[i][n * DPL + e];
+        k_[e] = kv[e];
+        q_[e] = qv[e];
       }
-      const float vm = Vs[i][4 * w + rl];
-      const float b = Bs[i];
-      float p = 0.f;
+      const float v_ = vm, b_ = bt;
+      if (i + 1 < DTB) read_tok(i + 1);
+      // retrieve: pairwise tree over the lane's elements, then the row sum
+      float pp[DPL / 2];
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) p += W[e] * kv[e];
-      const float vbar = sum16(p);          // retrieve
-      const float c = b * (vm - vbar);      // beta (v - vbar)
+      for (int e = 0; e < DPL / 2; ++e) pp[e] = W[2 * e] * k_[2 * e] + W[2 * e + 1] * k_[2 * e + 1];
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) W[e] += c * kv[e];  // write
-      float po = 0.f;
+      for (int h = DPL / 4; h >= 1; h >>= 1)
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) po += W[e] * qv[e];
-      const float om = sum16(po);           // read with the updated memory
-      if (n == 0) Os[i][4 * w + rl] = om;
+        for (int e = 0; e < h; ++e) pp[e] += pp[e + h];
+      const float vbar = sum16(pp[0]);
+      const float c = b_ * (v_ - vbar);  // beta (v - vbar)
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) W[e] += c * k_[e];  // write
+      // read with the updated memory
+#pragma unroll
+      for (int e = 0; e < DPL / 2; ++e) pp[e] = W[2 * e] * q_[2 * e] + W[2 * e + 1] * q_[2 * e + 1];
+#pragma unroll
+      for (int h = DPL / 4; h >= 1; h >>= 1)
+#pragma unroll
+        for (int e = 0; e < h; ++e) pp[e] += pp[e + h];
+      const float om = sum16(pp[0]);
+      oreg[i / 16] = n == (i % 16) ? om : oreg[i / 16];
     }
+#pragma unroll
+    for (int j = 0; j < DTB / 16; ++j) Os[16 * j + n][row] = oreg[j];
     __syncthreads();
     {  // coalesced output of the block's 16 columns
       const int tok = tid >> 2, c4 = (tid & 3) * 4;
