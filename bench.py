@@ -5,13 +5,16 @@ Default workload (the headline): causal linear attention, bf16 inputs with fp32
 accumulation and state, B=2 H=16 N=32768 D=M=64 — one step is one full
 ``linattn_causal_fwd`` over the batch (every kernel of the causal path).
 Other workloads (``--workload``): noncausal_long, decode (prefill + 1024
-single-token steps on 256x16 states), deltanet, causal_mid.
+single-token steps on 256x16 states), deltanet, deltanet_decode (the same for the
+delta-rule memory), causal_mid, and copy (a 1 GiB device copy that calibrates
+the HBM counters).
 
 Prints ONE JSON line.  Inputs are synthetic (seeded N(0,1), the recipe of the
 synth module), copied to the GPU before the timed region.  Timing: W untimed
-warm-up steps, then K timed steps bracketed by a device synchronisation;
-per-launch kernel time comes from HIP events recorded on the stream the library
-launches on (torch's current stream, passed to the C ABI).  The CPU baseline is
+warm-up steps, then K timed steps launched back to back and bracketed by a
+device synchronisation; HIP events at both ends of the timed region are recorded
+on the stream the library launches on (torch's current stream, passed to the C
+ABI), and the average launch duration is the region over its launches.  The CPU baseline is
 the oracle timed on the host cores on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -92,6 +95,22 @@ def time_oracle(workload, inputs, budget_s: float = 20.0):
         return {"value": nh * (w.N + T) / dt, "unit": "head-tokens/s", "cores": threads, "kind": "oracle",
                 "sample": f"prefill {w.N} tokens + {T} of {w.steps} steps on all {nh} states, {dt:.1f} s, "
                           f"{cpu_model()}"}
+    if w.name == "deltanet_decode":
+        q, k, v, beta, sq, sk, sv, sb = inputs
+        nh = w.B * w.H
+        # sample: all memories, prefill + the first T steps
+        t0 = time.perf_counter()
+        _, W = oracle.deltanet(q, k, v, beta)
+        T = 0
+        while T < w.steps:
+            _, W = oracle.deltanet(sq[T][:, :, None], sk[T][:, :, None], sv[T][:, :, None], sb[T][:, :, None], W0=W)
+            T += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+        return {"value": nh * (w.N + T) / dt, "unit": "head-tokens/s", "cores": threads, "kind": "oracle",
+                "sample": f"prefill {w.N} tokens + {T} of {w.steps} steps on all {nh} memories, {dt:.1f} s, "
+                          f"{cpu_model()}"}
     heads = w.B * w.H
     if w.name == "deltanet":
         q, k, v, beta = inputs
@@ -127,7 +146,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="causal_long",
-                    choices=["causal_long", "noncausal_long", "decode", "deltanet", "causal_mid", "copy"])
+                    choices=["causal_long", "noncausal_long", "decode", "deltanet", "deltanet_decode", "causal_mid", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--oracle-budget", type=float, default=20.0)
     args = ap.parse_args()
@@ -215,6 +234,24 @@ def main():
         alg_bytes = w.B * w.H * per_head_token       # per launch (one decode step)
         unit = "head-tokens/s"
         launches_per_step = w.steps
+    elif args.workload == "deltanet_decode":
+        q, k, v, beta, sq, sk, sv, sb = inputs
+        q, k, v, beta = q.to(dev), k.to(dev), v.to(dev), beta.to(dev)
+        sq, sk, sv, sb = sq.to(dev), sk.to(dev), sv.to(dev), sb.to(dev)
+        _, W0 = la.deltanet(q, k, v, beta, return_state=True)
+        W = W0.clone()
+        o = torch.empty(w.steps, w.B, w.H, w.M, dtype=w.dtype, device=dev)
+
+        def step():
+            for t in range(w.steps):
+                la.deltanet_decode_step(sq[t], sk[t], sv[t], sb[t], W, out=o[t])
+        kernel = "deltanet_decode_step (deltanet_step_kernel)"
+        units = w.B * w.H * w.steps                  # head-tokens per step (1024 decode steps)
+        es = 2
+        per_head_token = 2 * w.M * w.D * 4 + (2 * w.D + 2 * w.M) * es + es
+        alg_bytes = w.B * w.H * per_head_token       # per launch (one decode step)
+        unit = "head-tokens/s"
+        launches_per_step = w.steps
     else:  # deltanet
         q, k, v, beta = (t.to(dev) for t in inputs)
         o = torch.empty(w.B, w.H, w.N, w.M, dtype=w.dtype, device=dev)
@@ -269,9 +306,11 @@ def main():
         "decode": f"decode: RNN-form decode, {w.B}x{w.H} states D=M={w.D}, {w.steps} single-token bf16 steps "
                   f"after a {w.N}-token prefill",
         "deltanet": f"deltanet: delta-rule fast weights, fp32, B={w.B} H={w.H} N={w.N} D=M={w.D}",
+        "deltanet_decode": f"deltanet_decode: delta-rule decode, {w.B}x{w.H} memories D=M={w.D}, {w.steps} "
+                           f"single-token bf16 steps after a {w.N}-token prefill",
     }
     dtype = {"causal_long": "bf16", "noncausal_long": "bf16", "decode": "bf16", "causal_mid": "f32",
-             "deltanet": "f32"}[args.workload]
+             "deltanet": "f32", "deltanet_decode": "bf16"}[args.workload]
     line = {
         "metric": METRIC if args.workload == "causal_long" else f"{args.workload} {unit}",
         "value": value, "unit": unit, "n_gpus": 1, "steps": K, "warmup": Wm,

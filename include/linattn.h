@@ -16,7 +16,8 @@
  *                  Secretly Fast Weight Programmers" (Schlag et al. 2021; news
  *                  summary, paragraphs on the update rule and normalisation):
  *                  kh = phi(k)/sum(phi(k)), qh = phi(q)/sum(phi(q)),
- *                  vbar = W kh, W += beta (v - vbar) kh^T, o = W qh.
+ *                  vbar = W kh, W += beta (v - vbar) kh^T, o = W qh,
+ *                  over a sequence or as a single decode step.
  * No 1/sqrt(D) scaling and no epsilon is applied (the pages apply none to these
  * forms; phi > 0 keeps every denominator positive).
  *
@@ -42,7 +43,8 @@
  *   LINATTN_ERR_SHAPE       a size is negative or an element count overflows;
  *   LINATTN_ERR_DTYPE       dtype is not LINATTN_F32 / LINATTN_BF16;
  *   LINATTN_ERR_UNSUPPORTED (D, M) is outside the built set;
- *   LINATTN_ERR_ALIGN       a pointer is not 16-byte aligned;
+ *   LINATTN_ERR_ALIGN       a pointer is not 16-byte aligned (beta: not
+ *                           aligned to its element size);
  *   LINATTN_ERR_ALIAS       an output overlaps an input it must not overlap
  *                           (a state output identical to its input is allowed);
  *   LINATTN_ERR_WORKSPACE   the workspace is NULL or smaller than required;
@@ -129,6 +131,19 @@ int linattn_decode_step(const void* q, const void* k, const void* v, void* o,
 int deltanet_fwd(const void* q, const void* k, const void* v, const void* beta, void* o,
                  int B, int H, int N, int D, int M, int dtype,
                  const float* W0, float* W_out, void* stream);
+
+/* One autoregressive step of the delta-rule memory (the RNN form of
+ * deltanet_fwd, for one token) for B*H independent memories, in place:
+ *   kh = phi(k)/sum_c phi(k)_c,  qh = phi(q)/sum_c phi(q)_c,
+ *   vbar = W kh,  W <- W + beta (v - vbar) kh^T,  o = W qh
+ * ("Linear Transformers Are Secretly Fast Weight Programmers", news summary,
+ * paragraphs on the update rule and normalisation; the output reads the
+ * updated memory).  N steps of this call equal deltanet_fwd over N tokens.
+ * q, k: [B,H,D]; v, o: [B,H,M]; beta: [B,H] (dtype, used as given);
+ * W: [B,H,M,D] float32, read and written in place.
+ * o must not overlap q, k, v, beta or W; W must not overlap q, k, v or beta. */
+int deltanet_decode_step(const void* q, const void* k, const void* v, const void* beta, void* o,
+                         float* W, int B, int H, int D, int M, int dtype, void* stream);
 
 /* Static, human-readable name of a status code ("LINATTN_OK", ...). */
 const char* linattn_status_str(int status);

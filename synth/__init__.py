@@ -17,6 +17,8 @@ project's design notes for where each comes from):
   causal_long    B=2   H=16 N=32768  D=M=64  bf16, N(0,1)*0.5 (also run non-causally)
   decode         B=256 H=16 D=M=64, 512-token prefill + 1024 single-token steps, bf16
   deltanet       B=4   H=8  N=4096   D=M=64  fp32, beta=sigmoid(N(0,1))
+  deltanet_decode B=256 H=16 D=M=64, 512-token delta-rule prefill + 1024 single-token
+                 steps, bf16, beta=sigmoid(N(0,1))
 """
 from __future__ import annotations
 
@@ -45,6 +47,7 @@ WORKLOADS = {
     "causal_long": Workload("causal_long", 2, 16, 32768, 64, 64, torch.bfloat16, 0.5, 1003),
     "decode": Workload("decode", 256, 16, 512, 64, 64, torch.bfloat16, 1.0, 1004, steps=1024),
     "deltanet": Workload("deltanet", 4, 8, 4096, 64, 64, torch.float32, 1.0, 1005),
+    "deltanet_decode": Workload("deltanet_decode", 256, 16, 512, 64, 64, torch.bfloat16, 1.0, 1006, steps=1024),
 }
 
 
@@ -89,10 +92,26 @@ def decode_steps(B, H, D, M, T, *, dtype=torch.bfloat16, scale=1.0, seed=0):
     return q, k, v
 
 
+def decode_steps_beta(B, H, D, M, T, *, dtype=torch.bfloat16, scale=1.0, seed=0):
+    """Per-step inputs for T delta-rule decode steps: q, k [T,B,H,D]; v [T,B,H,M];
+    beta [T,B,H] = sigmoid(N(0,1))."""
+    g = _gen(seed)
+    q = _draw(g, (T, B, H, D), scale, dtype)
+    k = _draw(g, (T, B, H, D), scale, dtype)
+    v = _draw(g, (T, B, H, M), scale, dtype)
+    beta = torch.sigmoid(torch.randn(T, B, H, generator=g, dtype=torch.float32)).to(dtype)
+    return q, k, v, beta
+
+
 def workload_inputs(w: Workload, seed_offset: int = 0):
     """All inputs of a named workload.  Causal/non-causal: (q, k, v);
-    deltanet: (q, k, v, beta); decode: (prefill q, k, v, step q, k, v)."""
+    deltanet: (q, k, v, beta); decode: (prefill q, k, v, step q, k, v);
+    deltanet_decode: (prefill q, k, v, beta, step q, k, v, beta)."""
     s = w.seed + seed_offset
+    if w.name == "deltanet_decode":
+        pre = qkv_beta(w.B, w.H, w.N, w.D, w.M, dtype=w.dtype, scale=w.scale, seed=s)
+        steps = decode_steps_beta(w.B, w.H, w.D, w.M, w.steps, dtype=w.dtype, scale=w.scale, seed=s + 100000)
+        return pre + steps
     if w.name == "deltanet":
         return qkv_beta(w.B, w.H, w.N, w.D, w.M, dtype=w.dtype, scale=w.scale, seed=s)
     if w.name == "decode":

@@ -101,6 +101,7 @@ def test_empty_problems_are_no_ops(lib):
     assert lib.linattn_decode_step(None, None, None, None, None, None, 0, 16, 64, 64, 1, None) == OK
     assert lib.deltanet_fwd(None, None, None, None, None, 0, 8, 100, 64, 64, 0, None, None, None) == OK
     assert lib.deltanet_fwd(None, None, None, None, None, 2, 8, 0, 64, 64, 0, None, None, None) == OK
+    assert lib.deltanet_decode_step(None, None, None, None, None, None, 0, 16, 64, 64, 1, None) == OK
 
 
 @no_gpu
@@ -154,6 +155,26 @@ def test_deltanet_validation(lib):
     assert f(*bad) == UNSUP
     bad = list(args); bad[10] = -1
     assert f(*bad) == DTYPE
+
+
+@no_gpu
+def test_deltanet_decode_validation(lib):
+    f = lib.deltanet_decode_step
+    args = [Q, K, V, BETA, O, S0, 256, 16, 64, 64, 1, None]
+    bad = list(args); bad[5] = None
+    assert f(*bad) == NULL
+    bad = list(args); bad[3] = None
+    assert f(*bad) == NULL
+    bad = list(args); bad[4] = S0 + 64
+    assert f(*bad) == ALIAS        # o inside W
+    bad = list(args); bad[5] = BETA
+    assert f(*bad) == ALIAS        # W over beta
+    bad = list(args); bad[9] = 48
+    assert f(*bad) == UNSUP
+    bad = list(args); bad[10] = 2
+    assert f(*bad) == DTYPE
+    bad = list(args); bad[2] = V + 4
+    assert f(*bad) == ALIGN
 
 
 def test_binding_refuses_cpu_tensors():

@@ -320,3 +320,76 @@ def test_deltanet_empty_sequence_copies_memory():
     e = torch.empty(2, 2, 0, 32, device=DEV)
     o, W = la.deltanet(e, e, e, torch.empty(2, 2, 0, device=DEV), W0=W0, return_state=True)
     assert torch.equal(host(W), host(W0))
+
+
+# ------------------------------------------------------- delta-rule decode step
+
+def _oracle_delta_step(q, k, v, beta, W):
+    """One oracle step: the sequence oracle on a length-1 sequence."""
+    o, W2 = oracle.deltanet(q[:, :, None], k[:, :, None], v[:, :, None], beta[:, :, None], W0=W)
+    return o[:, :, 0], W2
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("D,M", [(32, 32), (32, 64), (64, 32), (64, 64)])
+def test_deltanet_decode_steps_small(dtype, D, M):
+    """Prefill a memory with the sequence kernel, then T single steps (B*H = 15,
+    a partial workgroup of wavefronts), each against the oracle."""
+    B, H, P, T = 3, 5, 40, 6
+    say("deltanet decode", dtype, D, M)
+    q, k, v, beta = synth.qkv_beta(B, H, P, D, M, dtype=dtype, seed=D * M + 1)
+    sq, sk, sv, sb = synth.decode_steps_beta(B, H, D, M, T, dtype=dtype, seed=D + M + 1)
+    W0 = torch.randn(B, H, M, D) * 0.1
+    _, W = la.deltanet(*gpu(q, k, v, beta), W0=W0.to(DEV), return_state=True)
+    _, rW = oracle.deltanet(q, k, v, beta, W0=W0)
+    gq, gk, gv, gb = gpu(sq, sk, sv, sb)
+    for t in range(T):
+        o = la.deltanet_decode_step(gq[t], gk[t], gv[t], gb[t], W)
+        ro, rW = _oracle_delta_step(sq[t], sk[t], sv[t], sb[t], rW)
+        assert row_rel_err(host(o), ro) < TOL[dtype], t
+        assert mat_rel_err(host(W), rW) < 1e-4, t
+
+
+def test_deltanet_decode_equals_sequence():
+    """N decode steps from W0 give the sequence kernel's outputs and memory (both
+    fp32, one rounding order apart)."""
+    B, H, N, D, M = 2, 4, 70, 64, 64
+    say("deltanet decode vs sequence")
+    q, k, v, beta = synth.qkv_beta(B, H, N, D, M, seed=77)
+    W0 = (torch.randn(B, H, M, D) * 0.1).to(DEV)
+    o_seq, W_seq = la.deltanet(*gpu(q, k, v, beta), W0=W0, return_state=True)
+    W = W0.clone()
+    gq, gk, gv, gb = gpu(q, k, v, beta)
+    outs = [la.deltanet_decode_step(gq[:, :, t].contiguous(), gk[:, :, t].contiguous(), gv[:, :, t].contiguous(),
+                                    gb[:, :, t].contiguous(), W) for t in range(N)]
+    o_dec = torch.stack(outs, dim=2)
+    assert row_rel_err(host(o_dec), host(o_seq).double()) < 1e-5
+    assert mat_rel_err(host(W), host(W_seq).double()) < 1e-5
+
+
+def test_deltanet_decode_workload_sampled_heads():
+    """Full delta-rule decode workload (512-token prefill + 1024 steps on 256 x 16
+    memories, the launch sequence the benchmark times): every head for the first
+    steps, 64 sampled heads through all 1024 steps and their final memories."""
+    w = synth.WORKLOADS["deltanet_decode"]
+    say(w)
+    q, k, v, beta, sq, sk, sv, sb = synth.workload_inputs(w)
+    _, W = la.deltanet(*gpu(q, k, v, beta), return_state=True)
+    hs = torch.randperm(w.B * w.H, generator=torch.Generator().manual_seed(11))[:64]
+    bi, hi = hs // w.H, hs % w.H
+    _, rW_s = oracle.deltanet(q[bi, hi][None], k[bi, hi][None], v[bi, hi][None], beta[bi, hi][None])
+    assert mat_rel_err(host(W)[bi, hi][None], rW_s) < 1e-4
+    Wall = host(W).double()
+    gq, gk, gv, gb = gpu(sq, sk, sv, sb)
+    outs = torch.empty(w.steps, w.B, w.H, w.M, dtype=w.dtype, device=DEV)
+    for t in range(w.steps):
+        la.deltanet_decode_step(gq[t], gk[t], gv[t], gb[t], W, out=outs[t])
+        if t < 2:  # every head, from the GPU memory of the step before
+            ro, Wall = _oracle_delta_step(sq[t], sk[t], sv[t], sb[t], Wall)
+            assert row_rel_err(host(outs[t]), ro) < 2e-2
+    outs = host(outs)
+    for t in range(w.steps):
+        ro, rW_s = _oracle_delta_step(sq[t][bi, hi][None], sk[t][bi, hi][None], sv[t][bi, hi][None],
+                                      sb[t][bi, hi][None], rW_s)
+        assert row_rel_err(outs[t][bi, hi][None], ro) < 2e-2, t
+    assert mat_rel_err(host(W)[bi, hi][None], rW_s) < 1e-4

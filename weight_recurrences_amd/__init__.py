@@ -16,7 +16,7 @@ import torch
 
 from ._lib import BF16, F32, LinAttnError, check, load
 
-__all__ = ["causal", "noncausal", "decode_step", "deltanet", "causal_workspace_bytes",
+__all__ = ["causal", "noncausal", "decode_step", "deltanet", "deltanet_decode_step", "causal_workspace_bytes",
            "noncausal_workspace_bytes", "LinAttnError", "abi_version"]
 
 _DT = {torch.float32: F32, torch.bfloat16: BF16}
@@ -170,3 +170,28 @@ def deltanet(q, k, v, beta, *, W0=None, return_state=False, out=None):
                           _ptr(W0), _ptr(W), _stream(dev))
     check(rc, "deltanet_fwd")
     return (o, W) if return_state else o
+
+
+def deltanet_decode_step(q, k, v, beta, W, *, out=None):
+    """One delta-rule step (the RNN form of ``deltanet`` for one token),
+    updating the memory W in place.
+
+    q, k: [B,H,D]; v: [B,H,M]; beta: [B,H] (float32 or bfloat16, same dtype);
+    W [B,H,M,D] float32.  Returns o [B,H,M] in the dtype of q.
+    """
+    lib = load()
+    dev = _dev(q, k, v, beta, W)
+    B, H, D = q.shape
+    M = v.shape[-1]
+    dt = _dtype_code(q)
+    if k.shape != q.shape or v.shape[:2] != (B, H) or beta.shape != (B, H):
+        raise ValueError("q, k [B,H,D], v [B,H,M], beta [B,H] expected")
+    if k.dtype != q.dtype or v.dtype != q.dtype or beta.dtype != q.dtype:
+        raise ValueError("q, k, v, beta must share a dtype")
+    if W.dtype != torch.float32 or W.shape != (B, H, M, D):
+        raise ValueError("W must be float32 [B,H,M,D]")
+    o = out if out is not None else torch.empty((B, H, M), dtype=q.dtype, device=dev)
+    rc = lib.deltanet_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(o), _ptr(W), B, H, D, M, dt,
+                                  _stream(dev))
+    check(rc, "deltanet_decode_step")
+    return o

@@ -52,6 +52,11 @@ int check_align(std::initializer_list<const void*> ptrs) {
   return LINATTN_OK;
 }
 
+// beta is read one element at a time: it needs only the alignment of its element.
+int check_align_elem(const void* p, int es) {
+  return (p && ((uintptr_t)p % (uintptr_t)es) != 0) ? LINATTN_ERR_ALIGN : LINATTN_OK;
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? LINATTN_OK : LINATTN_ERR_HIP; }
 
 }  // namespace
@@ -148,7 +153,8 @@ int deltanet_fwd(const void* q, const void* k, const void* v, const void* beta, 
   if (st) return st;
   const long long BH = (long long)B * H, es = esize(dtype);
   if (BH * N > 0 && (!q || !k || !v || !beta || !o)) return LINATTN_ERR_NULL;
-  if ((st = check_align({q, k, v, beta, o, W0, W_out}))) return st;
+  if ((st = check_align({q, k, v, o, W0, W_out}))) return st;
+  if ((st = check_align_elem(beta, (int)es))) return st;
   const long long nq = BH * N * D * es, nv = BH * N * M * es;
   const Span sq(q, nq), sk(k, nq), sv(v, nv), sb(beta, BH * N * es), so(o, nv);
   const Span sW0(W0, BH * M * D * 4), sWo(W_out, BH * M * D * 4);
@@ -160,6 +166,25 @@ int deltanet_fwd(const void* q, const void* k, const void* v, const void* beta, 
   if (BH == 0 || (N == 0 && !W_out)) return LINATTN_OK;
   return hip_status(la::launch_deltanet(q, k, v, beta, o, (int)BH, N, D, M, dtype == LINATTN_BF16, W0, W_out,
                                         (hipStream_t)stream));
+}
+
+int deltanet_decode_step(const void* q, const void* k, const void* v, const void* beta, void* o, float* W, int B,
+                         int H, int D, int M, int dtype, void* stream) {
+  int st = check_shape(B, H, 1, D, M, dtype);
+  if (st) return st;
+  const long long BH = (long long)B * H, es = esize(dtype);
+  if (BH == 0) return LINATTN_OK;
+  if (!q || !k || !v || !beta || !o || !W) return LINATTN_ERR_NULL;
+  if ((st = check_align({q, k, v, o, W}))) return st;
+  if ((st = check_align_elem(beta, (int)es))) return st;
+  const Span sq(q, BH * D * es), sk(k, BH * D * es), sv(v, BH * M * es), sb(beta, BH * es), so(o, BH * M * es);
+  const Span sW(W, BH * M * D * 4);
+  for (const Span& x : {sq, sk, sv, sb, sW})
+    if (so.overlaps(x)) return LINATTN_ERR_ALIAS;
+  for (const Span& x : {sq, sk, sv, sb})
+    if (sW.overlaps(x)) return LINATTN_ERR_ALIAS;
+  return hip_status(
+      la::launch_deltanet_step(q, k, v, beta, o, W, (int)BH, D, M, dtype == LINATTN_BF16, (hipStream_t)stream));
 }
 
 const char* linattn_status_str(int status) {

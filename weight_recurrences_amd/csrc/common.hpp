@@ -40,6 +40,21 @@ template <typename T> __device__ __forceinline__ T to_elem(float f);
 template <> __device__ __forceinline__ float to_elem<float>(float f) { return f; }
 template <> __device__ __forceinline__ bf16_t to_elem<bf16_t>(float f) { return (bf16_t)f2bf(f); }
 
+// Four consecutive elements as float4 (bf16 widened exactly) and back (bf16
+// rounded to nearest even).
+template <typename T> __device__ __forceinline__ float4 load4(const T* p);
+template <> __device__ __forceinline__ float4 load4<float>(const float* p) { return *reinterpret_cast<const float4*>(p); }
+template <> __device__ __forceinline__ float4 load4<bf16_t>(const bf16_t* p) {
+  const uint2 w = *reinterpret_cast<const uint2*>(p);
+  return float4{bf2f(w.x & 0xffffu), bf2f(w.x >> 16), bf2f(w.y & 0xffffu), bf2f(w.y >> 16)};
+}
+template <typename T> __device__ __forceinline__ void store4(T* p, float4 x);
+template <> __device__ __forceinline__ void store4<float>(float* p, float4 x) { *reinterpret_cast<float4*>(p) = x; }
+template <> __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, float4 x) {
+  *reinterpret_cast<uint2*>(p) = uint2{pack_bf2(x.x, x.y), pack_bf2(x.z, x.w)};
+}
+
+
 // ---- MFMA (16x16 output tiles, 64 lanes: lane = 16*g + n) --------------------
 // A operand: lane (n, g) holds row n, k-slots of group g.  B operand: lane
 // (n, g) holds column n, the same k-slots.  Result: lane (n, g) holds rows

@@ -16,18 +16,6 @@
 
 namespace la {
 
-template <typename T> __device__ __forceinline__ float4 load4(const T* p);
-template <> __device__ __forceinline__ float4 load4<float>(const float* p) { return *reinterpret_cast<const float4*>(p); }
-template <> __device__ __forceinline__ float4 load4<bf16_t>(const bf16_t* p) {
-  const uint2 w = *reinterpret_cast<const uint2*>(p);
-  return float4{bf2f(w.x & 0xffffu), bf2f(w.x >> 16), bf2f(w.y & 0xffffu), bf2f(w.y >> 16)};
-}
-template <typename T> __device__ __forceinline__ void store4(T* p, float4 x);
-template <> __device__ __forceinline__ void store4<float>(float* p, float4 x) { *reinterpret_cast<float4*>(p) = x; }
-template <> __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, float4 x) {
-  *reinterpret_cast<uint2*>(p) = uint2{pack_bf2(x.x, x.y), pack_bf2(x.z, x.w)};
-}
-
 template <typename T, int D, int M>
 __global__ __launch_bounds__(256) void decode_step_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                           const T* __restrict__ v, T* __restrict__ o,

@@ -212,6 +212,80 @@ static hipError_t deltanet_impl(const void* q, const void* k, const void* v, con
   return hipGetLastError();
 }
 
+// ----------------------------------------------------------------------------
+// Single-token step (the RNN form of the same rule), in place on W.  The step
+// is a pure memory stream: every (b, h) reads and writes its M x D float32
+// memory once (16 KiB each way at D = M = 64), so the kernel is bound by HBM
+// bandwidth.  One wavefront owns one memory; lane l covers the four columns
+// d = 4 (l % (D/4)) .. +3 of rows m = l / (D/4) + (256/D) p, so each load
+// instruction of the wave reads 1 KiB of consecutive memory.  kh and qh are
+// normalised with a reduction over the D/4 lanes of a row group; every row's
+// retrieval and read are reductions over the same lanes.
+template <typename T, int D, int M>
+__global__ __launch_bounds__(256) void deltanet_step_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                            const T* __restrict__ v, const T* __restrict__ beta,
+                                                            T* __restrict__ o, float* __restrict__ W, int BH) {
+  constexpr int LPR = D / 4;     // lanes per memory row
+  constexpr int RPP = 64 / LPR;  // rows per pass
+  constexpr int NP = M / RPP;    // passes
+  const int lane = threadIdx.x & 63;
+  const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (bh >= BH) return;  // whole wavefront; the kernel has no barrier
+  const int dc = lane % LPR, r0 = lane / LPR;
+  auto row_sum = [](float x) __attribute__((always_inline)) {
+    if constexpr (LPR == 16) return sum16(x);
+    else return sum8(x);
+  };
+
+  float* Wh = W + (size_t)bh * M * D + 4 * dc;
+  float4 w[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) w[p] = *reinterpret_cast<const float4*>(Wh + (size_t)(r0 + RPP * p) * D);
+  float vr[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) vr[p] = ld_scalar<T>(v + (size_t)bh * M + r0 + RPP * p);
+  const float b = ld_scalar<T>(beta + bh);
+
+  float4 kk = load4<T>(k + (size_t)bh * D + 4 * dc);
+  float4 qq = load4<T>(q + (size_t)bh * D + 4 * dc);
+  kk = float4{phi(kk.x), phi(kk.y), phi(kk.z), phi(kk.w)};
+  qq = float4{phi(qq.x), phi(qq.y), phi(qq.z), phi(qq.w)};
+  const float ik = 1.f / row_sum((kk.x + kk.y) + (kk.z + kk.w));
+  const float iq = 1.f / row_sum((qq.x + qq.y) + (qq.z + qq.w));
+  kk = float4{kk.x * ik, kk.y * ik, kk.z * ik, kk.w * ik};
+  qq = float4{qq.x * iq, qq.y * iq, qq.z * iq, qq.w * iq};
+
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const float vbar = row_sum((w[p].x * kk.x + w[p].y * kk.y) + (w[p].z * kk.z + w[p].w * kk.w));  // retrieve
+    const float c = b * (vr[p] - vbar);                                                            // beta (v - vbar)
+    w[p] = float4{w[p].x + c * kk.x, w[p].y + c * kk.y, w[p].z + c * kk.z, w[p].w + c * kk.w};     // write
+    const float om = row_sum((w[p].x * qq.x + w[p].y * qq.y) + (w[p].z * qq.z + w[p].w * qq.w));  // read
+    if (dc == 0) o[(size_t)bh * M + r0 + RPP * p] = to_elem<T>(om);
+  }
+#pragma unroll
+  for (int p = 0; p < NP; ++p) *reinterpret_cast<float4*>(Wh + (size_t)(r0 + RPP * p) * D) = w[p];
+}
+
+template <typename T, int D, int M>
+static hipError_t deltanet_step_impl(const void* q, const void* k, const void* v, const void* beta, void* o, float* W,
+                                     int BH, hipStream_t stream) {
+  const unsigned nb = (unsigned)((BH + 3) / 4);
+  hipLaunchKernelGGL((deltanet_step_kernel<T, D, M>), dim3(nb), dim3(256), 0, stream, (const T*)q, (const T*)k,
+                     (const T*)v, (const T*)beta, (T*)o, W, BH);
+  return hipGetLastError();
+}
+
+hipError_t launch_deltanet_step(const void* q, const void* k, const void* v, const void* beta, void* o, float* W,
+                                int BH, int D, int M, int bf16, hipStream_t stream) {
+  if (BH == 0) return hipSuccess;
+  if (bf16) {
+    LA_DISPATCH_DM(deltanet_step_impl, bf16_t, q, k, v, beta, o, W, BH, stream)
+  } else {
+    LA_DISPATCH_DM(deltanet_step_impl, float, q, k, v, beta, o, W, BH, stream)
+  }
+}
+
 // Copies W0 to W_out, or zero-fills it (empty sequence).
 __global__ __launch_bounds__(256) void memory_copy_kernel(const float* W0, float* W_out, long long n) {
   const long long e = (long long)blockIdx.x * 256 + threadIdx.x;

@@ -40,5 +40,7 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, void* o, f
                          int M, int bf16, hipStream_t stream);
 hipError_t launch_deltanet(const void* q, const void* k, const void* v, const void* beta, void* o, int BH, int N,
                            int D, int M, int bf16, const float* W0, float* W_out, hipStream_t stream);
+hipError_t launch_deltanet_step(const void* q, const void* k, const void* v, const void* beta, void* o, float* W,
+                                int BH, int D, int M, int bf16, hipStream_t stream);
 
 }  // namespace la
