@@ -255,8 +255,10 @@ def main():
     else:  # deltanet
         q, k, v, beta = (t.to(dev) for t in inputs)
         o = torch.empty(w.B, w.H, w.N, w.M, dtype=w.dtype, device=dev)
-        step = lambda: la.deltanet(q, k, v, beta, out=o)
-        kernel = "deltanet_fwd (deltanet_kernel)"
+        ws = torch.empty(max(1, la.deltanet_workspace_bytes(w.B, w.H, w.N, w.D, w.M, w.dtype)), dtype=torch.uint8,
+                         device=dev)
+        step = lambda: la.deltanet(q, k, v, beta, out=o, workspace=ws)
+        kernel = "deltanet_fwd (dn_prep_kernel + dn_scan_kernel + dn_out_kernel)"
         units = w.B * w.H * w.N
         alg_bytes = units * ((2 * w.D + 2 * w.M) * 4 + 4)
         unit = "tokens/s"

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define LINATTN_ABI_VERSION 1
+#define LINATTN_ABI_VERSION 2
 
 typedef enum { LINATTN_F32 = 0, LINATTN_BF16 = 1 } linattn_dtype_t;
 
@@ -127,10 +127,19 @@ int linattn_decode_step(const void* q, const void* k, const void* v, void* o,
  * beta: [B,H,N] in dtype, used as given (no squashing).
  * W0: [B,H,M,D] float32 initial memory, NULL means zero.
  * W_out: [B,H,M,D] float32 final memory, or NULL; may equal W0.
- * o must not overlap q, k, v, beta, W0 or W_out. */
+ * ws, ws_bytes: device workspace of at least deltanet_workspace_bytes();
+ *               contents need no initialisation and are clobbered.
+ * The sequence runs in chunks of 64 tokens: per chunk the same recurrence is
+ * solved exactly as a unit lower-triangular system in the values written,
+ * (I + diag(beta) L) U = diag(beta) (V - Kh W0^T), L the strictly lower part of
+ * Kh Kh^T, so that only W0 -> W0 + U^T Kh is sequential.
+ * o must not overlap q, k, v, beta, W0, W_out or ws. */
 int deltanet_fwd(const void* q, const void* k, const void* v, const void* beta, void* o,
                  int B, int H, int N, int D, int M, int dtype,
-                 const float* W0, float* W_out, void* stream);
+                 const float* W0, float* W_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of device workspace deltanet_fwd needs (0 when none). */
+size_t deltanet_workspace_bytes(int B, int H, int N, int D, int M, int dtype);
 
 /* One autoregressive step of the delta-rule memory (the RNN form of
  * deltanet_fwd, for one token) for B*H independent memories, in place:

@@ -37,7 +37,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.linattn_abi_version() == 1
+    assert lib.linattn_abi_version() == 2
     for code, name in _lib.STATUS.items():
         assert lib.linattn_status_str(code).decode() == name
     assert lib.linattn_status_str(99).decode() == "LINATTN_ERR_UNKNOWN"
@@ -56,9 +56,15 @@ def test_workspace_sizes(lib):
     # a single block per head needs no workspace
     assert lib.linattn_causal_workspace_bytes(1, 1, 256, 32, 32, 0) == 0
     assert lib.linattn_noncausal_workspace_bytes(1, 1, 256, 32, 32, 0) == 2 * (32 * 32 + 32) * 4
+    # delta rule: per chunk of 64 tokens kh, Wc (64 x D), Uc, U (64 x M) and the
+    # memory at the chunk start (M x D), float32
+    assert lib.deltanet_workspace_bytes(4, 8, 4096, 64, 64, 0) == 32 * 64 * (2 * 64 * 64 + 2 * 64 * 64 + 64 * 64) * 4
+    assert lib.deltanet_workspace_bytes(1, 1, 65, 32, 64, 1) == 2 * (2 * 64 * 32 + 2 * 64 * 64 + 64 * 32) * 4
+    assert lib.deltanet_workspace_bytes(4, 8, 0, 64, 64, 0) == 0
     for bad in [(1, 1, 256, 48, 32, 0), (1, 1, 256, 32, 32, 5), (-1, 1, 4, 32, 32, 0)]:
         assert lib.linattn_causal_workspace_bytes(*bad) == 0
         assert lib.linattn_noncausal_workspace_bytes(*bad) == 0
+        assert lib.deltanet_workspace_bytes(*bad) == 0
 
 
 def causal(lib, q=Q, k=K, v=V, o=O, B=1, H=2, N=4096, D=64, M=64, dt=1, s0=None, z0=None, so=None, zo=None,
@@ -99,8 +105,8 @@ def test_empty_problems_are_no_ops(lib):
     assert causal(lib, q=None, k=None, v=None, o=None, N=0, ws=None, wsb=0) == OK
     assert lib.linattn_noncausal_fwd(None, None, None, None, 3, 2, 0, 64, 64, 1, None, 0, None) == OK
     assert lib.linattn_decode_step(None, None, None, None, None, None, 0, 16, 64, 64, 1, None) == OK
-    assert lib.deltanet_fwd(None, None, None, None, None, 0, 8, 100, 64, 64, 0, None, None, None) == OK
-    assert lib.deltanet_fwd(None, None, None, None, None, 2, 8, 0, 64, 64, 0, None, None, None) == OK
+    assert lib.deltanet_fwd(None, None, None, None, None, 0, 8, 100, 64, 64, 0, None, None, None, 0, None) == OK
+    assert lib.deltanet_fwd(None, None, None, None, None, 2, 8, 0, 64, 64, 0, None, None, None, 0, None) == OK
     assert lib.deltanet_decode_step(None, None, None, None, None, None, 0, 16, 64, 64, 1, None) == OK
 
 
@@ -142,7 +148,8 @@ def test_decode_validation(lib):
 @no_gpu
 def test_deltanet_validation(lib):
     f = lib.deltanet_fwd
-    args = [Q, K, V, BETA, O, 4, 8, 4096, 64, 64, 0, S0, SO, None]
+    need = lib.deltanet_workspace_bytes(4, 8, 4096, 64, 64, 0)
+    args = [Q, K, V, BETA, O, 4, 8, 4096, 64, 64, 0, S0, SO, WSP, need, None]
     bad = list(args); bad[3] = None
     assert f(*bad) == NULL
     bad = list(args); bad[12] = S0 + 256
@@ -155,6 +162,14 @@ def test_deltanet_validation(lib):
     assert f(*bad) == UNSUP
     bad = list(args); bad[10] = -1
     assert f(*bad) == DTYPE
+    bad = list(args); bad[13] = None
+    assert f(*bad) == WS
+    bad = list(args); bad[14] = need - 16
+    assert f(*bad) == WS
+    bad = list(args); bad[13] = K
+    assert f(*bad) == ALIAS        # workspace over k
+    bad = list(args); bad[4] = WSP + 64
+    assert f(*bad) == ALIAS        # output inside the workspace
 
 
 @no_gpu

@@ -302,8 +302,10 @@ def test_deltanet_exact_recall_and_inplace_memory():
     lib = la._lib.load()
     qg, kg, vg, bg = gpu(q, k, v, beta)
     o = torch.empty(1, 1, N, M, device=DEV)
+    need = lib.deltanet_workspace_bytes(1, 1, N, D, M, 0)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=DEV)
     rc = lib.deltanet_fwd(qg.data_ptr(), kg.data_ptr(), vg.data_ptr(), bg.data_ptr(), o.data_ptr(), 1, 1, N, D, M,
-                          0, Wg.data_ptr(), Wg.data_ptr(), torch.cuda.current_stream().cuda_stream)
+                          0, Wg.data_ptr(), Wg.data_ptr(), ws.data_ptr(), need, torch.cuda.current_stream().cuda_stream)
     assert rc == 0
     # reading the slot just written returns exactly the value written
     np.testing.assert_allclose(host(o)[0, 0].numpy(), v[0, 0].numpy(), rtol=0, atol=1e-5)

@@ -17,7 +17,7 @@ import torch
 from ._lib import BF16, F32, LinAttnError, check, load
 
 __all__ = ["causal", "noncausal", "decode_step", "deltanet", "deltanet_decode_step", "causal_workspace_bytes",
-           "noncausal_workspace_bytes", "LinAttnError", "abi_version"]
+           "noncausal_workspace_bytes", "deltanet_workspace_bytes", "LinAttnError", "abi_version"]
 
 _DT = {torch.float32: F32, torch.bfloat16: BF16}
 
@@ -148,7 +148,11 @@ def decode_step(q, k, v, S, z, *, out=None):
     return o
 
 
-def deltanet(q, k, v, beta, *, W0=None, return_state=False, out=None):
+def deltanet_workspace_bytes(B, H, N, D, M, dtype) -> int:
+    return int(load().deltanet_workspace_bytes(B, H, N, D, M, _DT[dtype]))
+
+
+def deltanet(q, k, v, beta, *, W0=None, return_state=False, out=None, workspace=None):
     """Delta-rule fast-weight memory with sum-normalised phi.
 
     q, k: [B,H,N,D]; v: [B,H,N,M]; beta: [B,H,N] (same dtype, beta used as
@@ -166,8 +170,10 @@ def deltanet(q, k, v, beta, *, W0=None, return_state=False, out=None):
         raise ValueError("W0 must be float32 [B,H,M,D]")
     o = out if out is not None else torch.empty((B, H, N, M), dtype=q.dtype, device=dev)
     W = torch.empty((B, H, M, D), dtype=torch.float32, device=dev) if return_state else None
+    need = int(lib.deltanet_workspace_bytes(B, H, N, D, M, dt))
+    ws = _workspace(need, dev, workspace)
     rc = lib.deltanet_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(o), B, H, N, D, M, dt,
-                          _ptr(W0), _ptr(W), _stream(dev))
+                          _ptr(W0), _ptr(W), _ptr(ws), need, _stream(dev))
     check(rc, "deltanet_fwd")
     return (o, W) if return_state else o
 

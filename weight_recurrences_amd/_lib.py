@@ -35,7 +35,8 @@ SIGNATURES = {
     "linattn_noncausal_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "linattn_noncausal_fwd": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
     "linattn_decode_step": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
-    "deltanet_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp]),
+    "deltanet_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
+    "deltanet_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "deltanet_decode_step": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
     "linattn_status_str": (ctypes.c_char_p, [_i]),
     "linattn_abi_version": (_i, []),

@@ -147,25 +147,34 @@ int linattn_decode_step(const void* q, const void* k, const void* v, void* o, fl
   return hip_status(la::launch_decode(q, k, v, o, S, z, (int)BH, D, M, dtype == LINATTN_BF16, (hipStream_t)stream));
 }
 
+size_t deltanet_workspace_bytes(int B, int H, int N, int D, int M, int dtype) {
+  if (check_shape(B, H, N, D, M, dtype) != LINATTN_OK) return 0;
+  return la::deltanet_ws_bytes(B * H, N, D, M);
+}
+
 int deltanet_fwd(const void* q, const void* k, const void* v, const void* beta, void* o, int B, int H, int N, int D,
-                 int M, int dtype, const float* W0, float* W_out, void* stream) {
+                 int M, int dtype, const float* W0, float* W_out, void* ws, size_t ws_bytes, void* stream) {
   int st = check_shape(B, H, N, D, M, dtype);
   if (st) return st;
   const long long BH = (long long)B * H, es = esize(dtype);
   if (BH * N > 0 && (!q || !k || !v || !beta || !o)) return LINATTN_ERR_NULL;
-  if ((st = check_align({q, k, v, o, W0, W_out}))) return st;
+  if ((st = check_align({q, k, v, o, W0, W_out, ws}))) return st;
   if ((st = check_align_elem(beta, (int)es))) return st;
+  const size_t need = la::deltanet_ws_bytes((int)BH, N, D, M);
+  if (need > 0 && (!ws || ws_bytes < need)) return LINATTN_ERR_WORKSPACE;
   const long long nq = BH * N * D * es, nv = BH * N * M * es;
   const Span sq(q, nq), sk(k, nq), sv(v, nv), sb(beta, BH * N * es), so(o, nv);
-  const Span sW0(W0, BH * M * D * 4), sWo(W_out, BH * M * D * 4);
-  for (const Span& x : {sq, sk, sv, sb, sW0, sWo})
+  const Span sW0(W0, BH * M * D * 4), sWo(W_out, BH * M * D * 4), sws(ws, (long long)need);
+  for (const Span& x : {sq, sk, sv, sb, sW0, sWo, sws})
     if (so.overlaps(x)) return LINATTN_ERR_ALIAS;
-  for (const Span& x : {sq, sk, sv, sb})
+  for (const Span& x : {sq, sk, sv, sb, sws})
     if (sWo.overlaps(x)) return LINATTN_ERR_ALIAS;
   if (sWo.overlaps(sW0) && !sWo.same(sW0)) return LINATTN_ERR_ALIAS;
+  for (const Span& x : {sq, sk, sv, sb, sW0})
+    if (sws.overlaps(x)) return LINATTN_ERR_ALIAS;
   if (BH == 0 || (N == 0 && !W_out)) return LINATTN_OK;
   return hip_status(la::launch_deltanet(q, k, v, beta, o, (int)BH, N, D, M, dtype == LINATTN_BF16, W0, W_out,
-                                        (hipStream_t)stream));
+                                        need > 0 ? ws : nullptr, (hipStream_t)stream));
 }
 
 int deltanet_decode_step(const void* q, const void* k, const void* v, const void* beta, void* o, float* W, int B,

@@ -15,6 +15,9 @@
 // W (phi, the sum normalisation of k and q, the loads) is computed for a block
 // of 64 tokens at a time by the whole workgroup and staged in LDS, with the
 // next block's global loads in flight during the sequential phase.
+#include <stdlib.h>
+#include <string.h>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -292,8 +295,24 @@ __global__ __launch_bounds__(256) void memory_copy_kernel(const float* W0, float
   if (e < n) W_out[e] = W0 ? W0[e] : 0.f;
 }
 
+// Sequences run through the chunk-parallel kernels unless
+// LINATTN_DELTANET_PATH=sequential selects the token-by-token kernel (kept for
+// comparisons; it needs no workspace).
+static bool deltanet_chunked() {
+  static const bool chunked = [] {
+    const char* e = getenv("LINATTN_DELTANET_PATH");
+    return !(e && strcmp(e, "sequential") == 0);
+  }();
+  return chunked;
+}
+
+size_t deltanet_ws_bytes(int BH, int N, int D, int M) {
+  if (BH <= 0 || N <= 0 || !deltanet_chunked()) return 0;
+  return deltanet_chunk_ws_bytes(BH, N, D, M);
+}
+
 hipError_t launch_deltanet(const void* q, const void* k, const void* v, const void* beta, void* o, int BH, int N,
-                           int D, int M, int bf16, const float* W0, float* W_out, hipStream_t stream) {
+                           int D, int M, int bf16, const float* W0, float* W_out, void* ws, hipStream_t stream) {
   if (BH == 0) return hipSuccess;
   if (N == 0) {
     if (!W_out) return hipSuccess;
@@ -301,6 +320,7 @@ hipError_t launch_deltanet(const void* q, const void* k, const void* v, const vo
     hipLaunchKernelGGL(memory_copy_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, W0, W_out, n);
     return hipGetLastError();
   }
+  if (deltanet_chunked()) return launch_deltanet_chunked(q, k, v, beta, o, BH, N, D, M, bf16, W0, W_out, ws, stream);
   if (bf16) {
     LA_DISPATCH_DM(deltanet_impl, bf16_t, q, k, v, beta, o, BH, N, W0, W_out, stream)
   } else {

@@ -39,7 +39,13 @@ hipError_t launch_noncausal_bf16(const void* q, const void* k, const void* v, vo
 hipError_t launch_decode(const void* q, const void* k, const void* v, void* o, float* S, float* z, int BH, int D,
                          int M, int bf16, hipStream_t stream);
 hipError_t launch_deltanet(const void* q, const void* k, const void* v, const void* beta, void* o, int BH, int N,
-                           int D, int M, int bf16, const float* W0, float* W_out, hipStream_t stream);
+                           int D, int M, int bf16, const float* W0, float* W_out, void* ws, hipStream_t stream);
+// Chunk-parallel delta rule (prep, scan and output kernels) and the workspace it needs.
+size_t deltanet_chunk_ws_bytes(int BH, int N, int D, int M);
+hipError_t launch_deltanet_chunked(const void* q, const void* k, const void* v, const void* beta, void* o, int BH,
+                                   int N, int D, int M, int bf16, const float* W0, float* W_out, void* ws,
+                                   hipStream_t stream);
+size_t deltanet_ws_bytes(int BH, int N, int D, int M);
 hipError_t launch_deltanet_step(const void* q, const void* k, const void* v, const void* beta, void* o, float* W,
                                 int BH, int D, int M, int bf16, hipStream_t stream);
 
