@@ -13,23 +13,25 @@
 // L its strictly lower part and B = diag(beta), (I + B L) U = B (V - Kh W0^T),
 // i.e. U = Uc - Wc W0^T with the memory-independent Wc = T Kh and Uc = T V,
 // T = (I + B L)^{-1} B.  Then
-//   W_end = W0 + U^T Kh,   o_t = W0 qh_t + sum_{s<=t} (qh_t . kh_s) u_s.
-// Only W0 -> W_end is sequential; it costs two small matrix products per chunk.
+//   W_end = W0 + U^T Kh = W0 A + Bc,  A = I - Wc^T Kh,  Bc = Uc^T Kh,
+//   o_t = W0 qh_t + sum_{s<=t} (qh_t . kh_s) u_s.
+// A chunk maps the memory by an affine map (A, Bc) that does not depend on it,
+// so the only sequential work is one M x D by D x D product per chunk.
 //
 // Three kernels (fp32 arithmetic throughout, 16x16x4 f32 MFMA tiles):
-//   dn_prep_kernel  per (head, chunk), in parallel: kh, G on MFMA, then Wc and Uc
-//                   by forward substitution (one thread per column of [Kh | V]);
-//                   writes Kh, Wc, Uc.
-//   dn_scan_kernel  per (head, 16 rows of W): the chain over chunks,
-//                   X = Wc W0^T (the slice's columns), U = Uc - X, W += U^T Kh;
-//                   writes U and the memory at every chunk start.
-//   dn_out_kernel   per (head, chunk), in parallel: o = Qh W0^T + (Qh Kh^T, j <= i) U.
+//   dn_prep_kernel  per (head, chunk), in parallel: kh, G on MFMA, Wc and Uc by
+//                   forward substitution (one thread per column of [Kh | V]),
+//                   then A and Bc on MFMA; writes Kh, Wc, Uc, A, Bc.
+//   dn_scan_kernel  per head: W <- W A + Bc over the chunks, each wave a
+//                   16-row slice of W; writes the memory at every chunk start.
+//   dn_out_kernel   per (head, chunk), in parallel: U = Uc - Wc W0^T, then
+//                   o = Qh W0^T + (Qh Kh^T, j <= i) U.
 //
 // MFMA 16x16x4 f32 layouts (lane l = 16 g + n): operand a = A[n][g], b = B[g][n];
 // the accumulator holds D[4g + r][n] in element r.  The k index of a product may
 // be any permutation shared by both operands; the scan uses k = (tile dt, r) ->
 // d = 16 dt + 4 g + r so that the transposed memory tiles it keeps in registers
-// (the accumulator layout of the update) are directly the B operand of X.
+// (its own accumulator layout) are directly the B operand of the next chunk.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -46,8 +48,8 @@ struct G {
   static constexpr int VS = M + 4;   // row stride of v tiles
   static constexpr int GS = C + 4;   // row stride of the C x C tiles
   // Per-chunk records in the workspace (floats).
-  static constexpr size_t KH = (size_t)C * D, WC = (size_t)C * D, UC = (size_t)C * M, UU = (size_t)C * M,
-                          WS = (size_t)M * D;
+  static constexpr size_t KH = (size_t)C * D, WC = (size_t)C * D, UC = (size_t)C * M, AA = (size_t)D * D,
+                          BB = (size_t)M * D, WS = (size_t)M * D;
 };
 
 template <typename T> __device__ __forceinline__ float4 ld4(const T* p) { return load4<T>(p); }
@@ -85,14 +87,19 @@ template <typename T, int D, int M>
 __global__ __launch_bounds__(NT) void dn_prep_kernel(const T* __restrict__ k, const T* __restrict__ v,
                                                      const T* __restrict__ beta, int N, int nch,
                                                      float* __restrict__ kh_ws, float* __restrict__ wc_ws,
-                                                     float* __restrict__ uc_ws) {
+                                                     float* __restrict__ uc_ws, float* __restrict__ a_ws,
+                                                     float* __restrict__ b_ws) {
   using GG = G<D, M>;
   // Y = [Kh | V], one row per token: stride D + M + 4 keeps the column-slab reads
   // of the G product free of bank conflicts for every (D, M).
   constexpr int YS = D + M + 4;
+  constexpr int XS = D + M + 16;  // X = [Wc | Uc] row stride: (4kk + g) * XS = 16 g mod 64 banks
   __shared__ __attribute__((aligned(16))) float Ys[C * YS];
-  __shared__ __attribute__((aligned(16))) float Gs[C * GG::GS];
+  // G (during the substitution), then X = [Wc | Uc] (for the A and Bc products)
+  __shared__ __attribute__((aligned(16))) float GXs[C * (GG::GS > XS ? GG::GS : XS)];
   __shared__ float Bs[C];
+  float* Gs = GXs;
+  float* Xs = GXs;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
   const int bh = blockIdx.x / nch, c = blockIdx.x % nch;
   const int t0 = c * C, nt = min(C, N - t0);
@@ -115,16 +122,19 @@ __global__ __launch_bounds__(NT) void dn_prep_kernel(const T* __restrict__ k, co
   __syncthreads();
 
   // [Wc | Uc] = T [Kh | V]: x_t = beta_t (y_t - sum_{s<t} G[t][s] x_s), one column
-  // per thread; the column stays in registers.
+  // per thread, held in registers.  Right-looking order: once x_t is known it is
+  // removed from every later row at once (independent FMAs, and column t of G is
+  // its row t, G being symmetric).
   const size_t rec = (size_t)bh * nch + c;
+  float x[C];
   if (tid < D + M) {
-    float x[C];
+#pragma unroll
+    for (int t = 0; t < C; ++t) x[t] = Ys[t * YS + tid];
 #pragma unroll
     for (int t = 0; t < C; ++t) {
-      float acc = Ys[t * YS + tid];
+      x[t] *= Bs[t];
 #pragma unroll
-      for (int s = 0; s < t; ++s) acc -= Gs[t * GG::GS + s] * x[s];
-      x[t] = Bs[t] * acc;
+      for (int t2 = t + 1; t2 < C; ++t2) x[t2] -= Gs[t * GG::GS + t2] * x[t];
     }
     if (tid < D) {
 #pragma unroll
@@ -134,173 +144,192 @@ __global__ __launch_bounds__(NT) void dn_prep_kernel(const T* __restrict__ k, co
       for (int t = 0; t < C; ++t) uc_ws[rec * GG::UC + (size_t)t * M + (tid - D)] = x[t];
     }
   }
-  // Kh for the scan and output kernels.
+  // Kh for the output kernel.
   float* khd = kh_ws + rec * GG::KH;
   for (int u = tid; u < C * D / 4; u += NT) {
     const int row = u / (D / 4), c4 = (u % (D / 4)) * 4;
     *reinterpret_cast<float4*>(&khd[row * D + c4]) = *reinterpret_cast<const float4*>(&Ks[row * YS + c4]);
   }
+  __syncthreads();  // every read of G is done: its space takes X
+  if (tid < D + M) {
+#pragma unroll
+    for (int t = 0; t < C; ++t) Xs[t * XS + tid] = x[t];
+  }
+  __syncthreads();
+
+  // The chunk's affine map: A = I - Wc^T Kh (D x D), Bc = Uc^T Kh (M x D).  The
+  // TD * TD + TM * TD output tiles are dealt round robin to the waves; tile
+  // (i0, j0) = sum over tokens of X[t][i0 + i] Kh[t][j0 + j].
+  constexpr int NTA = GG::TD * GG::TD, NTB = GG::TM * GG::TD;
+  for (int tile = w; tile < NTA + NTB; tile += 4) {
+    const bool isa = tile < NTA;
+    const int tt = isa ? tile : tile - NTA;
+    const int it = tt / GG::TD, jt = tt % GG::TD;
+    const int xcol = (isa ? 0 : D) + 16 * it;
+    f32x4 acc{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < C / 4; ++kk)
+      acc = mma(Xs[(4 * kk + g) * XS + xcol + n], Ks[(4 * kk + g) * YS + 16 * jt + n], acc);
+    float* dst = isa ? a_ws + rec * GG::AA : b_ws + rec * GG::BB;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * it + 4 * g + r, j = 16 * jt + n;
+      dst[(size_t)i * D + j] = isa ? (i == j ? 1.f : 0.f) - acc[r] : acc[r];
+    }
+  }
 }
 
 // ----------------------------------------------------------------------------
-// Scan: grid (M/16) * BH, blockIdx.x = mg * BH + bh (the slices of one head are
-// BH workgroups apart, so with BH a multiple of 8 they share an XCD and its L2).
-// Wave w owns d-tile w of the transposed memory slice W^T[d][m0 .. m0 + 16); D/16
-// of the 4 waves are used for the update, all 4 for X (one 16-token tile each).
+// Scan: one workgroup per head; wave w keeps the 16-row slice m0 = 16 w of the
+// memory, transposed, in registers: wt[dt][r] = W^T[16 dt + 4 g + r][m0 + n].
+// Per chunk: W <- W A + Bc, i.e. W^T tile dt <- Bc^T tile dt + sum over k of
+// A[k][16 dt + i] W^T[k][m], with k = 16 dt' + 4 g + r.  A (shared by the
+// waves) is staged in LDS; each wave reads its Bc tiles from global memory.
 template <int D, int M>
-__global__ __launch_bounds__(NT) void dn_scan_kernel(const float* __restrict__ kh_ws, const float* __restrict__ wc_ws,
-                                                     const float* __restrict__ uc_ws, const float* __restrict__ W0,
-                                                     int BH, int nch, float* __restrict__ u_ws,
-                                                     float* __restrict__ ws_ws, float* __restrict__ W_out) {
+__global__ __launch_bounds__(NT) void dn_scan_kernel(const float* __restrict__ a_ws, const float* __restrict__ b_ws,
+                                                     const float* __restrict__ W0, int nch, float* __restrict__ ws_ws,
+                                                     float* __restrict__ W_out) {
   using GG = G<D, M>;
-  constexpr int WTS = C + 4;   // WcT row stride: (4g + r) * 68 = 16 g mod 64 banks
-  constexpr int KHS = 80;      // kh row stride: (4kk + g) * 80 = 16 g mod 64 banks
-  constexpr int UCS = 16;      // U / Uc slice row stride
-  constexpr int TS = 20;       // W^T exchange row stride
-  __shared__ __attribute__((aligned(16))) float WcT[D * WTS];  // Wc transposed: [d][t]
-  __shared__ __attribute__((aligned(16))) float Khs[C * KHS];  // kh: [t][d]
-  __shared__ __attribute__((aligned(16))) float Ucs[C * UCS];  // Uc slice: [t][m]
-  __shared__ __attribute__((aligned(16))) float Us[C * UCS];   // U slice: [t][m]
-  __shared__ __attribute__((aligned(16))) float Wts[D * TS];   // W^T slice: [d][m]
+  constexpr int AS = D + 4;  // A row stride: (4g + r) * AS = 16 g mod 64 banks at D = 64 (4 g at D = 32)
+  __shared__ __attribute__((aligned(16))) float As[2][D * AS];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
-  const int mg = blockIdx.x / BH, bh = blockIdx.x % BH, m0 = 16 * mg;
+  const int bh = blockIdx.x, m0 = 16 * w;
+  const bool active = w < GG::TM;  // waves past M/16 only help staging
 
-  // wt[dt][r] = W^T[16 dt + 4 g + r][m0 + n]
   f32x4 wt[GG::TD];
 #pragma unroll
   for (int dt = 0; dt < GG::TD; ++dt)
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      wt[dt][r] = W0 ? W0[((size_t)bh * M + m0 + n) * D + 16 * dt + 4 * g + r] : 0.f;
+      wt[dt][r] = (W0 && active) ? W0[((size_t)bh * M + m0 + n) * D + 16 * dt + 4 * g + r] : 0.f;
 
-  // Register staging of one chunk: Wc and kh as float4 units of rows, the Uc slice.
-  constexpr int NW4 = C * D / 4 / NT;   // float4 units per thread (Wc and kh each)
-  constexpr int NU4 = C * 16 / 4 / NT;  // Uc slice units per thread (1)
-  float4 rw[NW4], rk[NW4], ru[NU4 > 0 ? NU4 : 1];
+  // Register staging: A as float4 units of rows (all threads), this wave's Bc tiles.
+  constexpr int NA4 = D * D / 4 / NT > 0 ? D * D / 4 / NT : 1;
+  float4 ra[NA4];
+  f32x4 rb[GG::TD];
   auto load_chunk = [&](int c) __attribute__((always_inline)) {
     const size_t rec = (size_t)bh * nch + c;
 #pragma unroll
-    for (int i = 0; i < NW4; ++i) {
+    for (int i = 0; i < NA4; ++i) {
       const int u = tid + NT * i;
-      rw[i] = *reinterpret_cast<const float4*>(wc_ws + rec * GG::WC + 4 * u);
-      rk[i] = *reinterpret_cast<const float4*>(kh_ws + rec * GG::KH + 4 * u);
+      ra[i] = u < D * D / 4 ? *reinterpret_cast<const float4*>(a_ws + rec * GG::AA + 4 * u) : float4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
-    for (int i = 0; i < NU4; ++i) {
-      const int u = tid + NT * i, row = u / 4, c4 = (u % 4) * 4;
-      ru[i] = *reinterpret_cast<const float4*>(uc_ws + rec * GG::UC + (size_t)row * M + m0 + c4);
-    }
+    for (int dt = 0; dt < GG::TD; ++dt)
+      rb[dt] = active ? *reinterpret_cast<const f32x4*>(b_ws + rec * GG::BB + (size_t)(m0 + n) * D + 16 * dt + 4 * g)
+                      : f32x4{0.f, 0.f, 0.f, 0.f};
   };
   load_chunk(0);
 
   for (int c = 0; c < nch; ++c) {
     const size_t rec = (size_t)bh * nch + c;
-    // stage chunk c
+    float* Ab = As[c & 1];
 #pragma unroll
-    for (int i = 0; i < NW4; ++i) {
-      const int u = tid + NT * i, row = u / (D / 4), c4 = (u % (D / 4)) * 4;
-      WcT[(c4 + 0) * WTS + row] = rw[i].x;
-      WcT[(c4 + 1) * WTS + row] = rw[i].y;
-      WcT[(c4 + 2) * WTS + row] = rw[i].z;
-      WcT[(c4 + 3) * WTS + row] = rw[i].w;
-      *reinterpret_cast<float4*>(&Khs[row * KHS + c4]) = rk[i];
-    }
-#pragma unroll
-    for (int i = 0; i < NU4; ++i) {
-      const int u = tid + NT * i, row = u / 4, c4 = (u % 4) * 4;
-      *reinterpret_cast<float4*>(&Ucs[row * UCS + c4]) = ru[i];
+    for (int i = 0; i < NA4; ++i) {
+      const int u = tid + NT * i;
+      if (u < D * D / 4) *reinterpret_cast<float4*>(&Ab[(u / (D / 4)) * AS + (u % (D / 4)) * 4]) = ra[i];
     }
     // the memory at the chunk start, for the output kernel (W layout [m][d])
-    if (w < GG::TD)
-      *reinterpret_cast<f32x4*>(ws_ws + rec * GG::WS + (size_t)(m0 + n) * D + 16 * w + 4 * g) = wt[w];
-    __syncthreads();                     // (1) chunk staged
-    if (c + 1 < nch) load_chunk(c + 1);  // in flight during the chain
-
-    // X tile (tokens 16w .. 16w + 15) = Wc W0^T, k = (dt, r) -> d = 16 dt + 4 g + r
-    f32x4 x{0.f, 0.f, 0.f, 0.f};
+    if (active) {
 #pragma unroll
-    for (int dt = 0; dt < GG::TD; ++dt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) x = mma(WcT[(16 * dt + 4 * g + r) * WTS + 16 * w + n], wt[dt][r], x);
-    // U = Uc - X: lane (n, g) holds rows t = 16w + 4g + r of column m0 + n
-    f32x4 u;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 16 * w + 4 * g + r;
-      u[r] = Ucs[t * UCS + n] - x[r];
-      Us[t * UCS + n] = u[r];
+      for (int dt = 0; dt < GG::TD; ++dt)
+        *reinterpret_cast<f32x4*>(ws_ws + rec * GG::WS + (size_t)(m0 + n) * D + 16 * dt + 4 * g) = wt[dt];
     }
+    f32x4 acc[GG::TD];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) u_ws[rec * GG::UU + (size_t)(16 * w + 4 * g + r) * M + m0 + n] = u[r];
-    __syncthreads();  // (2) U complete
-
-    // W^T tile w += Kh^T U: A[d][t] = kh[t][d], B[t][m] = U[t][m]
-    if (w < GG::TD) {
-      f32x4 acc = wt[w];
+    for (int dt = 0; dt < GG::TD; ++dt) acc[dt] = rb[dt];
+    // One barrier per chunk: buffer c & 1 is rewritten two chunks later, after
+    // every wave has passed the next chunk's barrier.
+    __syncthreads();
+    if (c + 1 < nch) load_chunk(c + 1);
 #pragma unroll
-      for (int kk = 0; kk < C / 4; ++kk) acc = mma(Khs[(4 * kk + g) * KHS + 16 * w + n], Us[(4 * kk + g) * UCS + n], acc);
+    for (int dk = 0; dk < GG::TD; ++dk)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Wts[(16 * w + 4 * g + r) * TS + n] = acc[r];
-    }
-    __syncthreads();  // (3) updated memory published
+      for (int r = 0; r < 4; ++r)
 #pragma unroll
-    for (int dt = 0; dt < GG::TD; ++dt)
+        for (int dt = 0; dt < GG::TD; ++dt)
+          acc[dt] = mma(Ab[(16 * dk + 4 * g + r) * AS + 16 * dt + n], wt[dk][r], acc[dt]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) wt[dt][r] = Wts[(16 * dt + 4 * g + r) * TS + n];
+    for (int dt = 0; dt < GG::TD; ++dt) wt[dt] = acc[dt];
   }
-  if (W_out && w < GG::TD)
-    *reinterpret_cast<f32x4*>(W_out + ((size_t)bh * M + m0 + n) * D + 16 * w + 4 * g) = wt[w];
+  if (W_out && active) {
+#pragma unroll
+    for (int dt = 0; dt < GG::TD; ++dt)
+      *reinterpret_cast<f32x4*>(W_out + ((size_t)bh * M + m0 + n) * D + 16 * dt + 4 * g) = wt[dt];
+  }
 }
 
 // ----------------------------------------------------------------------------
 // Outputs: grid BH * nch, blockIdx.x = bh * nch + c.  Wave w owns tokens
 // 16w .. 16w + 15 of the chunk.
+//  1. U rows of the wave: U = Uc - Wc W0^T (in place over Uc in LDS).
+//  2. Score tiles transposed, S^T[s][t] = kh_s . qh_t for the wave's tokens t,
+//     zero where s > t.  Lane (n, g) of tile st holds s = 16 st + 4 g + r and
+//     t = 16 w + n, which with k = (st, r) is exactly the A operand of step 3.
+//  3. o = Qh W0^T + S U.
 template <typename T, int D, int M>
 __global__ __launch_bounds__(NT) void dn_out_kernel(const T* __restrict__ q, const float* __restrict__ kh_ws,
-                                                    const float* __restrict__ u_ws, const float* __restrict__ ws_ws,
-                                                    int N, int nch, T* __restrict__ o) {
+                                                    const float* __restrict__ wc_ws, const float* __restrict__ uc_ws,
+                                                    const float* __restrict__ ws_ws, int N, int nch,
+                                                    T* __restrict__ o) {
   using GG = G<D, M>;
-  __shared__ __attribute__((aligned(16))) float Qs[C * GG::KS];
-  __shared__ __attribute__((aligned(16))) float Ks[C * GG::KS];
-  __shared__ __attribute__((aligned(16))) float As[C * GG::GS];  // (qh . kh) with j <= i
-  constexpr int US = M + 16;  // U row stride: (4kk + g) * US = 16 g mod 64 banks
-  __shared__ __attribute__((aligned(16))) float Us[C * US];      // U [t][m]
-  __shared__ __attribute__((aligned(16))) float Wss[M * GG::KS]; // W0 [m][d]
+  constexpr int US = M + 4;  // U row stride: (4g + r) rows apart = 16 g mod 64 banks at M = 64
+  __shared__ __attribute__((aligned(16))) float Xs[C * GG::KS];   // Wc rows, then qh rows
+  __shared__ __attribute__((aligned(16))) float Ks[C * GG::KS];   // kh [t][d]
+  __shared__ __attribute__((aligned(16))) float Wss[M * GG::KS];  // W0 [m][d]
+  __shared__ __attribute__((aligned(16))) float Us[C * US];       // Uc, then U [t][m]
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
   const int bh = blockIdx.x / nch, c = blockIdx.x % nch;
   const int t0 = c * C, nt = min(C, N - t0);
   const size_t rec = (size_t)bh * nch + c;
-  load_rows<T, D, GG::KS, true>(Qs, q + ((size_t)bh * N + t0) * D, nt, tid);
+  load_rows<float, D, GG::KS, false>(Xs, wc_ws + rec * GG::WC, C, tid);
   load_rows<float, D, GG::KS, false>(Ks, kh_ws + rec * GG::KH, C, tid);
-  load_rows<float, M, US, false>(Us, u_ws + rec * GG::UU, C, tid);
+  load_rows<float, M, US, false>(Us, uc_ws + rec * GG::UC, C, tid);
   load_rows<float, D, GG::KS, false, M>(Wss, ws_ws + rec * GG::WS, M, tid);
   __syncthreads();
 
-  // A tiles of row tile w: (qh_i . kh_j), zero where j > i
+  // 1. U = Uc - Wc W0^T for tokens 16w .. 16w + 15
+#pragma unroll
+  for (int mt = 0; mt < GG::TM; ++mt) {
+    f32x4 acc{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < D / 4; ++kk)
+      acc = mma(Xs[(16 * w + n) * GG::KS + 4 * kk + g], Wss[(16 * mt + n) * GG::KS + 4 * kk + g], acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float& u = Us[(16 * w + 4 * g + r) * US + 16 * mt + n];
+      u = u - acc[r];
+    }
+  }
+  __syncthreads();  // U complete; Wc no longer read
+  load_rows<T, D, GG::KS, true>(Xs, q + ((size_t)bh * N + t0) * D, nt, tid);
+  __syncthreads();
+
+  // 2. transposed, masked score tiles
+  f32x4 st4[C / 16];
 #pragma unroll
   for (int st = 0; st < C / 16; ++st) {
     f32x4 acc{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < D / 4; ++kk)
-      acc = mma(Qs[(16 * w + n) * GG::KS + 4 * kk + g], Ks[(16 * st + n) * GG::KS + 4 * kk + g], acc);
+      acc = mma(Ks[(16 * st + n) * GG::KS + 4 * kk + g], Xs[(16 * w + n) * GG::KS + 4 * kk + g], acc);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 16 * w + 4 * g + r, j = 16 * st + n;
-      As[i * GG::GS + j] = j <= i ? acc[r] : 0.f;
-    }
+    for (int r = 0; r < 4; ++r) acc[r] = (16 * st + 4 * g + r <= 16 * w + n) ? acc[r] : 0.f;
+    st4[st] = acc;
   }
-  __syncthreads();
 
+  // 3. o = Qh W0^T + S U
   T* oh = o + ((size_t)bh * N + t0) * M;
 #pragma unroll
   for (int mt = 0; mt < GG::TM; ++mt) {
     f32x4 acc{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < D / 4; ++kk)
-      acc = mma(Qs[(16 * w + n) * GG::KS + 4 * kk + g], Wss[(16 * mt + n) * GG::KS + 4 * kk + g], acc);
+      acc = mma(Xs[(16 * w + n) * GG::KS + 4 * kk + g], Wss[(16 * mt + n) * GG::KS + 4 * kk + g], acc);
 #pragma unroll
-    for (int kk = 0; kk < C / 4; ++kk)
-      acc = mma(As[(16 * w + n) * GG::GS + 4 * kk + g], Us[(4 * kk + g) * US + 16 * mt + n], acc);
+    for (int st = 0; st < C / 16; ++st)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc = mma(st4[st][r], Us[(16 * st + 4 * g + r) * US + 16 * mt + n], acc);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = 16 * w + 4 * g + r;
@@ -315,7 +344,7 @@ template <int D, int M>
 static size_t ws_floats(int BH, int N) {
   using GG = G<D, M>;
   const size_t nch = (size_t)((N + C - 1) / C);
-  return (size_t)BH * nch * (GG::KH + GG::WC + GG::UC + GG::UU + GG::WS);
+  return (size_t)BH * nch * (GG::KH + GG::WC + GG::UC + GG::AA + GG::BB + GG::WS);
 }
 
 template <typename T, int D, int M>
@@ -327,14 +356,14 @@ static hipError_t impl(const void* q, const void* k, const void* v, const void* 
   float* kh = (float*)ws;
   float* wc = kh + rec * GG::KH;
   float* uc = wc + rec * GG::WC;
-  float* uu = uc + rec * GG::UC;
-  float* wsb = uu + rec * GG::UU;
+  float* aa = uc + rec * GG::UC;
+  float* bb = aa + rec * GG::AA;
+  float* wsb = bb + rec * GG::BB;
   const dim3 block(NT), grid((unsigned)rec);
   hipLaunchKernelGGL((dn_prep_kernel<T, D, M>), grid, block, 0, stream, (const T*)k, (const T*)v, (const T*)beta, N,
-                     nch, kh, wc, uc);
-  hipLaunchKernelGGL((dn_scan_kernel<D, M>), dim3((unsigned)(BH * (M / 16))), block, 0, stream, kh, wc, uc, W0, BH,
-                     nch, uu, wsb, W_out);
-  hipLaunchKernelGGL((dn_out_kernel<T, D, M>), grid, block, 0, stream, (const T*)q, kh, uu, wsb, N, nch, (T*)o);
+                     nch, kh, wc, uc, aa, bb);
+  hipLaunchKernelGGL((dn_scan_kernel<D, M>), dim3((unsigned)BH), block, 0, stream, aa, bb, W0, nch, wsb, W_out);
+  hipLaunchKernelGGL((dn_out_kernel<T, D, M>), grid, block, 0, stream, (const T*)q, kh, wc, uc, wsb, N, nch, (T*)o);
   return hipGetLastError();
 }
 
