@@ -186,3 +186,6 @@ def deltanet(q, k, v, beta, W0=None):
     W = np.empty((B, H, M, D))
     _load().oracle_deltanet(_p(q), _p(k), _p(v), _p(beta), B * H, N, D, M, _p(W0), _p(o), _p(W))
     return o, W
+
+
+from .gradients import causal_bwd  # noqa: E402  (fp64 autograd of the forward definition)

@@ -382,3 +382,78 @@ def test_nan_propagates():
     v[0, 0, 2, 1] = np.nan
     o, _, _ = oracle.causal(q, k, v)
     assert np.all(np.isfinite(o[0, 0, :2])) and np.isnan(o[0, 0, 2:, 1]).all()
+
+
+# ------------------------------------------- gradients (§3.3.1; equations not printed)
+
+def _bwd_inputs(B, H, N, D, M, seed):
+    return (rnd((B, H, N, D), seed), rnd((B, H, N, D), seed + 1), rnd((B, H, N, M), seed + 2),
+            rnd((B, H, N, M), seed + 3))
+
+
+def test_bwd_matches_central_finite_differences():
+    """Every input element: autograd of the oracle against (L(x+h) - L(x-h)) / 2h."""
+    from oracle import gradients
+    q, k, v, dO = _bwd_inputs(1, 2, 6, 3, 2, 11)
+    dq, dk, dv = gradients.causal_bwd(q, k, v, dO)
+    h = 1e-6
+    for name, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = {"q": q, "k": k, "v": v}
+            args_m = dict(args_p)
+            args_p[name], args_m[name] = xp, xm
+            fd = (gradients.causal_loss(args_p["q"], args_p["k"], args_p["v"], dO)
+                  - gradients.causal_loss(args_m["q"], args_m["k"], args_m["v"], dO)) / (2 * h)
+            assert abs(fd - grad[idx]) < 1e-6 * max(1.0, abs(grad[idx])), (name, idx, fd, grad[idx])
+
+
+def test_bwd_recurrent_and_explicit_forms_agree():
+    """Autograd through the prefix sums (eq.(10)-(12)) and through the masked matrix (eq.(9))."""
+    from oracle import gradients
+    q, k, v, dO = _bwd_inputs(2, 2, 50, 8, 5, 21)
+    r = gradients.causal_bwd(q, k, v, dO, form="recurrent")
+    e = gradients.causal_bwd(q, k, v, dO, form="explicit")
+    for a, b in zip(r, e):
+        assert mat_rel_err(a, b) < 1e-12
+
+
+def test_bwd_single_token_passes_values_through():
+    """N = 1: o = v whatever q, k, so dv = dO and dq = dk = 0."""
+    q, k, v, dO = _bwd_inputs(2, 3, 1, 8, 5, 31)
+    dq, dk, dv = oracle.causal_bwd(q, k, v, dO)
+    np.testing.assert_allclose(dv, dO, rtol=1e-14, atol=1e-14)
+    assert np.abs(dq).max() < 1e-13 and np.abs(dk).max() < 1e-13
+
+
+def test_bwd_is_causal():
+    """dq_i depends on keys and values j <= i only; dk_j, dv_j on output gradients i >= j only."""
+    q, k, v, dO = _bwd_inputs(1, 2, 40, 6, 4, 41)
+    dq, dk, dv = oracle.causal_bwd(q, k, v, dO)
+    k2, v2 = k.copy(), v.copy()
+    k2[:, :, 25:] += 1.0
+    v2[:, :, 25:] -= 2.0
+    dq2, _, _ = oracle.causal_bwd(q, k2, v2, dO)
+    np.testing.assert_allclose(dq2[:, :, :25], dq[:, :, :25], rtol=1e-12, atol=1e-14)
+    dO2 = dO.copy()
+    dO2[:, :, :25] *= -3.0
+    _, dk2, dv2 = oracle.causal_bwd(q, k, v, dO2)
+    np.testing.assert_allclose(dk2[:, :, 25:], dk[:, :, 25:], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(dv2[:, :, 25:], dv[:, :, 25:], rtol=1e-12, atol=1e-14)
+
+
+def test_bwd_invariants_of_the_normalised_form():
+    """o_i is a convex combination of v_1..v_i with weights homogeneous of degree 0 in phi(q_i):
+    (a) the derivative along phi(q_i) vanishes: sum_d dphi(q)_id phi(q)_id = 0;
+    (b) shifting every v by c shifts every o by c: dq, dk do not change and sum_j dv_j = sum_i dO_i."""
+    q, k, v, dO = _bwd_inputs(2, 2, 30, 5, 3, 51)
+    dq, dk, dv = oracle.causal_bwd(q, k, v, dO)
+    dphi = np.where(q > 0, 1.0, np.exp(np.minimum(q, 0.0)))
+    fq = phi_lib(q)
+    radial = (dq / dphi * fq).sum(axis=-1)
+    assert np.abs(radial).max() < 1e-12 * max(1.0, np.abs(dq).max())
+    dq2, dk2, _ = oracle.causal_bwd(q, k, v + np.array([0.7, -1.3, 2.0]), dO)
+    assert mat_rel_err(dq2, dq) < 1e-12 and mat_rel_err(dk2, dk) < 1e-12
+    np.testing.assert_allclose(dv.sum(axis=2), dO.sum(axis=2), rtol=1e-12, atol=1e-12)
