@@ -95,6 +95,20 @@ def time_oracle(workload, inputs, budget_s: float = 20.0):
         return {"value": nh * (w.N + T) / dt, "unit": "head-tokens/s", "cores": threads, "kind": "oracle",
                 "sample": f"prefill {w.N} tokens + {T} of {w.steps} steps on all {nh} states, {dt:.1f} s, "
                           f"{cpu_model()}"}
+    if w.name == "causal_long" and len(inputs) == 4:  # backward: one head, then as many as the budget allows
+        import torch
+        from oracle import gradients
+        q, k, v, dO = inputs
+        t0 = time.perf_counter()
+        gradients.causal_bwd(q[:1, :1], k[:1, :1], v[:1, :1], dO[:1, :1])
+        one = time.perf_counter() - t0
+        nh = max(1, min(w.B * w.H, int(budget_s / max(one, 1e-6))))
+        qf, kf, vf, gf = (t.reshape(1, w.B * w.H, w.N, -1)[:, :nh] for t in (q, k, v, dO))
+        t0 = time.perf_counter()
+        gradients.causal_bwd(qf, kf, vf, gf)
+        dt = time.perf_counter() - t0
+        return {"value": nh * w.N / dt, "unit": "tokens/s", "cores": torch.get_num_threads(), "kind": "oracle",
+                "sample": f"{nh} of {w.B * w.H} heads, all {w.N} tokens (fp64 autograd), {dt:.1f} s, {cpu_model()}"}
     if w.name == "deltanet_decode":
         q, k, v, beta, sq, sk, sv, sb = inputs
         nh = w.B * w.H
@@ -146,7 +160,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="causal_long",
-                    choices=["causal_long", "noncausal_long", "decode", "deltanet", "deltanet_decode", "causal_mid", "copy"])
+                    choices=["causal_long", "causal_bwd_long", "noncausal_long", "decode", "deltanet", "deltanet_decode",
+                             "causal_mid", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--oracle-budget", type=float, default=20.0)
     args = ap.parse_args()
@@ -190,7 +205,7 @@ def main():
                           "ms_per_step": ms, "higher_is_better": True, "bytes_per_copy": nbytes}), flush=True)
         return
 
-    wname = "causal_long" if args.workload == "noncausal_long" else args.workload
+    wname = "causal_long" if args.workload in ("noncausal_long", "causal_bwd_long") else args.workload
     w = synth.WORKLOADS[wname]
     inputs = synth.workload_inputs(w)
     K, Wm = args.steps, args.warmup
@@ -216,6 +231,21 @@ def main():
         alg_bytes = units * (2 * w.D + 2 * w.M) * es  # read q, k, v; write o
         unit = "tokens/s"
         launches_per_step = 1
+    elif args.workload == "causal_bwd_long":
+        q, k, v = (t.to(dev) for t in inputs)
+        dO = synth.qkv(w.B, w.H, w.N, w.M, w.M, dtype=w.dtype, seed=w.seed + 50)[0].to(dev)
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+        ws = torch.empty(max(1, la.causal_bwd_workspace_bytes(w.B, w.H, w.N, w.D, w.M, w.dtype)), dtype=torch.uint8,
+                         device=dev)
+        step = lambda: la.causal_bwd(q, k, v, dO, out=grads, workspace=ws)
+        kernel = ("linattn_causal_bwd (block_state + state_scan + bwd_q + bwd_rstate + suffix_scan + bwd_kv "
+                  "kernels)")
+        units = w.B * w.H * w.N
+        es = 2
+        alg_bytes = units * (4 * w.D + 3 * w.M) * es  # read q, k, v, dO; write dq, dk, dv
+        unit = "tokens/s"
+        launches_per_step = 1
+        inputs = (inputs[0], inputs[1], inputs[2], dO.cpu())
     elif args.workload == "decode":
         pq, pk, pv, sq, sk, sv = inputs
         pq, pk, pv = pq.to(dev), pk.to(dev), pv.to(dev)
@@ -305,13 +335,15 @@ def main():
                        f"B={w.B} H={w.H} N={w.N} D=M={w.D}",
         "noncausal_long": f"noncausal_long: non-causal linear attention, bf16, B={w.B} H={w.H} N={w.N} D=M={w.D}",
         "causal_mid": f"causal_mid: causal linear attention, fp32, B={w.B} H={w.H} N={w.N} D=M={w.D}",
+        "causal_bwd_long": f"causal_bwd_long: backward of causal linear attention (dq, dk, dv), bf16 in/out, fp32 "
+                           f"arithmetic, B={w.B} H={w.H} N={w.N} D=M={w.D}",
         "decode": f"decode: RNN-form decode, {w.B}x{w.H} states D=M={w.D}, {w.steps} single-token bf16 steps "
                   f"after a {w.N}-token prefill",
         "deltanet": f"deltanet: delta-rule fast weights, fp32, B={w.B} H={w.H} N={w.N} D=M={w.D}",
         "deltanet_decode": f"deltanet_decode: delta-rule decode, {w.B}x{w.H} memories D=M={w.D}, {w.steps} "
                            f"single-token bf16 steps after a {w.N}-token prefill",
     }
-    dtype = {"causal_long": "bf16", "noncausal_long": "bf16", "decode": "bf16", "causal_mid": "f32",
+    dtype = {"causal_long": "bf16", "causal_bwd_long": "bf16", "noncausal_long": "bf16", "decode": "bf16", "causal_mid": "f32",
              "deltanet": "f32", "deltanet_decode": "bf16"}[args.workload]
     line = {
         "metric": METRIC if args.workload == "causal_long" else f"{args.workload} {unit}",

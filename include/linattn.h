@@ -10,6 +10,7 @@
  *                  S_i = sum_{j<=i} phi(k_j) v_j^T,  z_i = sum_{j<=i} phi(k_j)
  *                  (same page, §3.3 eq.(9)-(12); the mask j <= i is inclusive);
  *   - non-causal:  the same with the sums over every j = 1..N (§3.2 eq.(5)-(6));
+ *   - causal backward: dq, dk, dv of the causal form (§3.3.1);
  *   - decode step: one step of the RNN form, state updated first and then read
  *                  (§3.4 eq.(16)-(20), without f_l and the residual);
  *   - delta rule:  the fast-weight memory W (M x D) of "Linear Transformers Are
@@ -95,6 +96,26 @@ size_t linattn_causal_workspace_bytes(int B, int H, int N, int D, int M, int dty
 int linattn_causal_fwd(const void* q, const void* k, const void* v, void* o,
                        int B, int H, int N, int D, int M, int dtype,
                        const float* S0, const float* z0, float* S_out, float* z_out,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of device workspace linattn_causal_bwd needs (0 when none). */
+size_t linattn_causal_bwd_workspace_bytes(int B, int H, int N, int D, int M, int dtype);
+
+/* Backward of the causal form for a sequence that starts from a zero state:
+ * given dO = dL/do, the gradients dq, dk, dv of L through eq.(9)-(12) and phi
+ * (§3.3.1 states that they are cumulative sums computable in linear time and
+ * constant memory, without printing them).  With a_i = dO_i / den_i and
+ * b_i = -(dO_i . o_i) / den_i:
+ *   dphi(q_i) = S_i a_i + z_i b_i,
+ *   dphi(k_j) = sum_{i>=j} phi(q_i) (a_i . v_j + b_i),
+ *   dv_j      = sum_{i>=j} (phi(q_i) . phi(k_j)) a_i,
+ *   dq = dphi(q) * phi'(q), dk = dphi(k) * phi'(k).
+ * q, k, dq, dk: [B,H,N,D]; v, dO, dv: [B,H,N,M], all in dtype; arithmetic is
+ * float32 for both dtypes.  The forward output is recomputed, not an input.
+ * ws, ws_bytes: device workspace of at least linattn_causal_bwd_workspace_bytes().
+ * dq, dk, dv must not overlap each other, the inputs or ws. */
+int linattn_causal_bwd(const void* q, const void* k, const void* v, const void* dO,
+                       void* dq, void* dk, void* dv, int B, int H, int N, int D, int M, int dtype,
                        void* ws, size_t ws_bytes, void* stream);
 
 /* Bytes of device workspace linattn_noncausal_fwd needs (0 when none). */

@@ -173,6 +173,32 @@ def test_deltanet_validation(lib):
 
 
 @no_gpu
+def test_causal_bwd_validation(lib):
+    f = lib.linattn_causal_bwd
+    need = lib.linattn_causal_bwd_workspace_bytes(2, 16, 32768, 64, 64, 1)
+    assert need > 0
+    DQ, DK, DV, DO = SO, ZO, Z0, S0
+    args = [Q, K, V, DO, DQ, DK, DV, 2, 16, 32768, 64, 64, 1, WSP, need, None]
+    bad = list(args); bad[3] = None
+    assert f(*bad) == NULL
+    bad = list(args); bad[13] = None
+    assert f(*bad) == WS
+    bad = list(args); bad[14] = need - 16
+    assert f(*bad) == WS
+    bad = list(args); bad[4] = Q
+    assert f(*bad) == ALIAS        # dq over q
+    bad = list(args); bad[5] = DQ + 64
+    assert f(*bad) == ALIAS        # dk overlapping dq
+    bad = list(args); bad[13] = V
+    assert f(*bad) == ALIAS        # workspace over v
+    bad = list(args); bad[10] = 48
+    assert f(*bad) == UNSUP
+    bad = list(args); bad[6] = DV + 8
+    assert f(*bad) == ALIGN
+    assert f(None, None, None, None, None, None, None, 2, 16, 0, 64, 64, 1, None, 0, None) == OK
+
+
+@no_gpu
 def test_deltanet_decode_validation(lib):
     f = lib.deltanet_decode_step
     args = [Q, K, V, BETA, O, S0, 256, 16, 64, 64, 1, None]

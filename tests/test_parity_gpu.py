@@ -395,3 +395,60 @@ def test_deltanet_decode_workload_sampled_heads():
                                       sb[t][bi, hi][None], rW_s)
         assert row_rel_err(outs[t][bi, hi][None], ro) < 2e-2, t
     assert mat_rel_err(host(W)[bi, hi][None], rW_s) < 1e-4
+
+
+# ------------------------------------------------------------- causal backward
+
+BWD_TOL = {torch.float32: 1e-4, torch.bfloat16: 1e-2}
+
+
+def _grad_err(got, ref, scale):
+    """max |got - ref| over max |ref|, the latter floored at 1e-3 of the scale of all
+    three gradients (dq and dk vanish identically at N = 1, where o = v)."""
+    got = got.to(torch.float64).numpy() if isinstance(got, torch.Tensor) else np.asarray(got, dtype=np.float64)
+    return float(np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-3 * scale))
+
+
+def _bwd_check(q, k, v, dO, dtype):
+    dq, dk, dv = la.causal_bwd(*gpu(q, k, v, dO))
+    rq, rk, rv = oracle.causal_bwd(q, k, v, dO)
+    scale = max(np.abs(rq).max(), np.abs(rk).max(), np.abs(rv).max())
+    for got, ref, name in ((dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv")):
+        e = _grad_err(host(got), ref, scale)
+        assert e < BWD_TOL[dtype], (name, e)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("D,M", [(32, 32), (32, 64), (64, 32), (64, 64)])
+@pytest.mark.parametrize("N", [1, 63, 64, 65, 300, 2500])
+def test_causal_bwd_ragged(dtype, D, M, N):
+    """Every size class: a single token, chunk edges, several chunks and blocks."""
+    say("causal bwd", dtype, D, M, N)
+    q, k, v = synth.qkv(2, 2, N, D, M, dtype=dtype, scale=0.5, seed=N + D + 2 * M)
+    dO = synth.qkv(2, 2, N, M, M, dtype=dtype, seed=N + 7)[0]
+    _bwd_check(q, k, v, dO, dtype)
+
+
+def test_causal_bwd_many_blocks():
+    """Many blocks per head (the prefix and suffix scans across blocks)."""
+    q, k, v = synth.qkv(1, 3, 9000, 64, 64, dtype=torch.float32, scale=0.5, seed=5)
+    dO = synth.qkv(1, 3, 9000, 64, 64, seed=6)[0]
+    say("causal bwd many blocks")
+    _bwd_check(q, k, v, dO, torch.float32)
+
+
+def test_causal_bwd_long_workload_sampled_head():
+    """The long bf16 workload (B=2 H=16 N=32768 D=M=64), every head computed on
+    the GPU; two heads checked in full against the oracle."""
+    w = synth.WORKLOADS["causal_long"]
+    say("causal bwd long", w)
+    q, k, v = synth.workload_inputs(w)
+    dO = synth.qkv(w.B, w.H, w.N, w.M, w.M, dtype=w.dtype, seed=w.seed + 50)[0]
+    dq, dk, dv = (host(t) for t in la.causal_bwd(*gpu(q, k, v, dO)))
+    for b, h in ((0, 3), (1, 15)):
+        sel = (slice(b, b + 1), slice(h, h + 1))
+        rq, rk, rv = oracle.causal_bwd(q[sel], k[sel], v[sel], dO[sel])
+        scale = max(np.abs(rq).max(), np.abs(rk).max(), np.abs(rv).max())
+        for got, ref, name in ((dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv")):
+            e = _grad_err(got[sel], ref, scale)
+            assert e < 1e-2, (b, h, name, e)

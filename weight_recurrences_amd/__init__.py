@@ -16,7 +16,7 @@ import torch
 
 from ._lib import BF16, F32, LinAttnError, check, load
 
-__all__ = ["causal", "noncausal", "decode_step", "deltanet", "deltanet_decode_step", "causal_workspace_bytes",
+__all__ = ["causal", "causal_bwd", "causal_bwd_workspace_bytes", "noncausal", "decode_step", "deltanet", "deltanet_decode_step", "causal_workspace_bytes",
            "noncausal_workspace_bytes", "deltanet_workspace_bytes", "LinAttnError", "abi_version"]
 
 _DT = {torch.float32: F32, torch.bfloat16: BF16}
@@ -108,6 +108,36 @@ def causal(q, k, v, *, state=None, return_state=False, output=True, out=None, wo
     if not output:
         return S, z
     return (o, (S, z)) if return_state else o
+
+
+def causal_bwd_workspace_bytes(B, H, N, D, M, dtype) -> int:
+    return int(load().linattn_causal_bwd_workspace_bytes(B, H, N, D, M, _DT[dtype]))
+
+
+def causal_bwd(q, k, v, dO, *, out=None, workspace=None):
+    """Gradients (dq, dk, dv) of sum(dO * causal(q, k, v)) from a zero state.
+
+    q, k: [B,H,N,D]; v, dO: [B,H,N,M] (float32 or bfloat16, one dtype); the
+    gradients come back in that dtype.  ``out`` may give (dq, dk, dv)."""
+    lib = load()
+    dev = _dev(q, k, v, dO)
+    B, H, N, D = q.shape
+    M = v.shape[-1]
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or dO.shape != v.shape:
+        raise ValueError("q, k [B,H,N,D], v, dO [B,H,N,M] expected")
+    if k.dtype != q.dtype or v.dtype != q.dtype or dO.dtype != q.dtype:
+        raise ValueError("q, k, v, dO must share a dtype")
+    dt = _dtype_code(q)
+    if out is not None:
+        dq, dk, dv = out
+    else:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    need = int(lib.linattn_causal_bwd_workspace_bytes(B, H, N, D, M, dt))
+    ws = _workspace(need, dev, workspace)
+    rc = lib.linattn_causal_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, D, M,
+                                dt, _ptr(ws), need, _stream(dev))
+    check(rc, "linattn_causal_bwd")
+    return dq, dk, dv
 
 
 def noncausal(q, k, v, *, out=None, workspace=None):

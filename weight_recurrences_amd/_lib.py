@@ -32,6 +32,8 @@ _sz = ctypes.c_size_t
 SIGNATURES = {
     "linattn_causal_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "linattn_causal_fwd": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "linattn_causal_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "linattn_causal_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
     "linattn_noncausal_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "linattn_noncausal_fwd": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
     "linattn_decode_step": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),

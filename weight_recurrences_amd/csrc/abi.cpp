@@ -68,6 +68,33 @@ size_t linattn_causal_workspace_bytes(int B, int H, int N, int D, int M, int dty
   return la::causal_ws_bytes(B * H, N, D, M, dtype == LINATTN_BF16);
 }
 
+size_t linattn_causal_bwd_workspace_bytes(int B, int H, int N, int D, int M, int dtype) {
+  if (check_shape(B, H, N, D, M, dtype) != LINATTN_OK) return 0;
+  return la::causal_bwd_ws_bytes(B * H, N, D, M);
+}
+
+int linattn_causal_bwd(const void* q, const void* k, const void* v, const void* dO, void* dq, void* dk, void* dv,
+                       int B, int H, int N, int D, int M, int dtype, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_shape(B, H, N, D, M, dtype);
+  if (st) return st;
+  const long long BH = (long long)B * H, es = esize(dtype);
+  if (BH * N == 0) return LINATTN_OK;
+  if (!q || !k || !v || !dO || !dq || !dk || !dv) return LINATTN_ERR_NULL;
+  if ((st = check_align({q, k, v, dO, dq, dk, dv, ws}))) return st;
+  const size_t need = la::causal_bwd_ws_bytes((int)BH, N, D, M);
+  if (need > 0 && (!ws || ws_bytes < need)) return LINATTN_ERR_WORKSPACE;
+  const long long nq = BH * N * D * es, nv = BH * N * M * es;
+  const Span sq(q, nq), sk(k, nq), sv(v, nv), sg(dO, nv), sdq(dq, nq), sdk(dk, nq), sdv(dv, nv), sws(ws, (long long)need);
+  for (const Span& out : {sdq, sdk, sdv})
+    for (const Span& x : {sq, sk, sv, sg, sws})
+      if (out.overlaps(x)) return LINATTN_ERR_ALIAS;
+  if (sdq.overlaps(sdk) || sdq.overlaps(sdv) || sdk.overlaps(sdv)) return LINATTN_ERR_ALIAS;
+  for (const Span& x : {sq, sk, sv, sg})
+    if (sws.overlaps(x)) return LINATTN_ERR_ALIAS;
+  return hip_status(la::launch_causal_bwd(q, k, v, dO, dq, dk, dv, (int)BH, N, D, M, dtype == LINATTN_BF16, ws,
+                                          (hipStream_t)stream));
+}
+
 size_t linattn_noncausal_workspace_bytes(int B, int H, int N, int D, int M, int dtype) {
   if (check_shape(B, H, N, D, M, dtype) != LINATTN_OK) return 0;
   return la::noncausal_ws_bytes(B * H, N, D, M, dtype == LINATTN_BF16);

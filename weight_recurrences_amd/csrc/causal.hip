@@ -769,6 +769,28 @@ static hipError_t noncausal_impl(const void* q, const void* k, const void* v, vo
   return hipGetLastError();
 }
 
+// Exclusive prefix state of every block of T = tblk tokens (agg [BH][nblk][D][M],
+// aggz [BH][nblk][D]), from a zero initial state; used by the backward pass.
+template <typename T, int D, int M>
+static hipError_t block_prefix_impl(const void* k, const void* v, int BH, int N, int tblk, int nblk, float* agg,
+                                    float* aggz, hipStream_t stream) {
+  hipLaunchKernelGGL((block_state_kernel<T, D, M>), dim3((unsigned)nblk * (unsigned)BH), dim3(NT), 0, stream,
+                     (const T*)k, (const T*)v, N, tblk, nblk, agg, aggz, nullptr, nullptr, 0);
+  const dim3 sgrid((unsigned)((D * M + D + NT - 1) / NT) * (unsigned)BH);
+  hipLaunchKernelGGL(state_scan_kernel, sgrid, dim3(NT), 0, stream, agg, aggz, nblk, D * M, D, nullptr, nullptr,
+                     nullptr, nullptr, 1);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_prefix(const void* k, const void* v, int BH, int N, int D, int M, int bf16, int tblk,
+                               int nblk, float* agg, float* aggz, hipStream_t stream) {
+  if (bf16) {
+    LA_DISPATCH_DM(block_prefix_impl, bf16_t, k, v, BH, N, tblk, nblk, agg, aggz, stream)
+  } else {
+    LA_DISPATCH_DM(block_prefix_impl, float, k, v, BH, N, tblk, nblk, agg, aggz, stream)
+  }
+}
+
 // bf16 causal calls take the single-pass kernel unless LINATTN_CAUSAL_BF16_PATH=blocked
 // selects the three-kernel path (kept for comparisons).
 static bool bf16_fused() {

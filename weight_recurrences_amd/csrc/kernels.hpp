@@ -36,6 +36,13 @@ hipError_t launch_noncausal(const void* q, const void* k, const void* v, void* o
 size_t noncausal_bf16_ws_bytes(int BH, int N, int D, int M);
 hipError_t launch_noncausal_bf16(const void* q, const void* k, const void* v, void* o, int BH, int N, int D, int M,
                                  void* ws, hipStream_t stream);
+// Exclusive per-block prefix states (S, z) from a zero initial state (backward pass).
+hipError_t launch_block_prefix(const void* k, const void* v, int BH, int N, int D, int M, int bf16, int tblk,
+                               int nblk, float* agg, float* aggz, hipStream_t stream);
+// Backward of causal linear attention.
+size_t causal_bwd_ws_bytes(int BH, int N, int D, int M);
+hipError_t launch_causal_bwd(const void* q, const void* k, const void* v, const void* dO, void* dq, void* dk,
+                             void* dv, int BH, int N, int D, int M, int bf16, void* ws, hipStream_t stream);
 hipError_t launch_decode(const void* q, const void* k, const void* v, void* o, float* S, float* z, int BH, int D,
                          int M, int bf16, hipStream_t stream);
 hipError_t launch_deltanet(const void* q, const void* k, const void* v, const void* beta, void* o, int BH, int N,
