@@ -36,14 +36,28 @@ METRIC = "causal linear-attn B·H·N tokens/s at N=32k, D=64; % of HBM/MFMA roof
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
-def source_hash() -> str:
-    """Hash of the kernel sources: counter figures taken from another source are stale."""
+# Kernel sources each workload's launches are built from (the kernels and the
+# headers they include): a counter summary is current while these are unchanged.
+WORKLOAD_SOURCES = {
+    "causal_long": ["causal_fused.hip", "common.hpp", "lds_tiles.hpp"],
+    "causal_mid": ["causal.hip", "common.hpp"],
+    "causal_bwd_long": ["causal_bwd.hip", "causal.hip", "common.hpp"],
+    "noncausal_long": ["noncausal.hip", "common.hpp", "lds_tiles.hpp"],
+    "decode": ["decode.hip", "common.hpp"],
+    "deltanet": ["deltanet.hip", "deltanet_chunk.hip", "common.hpp"],
+    "deltanet_decode": ["deltanet.hip", "common.hpp"],
+}
+
+
+def source_hash(workload: str = None) -> str:
+    """Hash of the kernel sources behind a workload (all of them without one):
+    counter figures taken from another source are stale."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "weight_recurrences_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp", ".cpp")):
-            h.update(name.encode())
-            h.update(open(os.path.join(csrc, name), "rb").read())
+    names = WORKLOAD_SOURCES.get(workload) or [n for n in os.listdir(csrc) if n.endswith((".hip", ".hpp", ".cpp"))]
+    for name in sorted(names):
+        h.update(name.encode())
+        h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -57,7 +71,7 @@ def traffic_from_profiles(workload: str):
     text = open(path).read()
     m_hash = re.search(r"source_hash:\s*([0-9a-f]+)", text)
     m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_hash or not m_bytes or m_hash.group(1) != source_hash():
+    if not m_hash or not m_bytes or m_hash.group(1) != source_hash(workload):
         return None
     return float(m_bytes.group(1))
 
@@ -356,7 +370,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "wall_s": round(wall, 4),
-        "source_hash": source_hash(),
+        "source_hash": source_hash(args.workload),
     }
     print(json.dumps(line), flush=True)
 
