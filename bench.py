@@ -41,7 +41,7 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 WORKLOAD_SOURCES = {
     "causal_long": ["causal_fused.hip", "common.hpp", "lds_tiles.hpp"],
     "causal_mid": ["causal.hip", "common.hpp"],
-    "causal_bwd_long": ["causal_bwd.hip", "causal.hip", "common.hpp"],
+    "causal_bwd_long": ["causal_bwd.hip", "causal_bwd_bf16.hip", "causal.hip", "common.hpp", "lds_tiles.hpp"],
     "noncausal_long": ["noncausal.hip", "common.hpp", "lds_tiles.hpp"],
     "decode": ["decode.hip", "common.hpp"],
     "deltanet": ["deltanet.hip", "deltanet_chunk.hip", "common.hpp"],

@@ -1,4 +1,6 @@
-// Backward of causal linear attention on gfx950 (fp32 arithmetic).
+// Backward of causal linear attention on gfx950: the float32 path (fp32 MFMA);
+// bf16 inputs take the bf16 MFMA kernels of causal_bwd_bf16.hip after the
+// shared block-prefix step.
 //
 // "Transformers are RNNs" (Katharopoulos et al., 2020), translated page
 // "線性變換器", §3.3 eq.(9)-(12) and §3.3.1: the gradients of the causal form
@@ -446,6 +448,8 @@ static hipError_t impl(const void* q, const void* k, const void* v, const void* 
   float *preS = base + l.preS, *preZ = base + l.preZ, *aw = base + l.a, *bw = base + l.b, *suf = base + l.suf;
   hipError_t e = launch_block_prefix(k, v, BH, N, D, M, sizeof(T) == 2, tblk, nblk, preS, preZ, stream);
   if (e != hipSuccess) return e;
+  if constexpr (sizeof(T) == 2)  // bf16 MFMA kernels; 1/den in the first BH * N floats of the a region
+    return launch_causal_bwd_bf16(q, k, v, dO, dq, dk, dv, BH, N, D, M, tblk, nblk, preS, preZ, aw, bw, suf, stream);
   const dim3 grid((unsigned)nblk * (unsigned)BH), block(NT);
   hipLaunchKernelGGL((bwd_q_kernel<T, D, M>), grid, block, 0, stream, (const T*)q, (const T*)k, (const T*)v,
                      (const T*)dO, (T*)dq, N, tblk, nblk, preS, preZ, aw, bw);
@@ -458,6 +462,12 @@ static hipError_t impl(const void* q, const void* k, const void* v, const void* 
 }
 
 }  // namespace bwd
+
+hipError_t launch_suffix_scan(float* suf, int BH, int nblk, int SZ, hipStream_t stream) {
+  const int parts = (SZ + bwd::NT - 1) / bwd::NT;
+  hipLaunchKernelGGL(bwd::suffix_scan_kernel, dim3((unsigned)(parts * BH)), dim3(bwd::NT), 0, stream, suf, nblk, SZ);
+  return hipGetLastError();
+}
 
 size_t causal_bwd_ws_bytes(int BH, int N, int D, int M) {
   if (BH <= 0 || N <= 0) return 0;

@@ -43,6 +43,13 @@ hipError_t launch_block_prefix(const void* k, const void* v, int BH, int N, int 
 size_t causal_bwd_ws_bytes(int BH, int N, int D, int M);
 hipError_t launch_causal_bwd(const void* q, const void* k, const void* v, const void* dO, void* dq, void* dk,
                              void* dv, int BH, int N, int D, int M, int bf16, void* ws, hipStream_t stream);
+// bf16 backward kernels, given the block prefix states (preS, preZ) and room
+// for 1/den and b per token and the per-block suffix states.
+hipError_t launch_causal_bwd_bf16(const void* q, const void* k, const void* v, const void* dO, void* dq, void* dk,
+                                  void* dv, int BH, int N, int D, int M, int tblk, int nblk, float* preS, float* preZ,
+                                  float* inv, float* b, float* suf, hipStream_t stream);
+// In-place exclusive suffix sums of per-block records of SZ floats (fixed order).
+hipError_t launch_suffix_scan(float* suf, int BH, int nblk, int SZ, hipStream_t stream);
 hipError_t launch_decode(const void* q, const void* k, const void* v, void* o, float* S, float* z, int BH, int D,
                          int M, int bf16, hipStream_t stream);
 hipError_t launch_deltanet(const void* q, const void* k, const void* v, const void* beta, void* o, int BH, int N,
