@@ -6,23 +6,26 @@
 //
 // One workgroup owns a block of T = 256 tokens of one (batch, head) and reads
 // each input byte from HBM exactly once:
-//   phase 1  K and V of the block are loaded, phi(K) is applied, and phi(K)
-//            (bf16) and V stay resident in LDS.  The block's state increment
-//            dS = phi(K_b)^T V_b, dz = colsum phi(K_b) is accumulated in
-//            float32 (phi(K) split into a bf16 head and tail so that the state
-//            keeps float32-level error), with a snapshot of the running local
-//            prefix at every chunk boundary.
+//   phase 1  K, V and the queries of the block are loaded, phi(K) is applied,
+//            and phi(K) (bf16) and V stay resident in LDS.  The block's state
+//            increment dS = phi(K_b)^T V_b, dz = colsum phi(K_b) is accumulated
+//            in float32, with a snapshot of the running local prefix at every
+//            chunk boundary.  When the caller asks for the state, phi(K) enters
+//            as a bf16 head and tail so that the state keeps float32-level error.
+//   phase 3a everything of the outputs that does not depend on earlier blocks,
+//            for chunk c of 64 tokens and query i in it:
+//              num_i = sum_{j in c, j<=i} (phi(q_i).phi(k_j)) v_j + phi(q_i)^T S_c
+//              den_i = sum_{j in c, j<=i}  phi(q_i).phi(k_j)      + phi(q_i)^T z_c
+//            with (S_c, z_c) the local prefix at the chunk start; the partial
+//            sums stay in registers.  The block's increment is published first,
+//            so its stores drain meanwhile.
 //   phase 2  decoupled look-back: the exclusive prefix P_b of the block is
 //            S0 + sum of the increments of all earlier blocks of the head
 //            (eq.(10)-(11) are plain sums, so blocks combine by addition).  The
-//            block publishes its increment, sums the increments of its
-//            predecessors until it meets one that has published its inclusive
-//            prefix, then publishes its own inclusive prefix.
-//   phase 3  outputs chunk by chunk from LDS: for chunk c with state
-//            S = P_b + (local prefix at c):
-//              num_i = phi(q_i)^T S + sum_{j in c, j<=i} (phi(q_i).phi(k_j)) v_j
-//              den_i = phi(q_i)^T z + sum_{j in c, j<=i}  phi(q_i).phi(k_j)
-//            with every product a 16x16x32 bf16 MFMA tile.
+//            block sums the increments of its predecessors until it meets one
+//            that has published its inclusive prefix, then publishes its own.
+//   phase 3b num_i += phi(q_i)^T P_b, den_i += phi(q_i)^T p_b, o_i = num_i / den_i.
+// Every product is a 16x16x32 bf16 MFMA tile with float32 accumulation.
 //
 // Synchronisation between workgroups uses one 64-bit flag per block holding
 // (epoch << 8 | producer XCD << 2 | status); the epoch is new for every launch, so the workspace
@@ -75,9 +78,10 @@ struct alignas(16) Smem {
   bf16_t V[TBLK * M];   // V, row-major, swizzled
   union {
     bf16_t Kl[CH * D];  // phase 1: phi(K) tail of the current chunk
-    bf16_t St[M * D];   // phase 3: S^T operand of the current chunk
+    bf16_t St[M * D];   // phase 3: S^T operand of a state
   } u;
-  float Zs[D];
+  bf16_t Zh[D];         // phase 3: z of that state as a bf16 head
+  bf16_t Zl[D];         //          and tail
   int status;
 };
 
@@ -242,7 +246,65 @@ __device__ void block_increment_direct(Tiles<D, M>& acc, const bf16_t* kh, const
 
 __device__ __forceinline__ unsigned long long rt_clock() { return __builtin_amdgcn_s_memrealtime(); }
 
-template <int D, int M, bool LOCAL>
+// Running local state at a chunk start in the form phase 3 consumes: S as the
+// packed bf16 pairs of this wave's tiles, z in float32.
+template <int D, int M>
+struct Snap {
+  u32x2 S[G<D, M>::TMW];
+  f32x4 Z;
+};
+
+template <int D, int M>
+__device__ __forceinline__ void snap_take(Snap<D, M>& s, const Tiles<D, M>& t) {
+#pragma unroll
+  for (int u = 0; u < G<D, M>::TMW; ++u) s.S[u] = u32x2{cvt_pk(t.S[u][0], t.S[u][1]), cvt_pk(t.S[u][2], t.S[u][3])};
+  s.Z = t.Z;
+}
+
+// A state as the phase-3 operands: S^T in bf16 (each wave writes its tiles) and
+// z as a bf16 head and tail, so that z . phi(q) keeps float32-level accuracy.
+template <int D, int M>
+__device__ __forceinline__ void put_operand(Smem<D, M>& sm, const u32x2 (&S)[G<D, M>::TMW], const f32x4& Z, int w,
+                                            int n, int g) {
+  using GG = G<D, M>;
+#pragma unroll
+  for (int u = 0; u < GG::TMW; ++u) {
+    int tdd, tm;
+    tile_coords<D, M>(w, u, tdd, tm);
+    unit8<GG::UK>(sm.u.St, 16 * tm + n, 16 * tdd + 4 * g) = S[u];
+  }
+  if (w < GG::TD && n == 0) {
+    const uint32_t h0 = cvt_pk(Z[0], Z[1]), h1 = cvt_pk(Z[2], Z[3]);
+    *reinterpret_cast<u32x2*>(&sm.Zh[16 * w + 4 * g]) = u32x2{h0, h1};
+    *reinterpret_cast<u32x2*>(&sm.Zl[16 * w + 4 * g]) =
+        u32x2{cvt_pk(Z[0] - lo_of(h0), Z[1] - hi_of(h0)), cvt_pk(Z[2] - lo_of(h1), Z[3] - hi_of(h1))};
+  }
+}
+
+// num^T += S^T phi(Q)^T and den += z^T phi(Q)^T for one wave's 16 query columns,
+// with (S, z) the operands in LDS.
+template <int D, int M>
+__device__ __forceinline__ void state_read(const Smem<D, M>& sm, const bf16x8 (&qf)[D / 32], f32x4 (&numT)[M / 16],
+                                           f32x4& den, int n, int g) {
+  using GG = G<D, M>;
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s) {
+#pragma unroll
+    for (int tm = 0; tm < GG::TM; ++tm) {
+      const bf16x8 as = as_bf16x8(unit16<GG::UK>((const bf16_t*)sm.u.St, 16 * tm + n, 32 * s + 8 * g));
+      numT[tm] = mma(as, qf[s], numT[tm]);
+    }
+    den = mma(as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.Zh[32 * s + 8 * g])), qf[s], den);
+    den = mma(as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.Zl[32 * s + 8 * g])), qf[s], den);
+  }
+}
+
+// EXACT: phi(K) enters the state increments as a bf16 head and tail, so that the
+// published prefixes and the final state carry float32-level error (used when the
+// caller asks for the state).  Otherwise the increments use the bf16 head only:
+// the prefixes then feed only the bf16 S^T operand of the outputs, whose own
+// rounding is of the same order.
+template <int D, int M, bool LOCAL, bool EXACT>
 __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, bf16_t* __restrict__ o,
     int N, int nblk, int BH, const float* S0, const float* z0, float* S_out, float* z_out,
@@ -261,12 +323,14 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
   const bf16_t* qh = q + (size_t)bh * N * D;
   const int xcc = LOCAL ? xcc_id() : 0;
 
-  // ---------------- phase 1: load K, V of the whole block ----------------
+  // ---------------- loads: K, V of the whole block, then its queries ----------------
   // Inputs are streamed with non-temporal loads, which leave the L2 to the
-  // published states and the outputs (measured: 4-5% faster than plain loads;
-  // non-temporal output stores measured slightly slower).
+  // published states and the outputs.  Keys past the end of the sequence read
+  // as bf16 -inf, whose phi is exactly 0, so they add nothing to the state or
+  // to a score; values past the end read as 0.
   constexpr int KV = CH * D * 2 / 16 / NT;  // 16-byte vectors per thread per chunk
   constexpr int VV = CH * M * 2 / 16 / NT;
+  constexpr uint32_t NEG_INF2 = 0xFF80FF80u;
   u32x4 rk[NCH][KV], rv[NCH][VV];
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
@@ -274,7 +338,8 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
     for (int i = 0; i < KV; ++i) {
       const int p = tid + NT * i, row = p / GG::UK, cu = p % GG::UK;
       const int t = c * CH + row;
-      rk[c][i] = t < ntok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kh + (size_t)(t0 + t) * D + cu * 8)) : u32x4{0u, 0u, 0u, 0u};
+      rk[c][i] = t < ntok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kh + (size_t)(t0 + t) * D + cu * 8))
+                          : u32x4{NEG_INF2, NEG_INF2, NEG_INF2, NEG_INF2};
     }
 #pragma unroll
     for (int i = 0; i < VV; ++i) {
@@ -283,74 +348,8 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
       rv[c][i] = t < ntok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vh + (size_t)(t0 + t) * M + cu * 8)) : u32x4{0u, 0u, 0u, 0u};
     }
   }
-
-  Tiles<D, M> L;  // running local state of the block (float32)
-  tiles_zero<D, M>(L);
-  Tiles<D, M> snap[NCH];  // exclusive local prefix at every chunk start
-  const bf16x8 ones = ones8();
-  const int td = w % GG::TD;
-
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    snap[c] = L;
-    if (c < nch) {
-      // phi(K): head into the resident tile, tail into the staging tile.
-#pragma unroll
-      for (int i = 0; i < KV; ++i) {
-        const int p = tid + NT * i, row = p / GG::UK, cu = p % GG::UK;
-        const int t = c * CH + row;
-        const bool ok = t < ntok;
-        u32x4 hv, lv;
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const uint32_t wd = rk[c][i][h];
-          const float a = ok ? phi(lo_of(wd)) : 0.f, bb = ok ? phi(hi_of(wd)) : 0.f;
-          const uint32_t hp = cvt_pk(a, bb);
-          hv[h] = hp;
-          lv[h] = cvt_pk(a - lo_of(hp), bb - hi_of(hp));
-        }
-        unit16<GG::UK>(sm.K, t, cu * 8) = hv;
-        unit16<GG::UK>(sm.u.Kl, row, cu * 8) = lv;
-      }
-#pragma unroll
-      for (int i = 0; i < VV; ++i) {
-        const int p = tid + NT * i, row = p / GG::UV, cu = p % GG::UV;
-        unit16<GG::UV>(sm.V, c * CH + row, cu * 8) = rv[c][i];
-      }
-      __syncthreads();
-      // L += phi(K_c)^T V_c (head and tail), z += colsum phi(K_c).
-#pragma unroll
-      for (int s = 0; s < CH / 32; ++s) {
-        const bf16x8 ah = jfrag<GG::UK>(sm.K, c * CH + 32 * s, 16 * td, g, n);
-        const bf16x8 al = jfrag<GG::UK>(sm.u.Kl, 32 * s, 16 * td, g, n);
-#pragma unroll
-        for (int u = 0; u < GG::TMW; ++u) {
-          int tdd, tm;
-          tile_coords<D, M>(w, u, tdd, tm);
-          const bf16x8 bv = jfrag<GG::UV>(sm.V, c * CH + 32 * s, 16 * tm, g, n);
-          L.S[u] = mma(ah, bv, L.S[u]);
-          L.S[u] = mma(al, bv, L.S[u]);
-        }
-        if (w < GG::TD) {
-          L.Z = mma(ah, ones, L.Z);
-          L.Z = mma(al, ones, L.Z);
-        }
-      }
-      __syncthreads();  // the staging tile is rewritten by the next chunk
-    }
-  }
-
-  // ---------------- phase 2: exclusive prefix of the block ----------------
-  // P_b is the left fold S0 + a_0 + a_1 + ... + a_{b-1} of the block
-  // increments a_j, evaluated in that order whatever the timing: the block
-  // starts from the nearest published inclusive prefix (itself such a fold)
-  // and adds the later increments in forward order.  Results are therefore
-  // bitwise repeatable; only the never-expected fallback (a predecessor that
-  // publishes nothing within the spin bound) computes increments differently.
-  // Prefetch phase 3's queries (raw bits; phi is applied per chunk).  They are
-  // issued before the look-back on purpose: a workgroup's vector memory
-  // operations complete in issue order, so the flag polls and state loads of the
-  // look-back must not queue behind them.
+  // Queries of this wave's rows 16 w + n of every chunk (raw bits; phi is
+  // applied in phase 3).
   constexpr int QV = D / 32;
   u32x4 rq[NCH][QV];
 #pragma unroll
@@ -362,11 +361,145 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
                                  : u32x4{0u, 0u, 0u, 0u};
   }
 
+  // ---------------- phase 1: block increment and local prefixes ----------------
+  Tiles<D, M> L;  // running local state of the block (float32)
+  tiles_zero<D, M>(L);
+  Snap<D, M> snap[NCH];  // local prefix at the start of chunks 1.. (chunk 0 starts from 0)
+  const bf16x8 ones = ones8();
+  const int td = w % GG::TD;
+
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    if (c >= nch) break;
+    if (c > 0) snap_take<D, M>(snap[c], L);
+    // phi(K): head into the resident tile, tail (EXACT) into the staging tile.
+#pragma unroll
+    for (int i = 0; i < KV; ++i) {
+      const int p = tid + NT * i, row = p / GG::UK, cu = p % GG::UK;
+      u32x4 hv, lv;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const uint32_t wd = rk[c][i][h];
+        const float a = phi(lo_of(wd)), bb = phi(hi_of(wd));
+        const uint32_t hp = cvt_pk(a, bb);
+        hv[h] = hp;
+        if (EXACT) lv[h] = cvt_pk(a - lo_of(hp), bb - hi_of(hp));
+      }
+      unit16<GG::UK>(sm.K, c * CH + row, cu * 8) = hv;
+      if (EXACT) unit16<GG::UK>(sm.u.Kl, row, cu * 8) = lv;
+    }
+#pragma unroll
+    for (int i = 0; i < VV; ++i) {
+      const int p = tid + NT * i, row = p / GG::UV, cu = p % GG::UV;
+      unit16<GG::UV>(sm.V, c * CH + row, cu * 8) = rv[c][i];
+    }
+    __syncthreads();
+    // L += phi(K_c)^T V_c, z += colsum phi(K_c).
+#pragma unroll
+    for (int s = 0; s < CH / 32; ++s) {
+      const bf16x8 ah = jfrag<GG::UK>(sm.K, c * CH + 32 * s, 16 * td, g, n);
+      bf16x8 al;
+      if (EXACT) al = jfrag<GG::UK>(sm.u.Kl, 32 * s, 16 * td, g, n);
+#pragma unroll
+      for (int u = 0; u < GG::TMW; ++u) {
+        int tdd, tm;
+        tile_coords<D, M>(w, u, tdd, tm);
+        const bf16x8 bv = jfrag<GG::UV>(sm.V, c * CH + 32 * s, 16 * tm, g, n);
+        L.S[u] = mma(ah, bv, L.S[u]);
+        if (EXACT) L.S[u] = mma(al, bv, L.S[u]);
+      }
+      if (w < GG::TD) {
+        L.Z = mma(ah, ones, L.Z);
+        if (EXACT) L.Z = mma(al, ones, L.Z);
+      }
+    }
+    if (EXACT) __syncthreads();  // the staging tile is rewritten by the next chunk
+  }
+
+  // The block increment is published now; its stores drain while phase 3a runs.
+  const size_t slot = (size_t)bh * nblk + b;
+  if (b > 0) slot_store<D, M, LOCAL>(agg_ws + slot * GG::SLOT, L, w, lane, n, g);
+
+  // ---------------- phase 3a: outputs relative to the block start ----------------
+  // For query i of chunk c: num_i = phi(q_i)^T (P + S_c) + sum_{j in c, j<=i} A_ij v_j,
+  // den_i likewise.  Everything except the prefix P of earlier blocks is formed
+  // here, before the look-back, and kept in registers.
+  f32x4 numT[NCH][GG::TM];  // transposed accumulators: row m (16 tm + 4g + r), column i (16 w + n)
+  float dsum[NCH];
+  bf16x8 qf[NCH][QV];
+  if (o) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      if (c >= nch) break;
+      if (c > 0) {
+        __syncthreads();  // the previous readers of the operand tiles are done
+        put_operand<D, M>(sm, snap[c].S, snap[c].Z, w, n, g);
+        __syncthreads();
+      }
+#pragma unroll
+      for (int s = 0; s < QV; ++s) {
+        u32x4 pk;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const uint32_t wd = rq[c][s][h];
+          pk[h] = cvt_pk(phi(lo_of(wd)), phi(hi_of(wd)));
+        }
+        qf[c][s] = as_bf16x8(pk);
+      }
+#pragma unroll
+      for (int tm = 0; tm < GG::TM; ++tm) numT[c][tm] = f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 den{0.f, 0.f, 0.f, 0.f};
+
+      // Scores A^T[j][i] = phi(k_j).phi(q_i), j-tiles t <= w, masked on the diagonal.
+      f32x4 at[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        at[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (t <= w) {
+#pragma unroll
+          for (int s = 0; s < QV; ++s) {
+            const bf16x8 a = as_bf16x8(unit16<GG::UK>((const bf16_t*)sm.K, c * CH + 16 * t + n, 32 * s + 8 * g));
+            at[t] = mma(a, qf[c][s], at[t]);
+          }
+          if (t == w) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (4 * g + r > n) at[t][r] = 0.f;
+          }
+        }
+      }
+      // Intra-chunk: num^T += V^T A^T, den += 1^T A^T (the score tiles are already
+      // the B operand: lane (n, g) holds column i = n at the j-slots of group g).
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        if (2 * s <= w) {
+          const bf16x8 pf = as_bf16x8(u32x4{cvt_pk(at[2 * s][0], at[2 * s][1]), cvt_pk(at[2 * s][2], at[2 * s][3]),
+                                            cvt_pk(at[2 * s + 1][0], at[2 * s + 1][1]),
+                                            cvt_pk(at[2 * s + 1][2], at[2 * s + 1][3])});
+#pragma unroll
+          for (int tm = 0; tm < GG::TM; ++tm) {
+            const bf16x8 av = jfrag<GG::UV>(sm.V, c * CH + 32 * s, 16 * tm, g, n);
+            numT[c][tm] = mma(av, pf, numT[c][tm]);
+          }
+          den = mma(ones, pf, den);
+        }
+      }
+      // Local prefix of the block at the chunk start.
+      if (c > 0) state_read<D, M>(sm, qf[c], numT[c], den, n, g);
+      dsum[c] = den[0];
+    }
+  }
+
+  // ---------------- phase 2: exclusive prefix of the block ----------------
+  // P_b is the left fold S0 + a_0 + a_1 + ... + a_{b-1} of the block
+  // increments a_j, evaluated in that order whatever the timing: the block
+  // starts from the nearest published inclusive prefix (itself such a fold)
+  // and adds the later increments in forward order.  Results are therefore
+  // bitwise repeatable; only the never-expected fallback (a predecessor that
+  // publishes nothing within the spin bound) computes increments differently.
   Tiles<D, M> P;
   tiles_zero<D, M>(P);
-  const size_t slot = (size_t)bh * nblk + b;
   if (b > 0) {
-    slot_store<D, M, LOCAL>(agg_ws + slot * GG::SLOT, L, w, lane, n, g);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's stores are complete
     __syncthreads();
     if (tid == 0)
@@ -404,16 +537,12 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
     if (pstar >= 0) {
       slot_load<D, M, LOCAL>(P, incl_ws + ((size_t)bh * nblk + pstar) * GG::SLOT, w, lane, g);
       int j = pstar + 1;
-      for (; j + 4 <= b; j += 4) {  // four loads in flight, added in order
-        Tiles<D, M> a0, a1, a2, a3;
+      for (; j + 2 <= b; j += 2) {  // two loads in flight, added in order
+        Tiles<D, M> a0, a1;
         slot_load<D, M, LOCAL>(a0, agg_ws + ((size_t)bh * nblk + j) * GG::SLOT, w, lane, g);
         slot_load<D, M, LOCAL>(a1, agg_ws + ((size_t)bh * nblk + j + 1) * GG::SLOT, w, lane, g);
-        slot_load<D, M, LOCAL>(a2, agg_ws + ((size_t)bh * nblk + j + 2) * GG::SLOT, w, lane, g);
-        slot_load<D, M, LOCAL>(a3, agg_ws + ((size_t)bh * nblk + j + 3) * GG::SLOT, w, lane, g);
         tiles_acc<D, M>(P, a0);
         tiles_acc<D, M>(P, a1);
-        tiles_acc<D, M>(P, a2);
-        tiles_acc<D, M>(P, a3);
       }
       for (; j < b; ++j) {
         Tiles<D, M> a0;
@@ -479,113 +608,38 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
   }
   if (!o) return;
 
-  // ---------------- phase 3: outputs ----------------
+  // ---------------- phase 3b: add the prefix of earlier blocks, store ----------------
+  const bool have_p = b > 0 || S0 != nullptr;
+  if (have_p) {
+    __syncthreads();  // phase 3a's readers of the operand tiles are done
+    u32x2 ps[GG::TMW];
+#pragma unroll
+    for (int u = 0; u < GG::TMW; ++u) ps[u] = u32x2{cvt_pk(P.S[u][0], P.S[u][1]), cvt_pk(P.S[u][2], P.S[u][3])};
+    put_operand<D, M>(sm, ps, P.Z, w, n, g);
+    __syncthreads();
+  }
   bf16_t* oh = o + (size_t)bh * N * M;
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     if (c >= nch) break;
-    __syncthreads();  // previous readers of St / Zs are done
-    // state at the chunk start: P + local prefix, published as the S^T operand
-#pragma unroll
-    for (int u = 0; u < GG::TMW; ++u) {
-      int tdd, tm;
-      tile_coords<D, M>(w, u, tdd, tm);
-      const f32x4 x = P.S[u] + snap[c].S[u];
-      unit8<GG::UK>(sm.u.St, 16 * tm + n, 16 * tdd + 4 * g) = u32x2{cvt_pk(x[0], x[1]), cvt_pk(x[2], x[3])};
-    }
-    if (w < GG::TD && n == 0) *reinterpret_cast<f32x4*>(&sm.Zs[16 * w + 4 * g]) = P.Z + snap[c].Z;
-    __syncthreads();
-
-    // phi(Q) fragments of this wave's 16 rows.
-    bf16x8 qf[QV];
-#pragma unroll
-    for (int s = 0; s < QV; ++s) {
-      u32x4 pk;
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const uint32_t wd = rq[c][s][h];
-        pk[h] = cvt_pk(phi(lo_of(wd)), phi(hi_of(wd)));
-      }
-      qf[s] = as_bf16x8(pk);
-    }
-
-    // Transposed accumulators: numT[tm] row m (16 tm + 4g + r), column i (16 w + n);
-    // every row of den holds the denominator of query column i.
-    f32x4 numT[GG::TM];
-#pragma unroll
-    for (int tm = 0; tm < GG::TM; ++tm) numT[tm] = f32x4{0.f, 0.f, 0.f, 0.f};
-    f32x4 den{0.f, 0.f, 0.f, 0.f};
-
-    // Scores A^T[j][i] = phi(k_j).phi(q_i), j-tiles t <= w, masked on the diagonal.
-    f32x4 at[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      at[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (t <= w) {
-#pragma unroll
-        for (int s = 0; s < QV; ++s) {
-          const bf16x8 a = as_bf16x8(unit16<GG::UK>((const bf16_t*)sm.K, c * CH + 16 * t + n, 32 * s + 8 * g));
-          at[t] = mma(a, qf[s], at[t]);
-        }
-        if (t == w) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (4 * g + r > n) at[t][r] = 0.f;
-        }
-      }
-    }
-    // Intra-chunk: num^T += V^T P^T, den += 1^T P^T (the score tiles are already
-    // the B operand: lane (n, g) holds column i = n at the j-slots of group g).
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      if (2 * s <= w) {
-        const bf16x8 pf = as_bf16x8(u32x4{cvt_pk(at[2 * s][0], at[2 * s][1]), cvt_pk(at[2 * s][2], at[2 * s][3]),
-                                          cvt_pk(at[2 * s + 1][0], at[2 * s + 1][1]),
-                                          cvt_pk(at[2 * s + 1][2], at[2 * s + 1][3])});
-#pragma unroll
-        for (int tm = 0; tm < GG::TM; ++tm) {
-          const bf16x8 av = jfrag<GG::UV>(sm.V, c * CH + 32 * s, 16 * tm, g, n);
-          numT[tm] = mma(av, pf, numT[tm]);
-        }
-        den = mma(ones, pf, den);
-      }
-    }
-    // Inter-chunk: num^T += S^T phi(Q)^T, den += z^T phi(Q)^T (z as a bf16 head + tail).
-#pragma unroll
-    for (int s = 0; s < QV; ++s) {
-#pragma unroll
-      for (int tm = 0; tm < GG::TM; ++tm) {
-        const bf16x8 as = as_bf16x8(unit16<GG::UK>((const bf16_t*)sm.u.St, 16 * tm + n, 32 * s + 8 * g));
-        numT[tm] = mma(as, qf[s], numT[tm]);
-      }
-      const f32x4 za = *reinterpret_cast<const f32x4*>(&sm.Zs[32 * s + 8 * g]);
-      const f32x4 zb = *reinterpret_cast<const f32x4*>(&sm.Zs[32 * s + 8 * g + 4]);
-      uint32_t zh[4], zl[4];
-      zh[0] = cvt_pk(za[0], za[1]);
-      zh[1] = cvt_pk(za[2], za[3]);
-      zh[2] = cvt_pk(zb[0], zb[1]);
-      zh[3] = cvt_pk(zb[2], zb[3]);
-      zl[0] = cvt_pk(za[0] - lo_of(zh[0]), za[1] - hi_of(zh[0]));
-      zl[1] = cvt_pk(za[2] - lo_of(zh[1]), za[3] - hi_of(zh[1]));
-      zl[2] = cvt_pk(zb[0] - lo_of(zh[2]), zb[1] - hi_of(zh[2]));
-      zl[3] = cvt_pk(zb[2] - lo_of(zh[3]), zb[3] - hi_of(zh[3]));
-      den = mma(as_bf16x8(u32x4{zh[0], zh[1], zh[2], zh[3]}), qf[s], den);
-      den = mma(as_bf16x8(u32x4{zl[0], zl[1], zl[2], zl[3]}), qf[s], den);
+    float den = dsum[c];
+    if (have_p) {
+      f32x4 dd{0.f, 0.f, 0.f, 0.f};
+      state_read<D, M>(sm, qf[c], numT[c], dd, n, g);
+      den += dd[0];
     }
     // o_i = num_i / den_i for query i = 16w + n: lane (n, g) holds the four
     // consecutive columns 16 tm + 4g .. +3 of every m-tile, one 8-byte store each.
-    {
-      const int i = c * CH + 16 * w + n;
-      const float inv = __builtin_amdgcn_rcpf(den[0]);
-      u32x2 pk[GG::TM];
+    const int i = c * CH + 16 * w + n;
+    const float inv = __builtin_amdgcn_rcpf(den);
+    u32x2 pk[GG::TM];
 #pragma unroll
-      for (int tm = 0; tm < GG::TM; ++tm)
-        pk[tm] = u32x2{cvt_pk(numT[tm][0] * inv, numT[tm][1] * inv), cvt_pk(numT[tm][2] * inv, numT[tm][3] * inv)};
-      if (i < ntok) {
-        bf16_t* dst = oh + (size_t)(t0 + i) * M + 4 * g;
+    for (int tm = 0; tm < GG::TM; ++tm)
+      pk[tm] = u32x2{cvt_pk(numT[c][tm][0] * inv, numT[c][tm][1] * inv), cvt_pk(numT[c][tm][2] * inv, numT[c][tm][3] * inv)};
+    if (i < ntok) {
+      bf16_t* dst = oh + (size_t)(t0 + i) * M + 4 * g;
 #pragma unroll
-        for (int tm = 0; tm < GG::TM; ++tm) *reinterpret_cast<u32x2*>(dst + 16 * tm) = pk[tm];
-      }
+      for (int tm = 0; tm < GG::TM; ++tm) *reinterpret_cast<u32x2*>(dst + 16 * tm) = pk[tm];
     }
   }
 }
@@ -657,14 +711,19 @@ static hipError_t fused_impl(const void* q, const void* k, const void* v, void* 
   // 8 every block of a head (workgroup indices b * BH + h) runs on one XCD and
   // states are exchanged through its L2.
   const dim3 grid((unsigned)nblk * (unsigned)BH), block(NT);
-  if (BH % 8 == 0)
-    hipLaunchKernelGGL((causal_fused_kernel<D, M, true>), grid, block, 0, stream, (const bf16_t*)q, (const bf16_t*)k,
-                       (const bf16_t*)v, (bf16_t*)o, N, nblk, BH, S0, z0, S_out, z_out, flags, agg, incl, next_epoch(),
-                       spin_ticks);
-  else
-    hipLaunchKernelGGL((causal_fused_kernel<D, M, false>), grid, block, 0, stream, (const bf16_t*)q, (const bf16_t*)k,
-                       (const bf16_t*)v, (bf16_t*)o, N, nblk, BH, S0, z0, S_out, z_out, flags, agg, incl, next_epoch(),
-                       spin_ticks);
+  const bool exact = S_out != nullptr || o == nullptr;
+#define LA_FUSED_LAUNCH(LOC, EX)                                                                                  \
+  hipLaunchKernelGGL((causal_fused_kernel<D, M, LOC, EX>), grid, block, 0, stream, (const bf16_t*)q, (const bf16_t*)k, \
+                     (const bf16_t*)v, (bf16_t*)o, N, nblk, BH, S0, z0, S_out, z_out, flags, agg, incl, next_epoch(),  \
+                     spin_ticks)
+  if (BH % 8 == 0) {
+    if (exact) LA_FUSED_LAUNCH(true, true);
+    else LA_FUSED_LAUNCH(true, false);
+  } else {
+    if (exact) LA_FUSED_LAUNCH(false, true);
+    else LA_FUSED_LAUNCH(false, false);
+  }
+#undef LA_FUSED_LAUNCH
   return hipGetLastError();
 }
 
