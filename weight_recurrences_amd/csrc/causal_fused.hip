@@ -263,15 +263,16 @@ __device__ __forceinline__ void snap_take(Snap<D, M>& s, const Tiles<D, M>& t) {
 
 // A state as the phase-3 operands: S^T in bf16 (each wave writes its tiles) and
 // z as a bf16 head and tail, so that z . phi(q) keeps float32-level accuracy.
+// l_wr = lane_off<UK>(n, 4 g).
 template <int D, int M>
 __device__ __forceinline__ void put_operand(Smem<D, M>& sm, const u32x2 (&S)[G<D, M>::TMW], const f32x4& Z, int w,
-                                            int n, int g) {
+                                            int n, int g, uint32_t l_wr) {
   using GG = G<D, M>;
 #pragma unroll
   for (int u = 0; u < GG::TMW; ++u) {
     int tdd, tm;
     tile_coords<D, M>(w, u, tdd, tm);
-    unit8<GG::UK>(sm.u.St, 16 * tm + n, 16 * tdd + 4 * g) = S[u];
+    *reinterpret_cast<u32x2*>(tile_at<GG::UK>(sm.u.St, l_wr, 16 * tm, 16 * tdd)) = S[u];
   }
   if (w < GG::TD && n == 0) {
     const uint32_t h0 = cvt_pk(Z[0], Z[1]), h1 = cvt_pk(Z[2], Z[3]);
@@ -282,16 +283,16 @@ __device__ __forceinline__ void put_operand(Smem<D, M>& sm, const u32x2 (&S)[G<D
 }
 
 // num^T += S^T phi(Q)^T and den += z^T phi(Q)^T for one wave's 16 query columns,
-// with (S, z) the operands in LDS.
+// with (S, z) the operands in LDS; l_rd = lane_off<UK>(n, 8 g).
 template <int D, int M>
 __device__ __forceinline__ void state_read(const Smem<D, M>& sm, const bf16x8 (&qf)[D / 32], f32x4 (&numT)[M / 16],
-                                           f32x4& den, int n, int g) {
+                                           f32x4& den, int g, uint32_t l_rd) {
   using GG = G<D, M>;
 #pragma unroll
   for (int s = 0; s < D / 32; ++s) {
 #pragma unroll
     for (int tm = 0; tm < GG::TM; ++tm) {
-      const bf16x8 as = as_bf16x8(unit16<GG::UK>((const bf16_t*)sm.u.St, 16 * tm + n, 32 * s + 8 * g));
+      const bf16x8 as = as_bf16x8(*reinterpret_cast<const u32x4*>(tile_at<GG::UK>((const bf16_t*)sm.u.St, l_rd, 16 * tm, 32 * s)));
       numT[tm] = mma(as, qf[s], numT[tm]);
     }
     den = mma(as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.Zh[32 * s + 8 * g])), qf[s], den);
@@ -322,6 +323,18 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
   const bf16_t* vh = v + (size_t)bh * N * M;
   const bf16_t* qh = q + (size_t)bh * N * D;
   const int xcc = LOCAL ? xcc_id() : 0;
+  // Lane parts of the LDS addresses (tile_at): unit stores of the loaded rows,
+  // transposed fragment reads, unit reads of score and state operands, and the
+  // 8-byte state operand writes.  The transposed reads of phase 1 fold in this
+  // wave's tile columns (d-tile td of phi(K), m-tiles w / TD + WPT u of V).
+  const int td = w % GG::TD;
+  const uint32_t l_kst = lane_off<GG::UK>(tid / GG::UK, 8 * (tid % GG::UK));
+  const uint32_t l_vst = lane_off<GG::UV>(tid / GG::UV, 8 * (tid % GG::UV));
+  const uint32_t l_trv = lane_off<GG::UV>(4 * g + (n >> 2), 4 * (n & 3));
+  const uint32_t l_trk_w = lane_off<GG::UK>(4 * g + (n >> 2), 4 * (n & 3)) ^ xor_off<GG::UK>(0, 16 * td);
+  const uint32_t l_trv_w = l_trv ^ xor_off<GG::UV>(0, 16 * (w / GG::TD));
+  const uint32_t l_rd = lane_off<GG::UK>(n, 8 * g);
+  const uint32_t l_wr = lane_off<GG::UK>(n, 4 * g);
 
   // ---------------- loads: K, V of the whole block, then its queries ----------------
   // Inputs are streamed with non-temporal loads, which leave the L2 to the
@@ -366,7 +379,6 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
   tiles_zero<D, M>(L);
   Snap<D, M> snap[NCH];  // local prefix at the start of chunks 1.. (chunk 0 starts from 0)
   const bf16x8 ones = ones8();
-  const int td = w % GG::TD;
 
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
@@ -375,7 +387,6 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
     // phi(K): head into the resident tile, tail (EXACT) into the staging tile.
 #pragma unroll
     for (int i = 0; i < KV; ++i) {
-      const int p = tid + NT * i, row = p / GG::UK, cu = p % GG::UK;
       u32x4 hv, lv;
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
@@ -385,26 +396,22 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
         hv[h] = hp;
         if (EXACT) lv[h] = cvt_pk(a - lo_of(hp), bb - hi_of(hp));
       }
-      unit16<GG::UK>(sm.K, c * CH + row, cu * 8) = hv;
-      if (EXACT) unit16<GG::UK>(sm.u.Kl, row, cu * 8) = lv;
+      *reinterpret_cast<u32x4*>(tile_at<GG::UK>(sm.K, l_kst, c * CH + i * (NT / GG::UK), 0)) = hv;
+      if (EXACT) *reinterpret_cast<u32x4*>(tile_at<GG::UK>(sm.u.Kl, l_kst, i * (NT / GG::UK), 0)) = lv;
     }
 #pragma unroll
-    for (int i = 0; i < VV; ++i) {
-      const int p = tid + NT * i, row = p / GG::UV, cu = p % GG::UV;
-      unit16<GG::UV>(sm.V, c * CH + row, cu * 8) = rv[c][i];
-    }
+    for (int i = 0; i < VV; ++i)
+      *reinterpret_cast<u32x4*>(tile_at<GG::UV>(sm.V, l_vst, c * CH + i * (NT / GG::UV), 0)) = rv[c][i];
     __syncthreads();
     // L += phi(K_c)^T V_c, z += colsum phi(K_c).
 #pragma unroll
     for (int s = 0; s < CH / 32; ++s) {
-      const bf16x8 ah = jfrag<GG::UK>(sm.K, c * CH + 32 * s, 16 * td, g, n);
+      const bf16x8 ah = jfrag_at<GG::UK>(sm.K, l_trk_w, c * CH + 32 * s, 0);
       bf16x8 al;
-      if (EXACT) al = jfrag<GG::UK>(sm.u.Kl, 32 * s, 16 * td, g, n);
+      if (EXACT) al = jfrag_at<GG::UK>(sm.u.Kl, l_trk_w, 32 * s, 0);
 #pragma unroll
       for (int u = 0; u < GG::TMW; ++u) {
-        int tdd, tm;
-        tile_coords<D, M>(w, u, tdd, tm);
-        const bf16x8 bv = jfrag<GG::UV>(sm.V, c * CH + 32 * s, 16 * tm, g, n);
+        const bf16x8 bv = jfrag_at<GG::UV>(sm.V, l_trv_w, c * CH + 32 * s, 16 * GG::WPT * u);
         L.S[u] = mma(ah, bv, L.S[u]);
         if (EXACT) L.S[u] = mma(al, bv, L.S[u]);
       }
@@ -433,7 +440,7 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
       if (c >= nch) break;
       if (c > 0) {
         __syncthreads();  // the previous readers of the operand tiles are done
-        put_operand<D, M>(sm, snap[c].S, snap[c].Z, w, n, g);
+        put_operand<D, M>(sm, snap[c].S, snap[c].Z, w, n, g, l_wr);
         __syncthreads();
       }
 #pragma unroll
@@ -458,7 +465,7 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
         if (t <= w) {
 #pragma unroll
           for (int s = 0; s < QV; ++s) {
-            const bf16x8 a = as_bf16x8(unit16<GG::UK>((const bf16_t*)sm.K, c * CH + 16 * t + n, 32 * s + 8 * g));
+            const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(tile_at<GG::UK>((const bf16_t*)sm.K, l_rd, c * CH + 16 * t, 32 * s)));
             at[t] = mma(a, qf[c][s], at[t]);
           }
           if (t == w) {
@@ -478,14 +485,14 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
                                             cvt_pk(at[2 * s + 1][2], at[2 * s + 1][3])});
 #pragma unroll
           for (int tm = 0; tm < GG::TM; ++tm) {
-            const bf16x8 av = jfrag<GG::UV>(sm.V, c * CH + 32 * s, 16 * tm, g, n);
+            const bf16x8 av = jfrag_at<GG::UV>(sm.V, l_trv, c * CH + 32 * s, 16 * tm);
             numT[c][tm] = mma(av, pf, numT[c][tm]);
           }
           den = mma(ones, pf, den);
         }
       }
       // Local prefix of the block at the chunk start.
-      if (c > 0) state_read<D, M>(sm, qf[c], numT[c], den, n, g);
+      if (c > 0) state_read<D, M>(sm, qf[c], numT[c], den, g, l_rd);
       dsum[c] = den[0];
     }
   }
@@ -615,7 +622,7 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
     u32x2 ps[GG::TMW];
 #pragma unroll
     for (int u = 0; u < GG::TMW; ++u) ps[u] = u32x2{cvt_pk(P.S[u][0], P.S[u][1]), cvt_pk(P.S[u][2], P.S[u][3])};
-    put_operand<D, M>(sm, ps, P.Z, w, n, g);
+    put_operand<D, M>(sm, ps, P.Z, w, n, g, l_wr);
     __syncthreads();
   }
   bf16_t* oh = o + (size_t)bh * N * M;
@@ -625,7 +632,7 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
     float den = dsum[c];
     if (have_p) {
       f32x4 dd{0.f, 0.f, 0.f, 0.f};
-      state_read<D, M>(sm, qf[c], numT[c], dd, n, g);
+      state_read<D, M>(sm, qf[c], numT[c], dd, g, l_rd);
       den += dd[0];
     }
     // o_i = num_i / den_i for query i = 16w + n: lane (n, g) holds the four

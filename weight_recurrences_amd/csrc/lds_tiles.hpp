@@ -11,6 +11,8 @@
 //    out[i][e] = in[4 e + i / 4][i % 4]).
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace la {
@@ -23,9 +25,41 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 // row-major unit stores, unit reads of a column slab and transposed reads free
 // of bank conflicts.
 template <int U>
-__device__ __forceinline__ int swz(int row, int col) {
+__host__ __device__ __forceinline__ int swz(int row, int col) {
   const int unit = (col >> 3) ^ ((row ^ (row >> 3)) & (U - 1));
   return row * U * 8 + unit * 8 + (col & 7);
+}
+
+// The swizzle splits into a per-lane part and a part fixed at compile time.  For
+// element (R + r, C + c) with R and C multiples of 8, where (R >> 3) and (r >> 3)
+// share no bit below U and neither do (C >> 3) and (c >> 3) (so the sums carry
+// nothing into the unit bits):
+//   2 * swz<U>(R + r, C + c) == (lane_off<U>(r, c) ^ xor_off<U>(R, C)) + 16 U R.
+// The lane part is formed once per kernel; every access is then one XOR (none
+// when the XOR term is 0) and an immediate offset.
+template <int U>
+__host__ __device__ constexpr uint32_t lane_off(int r, int c) {
+  return (uint32_t)(16 * U * r + 2 * (c & 7) + 16 * (((c >> 3) ^ r ^ (r >> 3)) & (U - 1)));
+}
+template <int U>
+__host__ __device__ constexpr uint32_t xor_off(int R, int C) {
+  return (uint32_t)(16 * (((C >> 3) ^ (R >> 3)) & (U - 1)));
+}
+// Address of (R + r, C + c) from the lane part of (r, c).
+template <int U, typename T>
+__device__ __forceinline__ T* tile_at(T* tile, uint32_t lane, int R, int C) {
+  typedef typename std::conditional<std::is_const<T>::value, const char, char>::type byte;
+  return reinterpret_cast<T*>(reinterpret_cast<byte*>(tile) + 16 * U * R + (lane ^ xor_off<U>(R, C)));
+}
+
+// j-slot fragment as jfrag below, from the lane part ltr = lane_off<U>(4 g + n / 4, 4 (n % 4))
+// and a column base col0 (a multiple of 16): rows rbase + 32-row slab (rbase a multiple of 16).
+template <int U>
+__device__ __forceinline__ bf16x8 jfrag_at(const bf16_t* tile, uint32_t ltr, int rbase, int col0) {
+  const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)tile_at<U>(tile, ltr, rbase, col0));
+  const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)tile_at<U>(tile, ltr, rbase + 16, col0));
+  const u32x2 x = __builtin_bit_cast(u32x2, a), y = __builtin_bit_cast(u32x2, b);
+  return as_bf16x8(u32x4{x[0], x[1], y[0], y[1]});
 }
 
 // 16-byte unit (row, col..col+7) of a swizzled tile; col is a multiple of 8.
