@@ -40,9 +40,9 @@
 //    LDS tiles with ds_read_b64_tr_b16 (within a 16-lane group the
 //    instruction returns out[i][e] = in[4e + i/4][i % 4]).
 //  * B-operand column n of tile t is column 16 t + n.
-// LDS rows are 16-byte units XOR-swizzled by (row ^ row >> 3) & 7, which keeps
-// the row-major stores, the score-operand reads and the transposed reads free
-// of bank conflicts.
+// LDS rows are 16-byte units XOR-swizzled by a function of the row (row_swz),
+// which keeps the row-major stores, the score-operand reads and the transposed
+// reads free of bank conflicts.
 #include <atomic>
 #include <chrono>
 
@@ -331,8 +331,8 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
   const uint32_t l_kst = lane_off<GG::UK>(tid / GG::UK, 8 * (tid % GG::UK));
   const uint32_t l_vst = lane_off<GG::UV>(tid / GG::UV, 8 * (tid % GG::UV));
   const uint32_t l_trv = lane_off<GG::UV>(4 * g + (n >> 2), 4 * (n & 3));
-  const uint32_t l_trk_w = lane_off<GG::UK>(4 * g + (n >> 2), 4 * (n & 3)) ^ xor_off<GG::UK>(0, 16 * td);
-  const uint32_t l_trv_w = l_trv ^ xor_off<GG::UV>(0, 16 * (w / GG::TD));
+  const uint32_t l_trk_w = lane_off<GG::UK>(4 * g + (n >> 2), 4 * (n & 3)) ^ xor_off<GG::UK>(16 * td);
+  const uint32_t l_trv_w = l_trv ^ xor_off<GG::UV>(16 * (w / GG::TD));
   const uint32_t l_rd = lane_off<GG::UK>(n, 8 * g);
   const uint32_t l_wr = lane_off<GG::UK>(n, 4 * g);
 

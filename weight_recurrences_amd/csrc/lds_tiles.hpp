@@ -20,36 +20,50 @@ namespace la {
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
+// Row term of the swizzle: with row = 8d + 4a + 2b + c (low bits), the unit
+// index of a 16-byte unit is XORed with
+//   U = 8: (b, a^c, a^d) as bits (2, 1, 0);   U = 4: (a^b, a^d) as bits (1, 0).
+// It depends on the row only modulo 16.  Under either LDS bank width (32 or 64
+// four-byte banks per cycle) it leaves these patterns free of bank conflicts:
+//  * 16-byte unit reads of one unit in 16 consecutive rows (MFMA operands),
+//  * 16-byte unit stores of whole consecutive rows,
+//  * ds_read_b64_tr_b16 over 16 consecutive rows and two adjacent units.
+// (The earlier row ^ row >> 3 term serialised the transposed reads two-way on a
+// 32-bank LDS; measured by the SQ_LDS_BANK_CONFLICT counter.)
+template <int U>
+__host__ __device__ constexpr int row_swz(int row) {
+  static_assert(U == 4 || U == 8, "tiles have 4 or 8 units per row");
+  const int a = (row >> 2) & 1, b = (row >> 1) & 1, c = row & 1, d = (row >> 3) & 1;
+  return U == 8 ? (b << 2) | ((a ^ c) << 1) | (a ^ d) : ((a ^ b) << 1) | (a ^ d);
+}
+
 // Swizzled element offset of (row, col) in a row-major bf16 tile with U 16-byte
-// units per row: unit (col / 8) is XORed with (row ^ row >> 3) mod U, which keeps
-// row-major unit stores, unit reads of a column slab and transposed reads free
-// of bank conflicts.
+// units per row: unit (col / 8) is XORed with row_swz(row).
 template <int U>
 __host__ __device__ __forceinline__ int swz(int row, int col) {
-  const int unit = (col >> 3) ^ ((row ^ (row >> 3)) & (U - 1));
+  const int unit = (col >> 3) ^ row_swz<U>(row);
   return row * U * 8 + unit * 8 + (col & 7);
 }
 
 // The swizzle splits into a per-lane part and a part fixed at compile time.  For
-// element (R + r, C + c) with R and C multiples of 8, where (R >> 3) and (r >> 3)
-// share no bit below U and neither do (C >> 3) and (c >> 3) (so the sums carry
-// nothing into the unit bits):
-//   2 * swz<U>(R + r, C + c) == (lane_off<U>(r, c) ^ xor_off<U>(R, C)) + 16 U R.
+// element (R + r, C + c) with R a multiple of 16, C a multiple of 8, and (C >> 3)
+// and (c >> 3) sharing no bit (so their sum carries nothing):
+//   2 * swz<U>(R + r, C + c) == (lane_off<U>(r, c) ^ xor_off<U>(C)) + 16 U R.
 // The lane part is formed once per kernel; every access is then one XOR (none
 // when the XOR term is 0) and an immediate offset.
 template <int U>
 __host__ __device__ constexpr uint32_t lane_off(int r, int c) {
-  return (uint32_t)(16 * U * r + 2 * (c & 7) + 16 * (((c >> 3) ^ r ^ (r >> 3)) & (U - 1)));
+  return (uint32_t)(16 * U * r + 2 * (c & 7) + 16 * (((c >> 3) ^ row_swz<U>(r)) & (U - 1)));
 }
 template <int U>
-__host__ __device__ constexpr uint32_t xor_off(int R, int C) {
-  return (uint32_t)(16 * (((C >> 3) ^ (R >> 3)) & (U - 1)));
+__host__ __device__ constexpr uint32_t xor_off(int C) {
+  return (uint32_t)(16 * ((C >> 3) & (U - 1)));
 }
 // Address of (R + r, C + c) from the lane part of (r, c).
 template <int U, typename T>
 __device__ __forceinline__ T* tile_at(T* tile, uint32_t lane, int R, int C) {
   typedef typename std::conditional<std::is_const<T>::value, const char, char>::type byte;
-  return reinterpret_cast<T*>(reinterpret_cast<byte*>(tile) + 16 * U * R + (lane ^ xor_off<U>(R, C)));
+  return reinterpret_cast<T*>(reinterpret_cast<byte*>(tile) + 16 * U * R + (lane ^ xor_off<U>(C)));
 }
 
 // j-slot fragment as jfrag below, from the lane part ltr = lane_off<U>(4 g + n / 4, 4 (n % 4))
