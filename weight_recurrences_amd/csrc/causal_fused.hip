@@ -191,6 +191,67 @@ __device__ __forceinline__ void tiles_acc(Tiles<D, M>& a, const Tiles<D, M>& b) 
   a.Z += b.Z;
 }
 
+// Block increments.  EXACT: float32, as slot_store / slot_load.  Otherwise
+// S is published as bf16 (8 bytes per lane and tile, half the float32 image) and
+// z as float32: the increments then only feed the bf16 S^T operand of the
+// outputs.  A block adds its own increment to an inclusive prefix in the same
+// rounded form (round_increment), so every fold of the same increments gives
+// the same bits.
+template <int D, int M, bool EXACT>
+__device__ __forceinline__ void round_increment(Tiles<D, M>& t) {
+  if (EXACT) return;
+#pragma unroll
+  for (int u = 0; u < G<D, M>::TMW; ++u) {
+    const uint32_t a = cvt_pk(t.S[u][0], t.S[u][1]), b = cvt_pk(t.S[u][2], t.S[u][3]);
+    t.S[u] = f32x4{lo_of(a), hi_of(a), lo_of(b), hi_of(b)};
+  }
+}
+
+template <int D, int M, bool LOCAL, bool EXACT>
+__device__ __forceinline__ void agg_store(char* slot, const Tiles<D, M>& t, int w, int lane, int n, int g) {
+  using GG = G<D, M>;
+  if (EXACT) {
+    slot_store<D, M, LOCAL>(slot, t, w, lane, n, g);
+    return;
+  }
+  unsigned long long* s = reinterpret_cast<unsigned long long*>(slot);
+#pragma unroll
+  for (int u = 0; u < GG::TMW; ++u) {
+    const unsigned long long x = (unsigned long long)cvt_pk(t.S[u][0], t.S[u][1]) |
+                                 ((unsigned long long)cvt_pk(t.S[u][2], t.S[u][3]) << 32);
+    __hip_atomic_store(&s[(w * GG::TMW + u) * 64 + lane], x, __ATOMIC_RELAXED, Scope<LOCAL>::value);
+  }
+  if (w < GG::TD && n == 0) {
+    unsigned* z = reinterpret_cast<unsigned*>(slot) + GG::SIMG;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      __hip_atomic_store(&z[16 * w + 4 * g + r], __float_as_uint(t.Z[r]), __ATOMIC_RELAXED, Scope<LOCAL>::value);
+  }
+}
+
+template <int D, int M, bool LOCAL, bool EXACT>
+__device__ __forceinline__ void agg_load(Tiles<D, M>& t, const char* slot, int w, int lane, int g) {
+  using GG = G<D, M>;
+  if (EXACT) {
+    slot_load<D, M, LOCAL>(t, slot, w, lane, g);
+    return;
+  }
+  unsigned long long* s = reinterpret_cast<unsigned long long*>(const_cast<char*>(slot));
+#pragma unroll
+  for (int u = 0; u < GG::TMW; ++u) {
+    const unsigned long long x = __hip_atomic_load(&s[(w * GG::TMW + u) * 64 + lane], __ATOMIC_RELAXED, Scope<LOCAL>::value);
+    const uint32_t a = (uint32_t)x, b = (uint32_t)(x >> 32);
+    t.S[u] = f32x4{lo_of(a), hi_of(a), lo_of(b), hi_of(b)};
+  }
+  t.Z = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (w < GG::TD) {
+    unsigned* z = reinterpret_cast<unsigned*>(const_cast<char*>(slot)) + GG::SIMG;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      t.Z[r] = __uint_as_float(__hip_atomic_load(&z[16 * w + 4 * g + r], __ATOMIC_RELAXED, Scope<LOCAL>::value));
+  }
+}
+
 // Adds this wave's elements of a caller state (S [D][M], z [D]).
 template <int D, int M>
 __device__ __forceinline__ void tiles_add_from_state(Tiles<D, M>& t, const float* S, const float* z, int w, int n,
@@ -425,7 +486,7 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
 
   // The block increment is published now; its stores drain while phase 3a runs.
   const size_t slot = (size_t)bh * nblk + b;
-  if (b > 0) slot_store<D, M, LOCAL>(agg_ws + slot * GG::SLOT, L, w, lane, n, g);
+  if (b > 0) agg_store<D, M, LOCAL, EXACT>(agg_ws + slot * GG::SLOT, L, w, lane, n, g);
 
   // ---------------- phase 3a: outputs relative to the block start ----------------
   // For query i of chunk c: num_i = phi(q_i)^T (P + S_c) + sum_{j in c, j<=i} A_ij v_j,
@@ -546,14 +607,14 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
       int j = pstar + 1;
       for (; j + 2 <= b; j += 2) {  // two loads in flight, added in order
         Tiles<D, M> a0, a1;
-        slot_load<D, M, LOCAL>(a0, agg_ws + ((size_t)bh * nblk + j) * GG::SLOT, w, lane, g);
-        slot_load<D, M, LOCAL>(a1, agg_ws + ((size_t)bh * nblk + j + 1) * GG::SLOT, w, lane, g);
+        agg_load<D, M, LOCAL, EXACT>(a0, agg_ws + ((size_t)bh * nblk + j) * GG::SLOT, w, lane, g);
+        agg_load<D, M, LOCAL, EXACT>(a1, agg_ws + ((size_t)bh * nblk + j + 1) * GG::SLOT, w, lane, g);
         tiles_acc<D, M>(P, a0);
         tiles_acc<D, M>(P, a1);
       }
       for (; j < b; ++j) {
         Tiles<D, M> a0;
-        slot_load<D, M, LOCAL>(a0, agg_ws + ((size_t)bh * nblk + j) * GG::SLOT, w, lane, g);
+        agg_load<D, M, LOCAL, EXACT>(a0, agg_ws + ((size_t)bh * nblk + j) * GG::SLOT, w, lane, g);
         tiles_acc<D, M>(P, a0);
       }
     } else {
@@ -585,10 +646,11 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
           slot_load<D, M, LOCAL>(a0, incl_ws + ps * GG::SLOT, w, lane, g);
           done = true;
         } else if (st == 1) {
-          slot_load<D, M, LOCAL>(a0, agg_ws + ps * GG::SLOT, w, lane, g);
+          agg_load<D, M, LOCAL, EXACT>(a0, agg_ws + ps * GG::SLOT, w, lane, g);
         } else {
           tiles_zero<D, M>(a0);
           block_increment_direct<D, M>(a0, kh, vh, p * TBLK, min(N, (p + 1) * TBLK), w, n, g);
+          round_increment<D, M, EXACT>(a0);
         }
         tiles_acc<D, M>(P, a0);
       }
@@ -599,10 +661,11 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
   }
 
   {
-    Tiles<D, M> inc;
+    Tiles<D, M> inc = L;
+    round_increment<D, M, EXACT>(inc);  // the increment as the successors fold it
 #pragma unroll
-    for (int u = 0; u < GG::TMW; ++u) inc.S[u] = P.S[u] + L.S[u];
-    inc.Z = P.Z + L.Z;
+    for (int u = 0; u < GG::TMW; ++u) inc.S[u] = P.S[u] + inc.S[u];
+    inc.Z = P.Z + inc.Z;
     if (b == nblk - 1) {
       if (S_out) tiles_store<D, M>(inc, S_out + (size_t)bh * D * M, z_out + (size_t)bh * D, w, n, g);
     } else {
