@@ -41,7 +41,7 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 WORKLOAD_SOURCES = {
     "causal_long": ["causal_fused.hip", "common.hpp", "lds_tiles.hpp"],
     "causal_mid": ["causal.hip", "common.hpp"],
-    "causal_bwd_long": ["causal_bwd.hip", "causal_bwd_bf16.hip", "causal.hip", "common.hpp", "lds_tiles.hpp"],
+    "causal_bwd_long": ["causal_bwd.hip", "causal_bwd_bf16.hip", "causal.hip", "noncausal.hip", "common.hpp", "lds_tiles.hpp"],
     "noncausal_long": ["noncausal.hip", "common.hpp", "lds_tiles.hpp"],
     "decode": ["decode.hip", "common.hpp"],
     "deltanet": ["deltanet.hip", "deltanet_chunk.hip", "common.hpp"],
@@ -252,7 +252,7 @@ def main():
         ws = torch.empty(max(1, la.causal_bwd_workspace_bytes(w.B, w.H, w.N, w.D, w.M, w.dtype)), dtype=torch.uint8,
                          device=dev)
         step = lambda: la.causal_bwd(q, k, v, dO, out=grads, workspace=ws)
-        kernel = ("linattn_causal_bwd (block_state + state_scan + bwd_q + bwd_rstate + suffix_scan + bwd_kv "
+        kernel = ("linattn_causal_bwd (nc_state (block increments) + state_scan + bwd_q + bwd_rstate + suffix_scan + bwd_kv "
                   "kernels)")
         units = w.B * w.H * w.N
         es = 2

@@ -774,8 +774,13 @@ static hipError_t noncausal_impl(const void* q, const void* k, const void* v, vo
 template <typename T, int D, int M>
 static hipError_t block_prefix_impl(const void* k, const void* v, int BH, int N, int tblk, int nblk, float* agg,
                                     float* aggz, hipStream_t stream) {
-  hipLaunchKernelGGL((block_state_kernel<T, D, M>), dim3((unsigned)nblk * (unsigned)BH), dim3(NT), 0, stream,
-                     (const T*)k, (const T*)v, N, tblk, nblk, agg, aggz, nullptr, nullptr, 0);
+  if constexpr (sizeof(T) == 2) {  // bf16: the bf16-MFMA block kernel of the non-causal path
+    const hipError_t e = launch_block_state_bf16(k, v, BH, N, D, M, tblk, nblk, agg, aggz, stream);
+    if (e != hipSuccess) return e;
+  } else {
+    hipLaunchKernelGGL((block_state_kernel<T, D, M>), dim3((unsigned)nblk * (unsigned)BH), dim3(NT), 0, stream,
+                       (const T*)k, (const T*)v, N, tblk, nblk, agg, aggz, nullptr, nullptr, 0);
+  }
   const dim3 sgrid((unsigned)((D * M + D + NT - 1) / NT) * (unsigned)BH);
   hipLaunchKernelGGL(state_scan_kernel, sgrid, dim3(NT), 0, stream, agg, aggz, nblk, D * M, D, nullptr, nullptr,
                      nullptr, nullptr, 1);

@@ -36,6 +36,10 @@ hipError_t launch_noncausal(const void* q, const void* k, const void* v, void* o
 size_t noncausal_bf16_ws_bytes(int BH, int N, int D, int M);
 hipError_t launch_noncausal_bf16(const void* q, const void* k, const void* v, void* o, int BH, int N, int D, int M,
                                  void* ws, hipStream_t stream);
+// Per-block state increments for bf16 inputs on bf16 MFMA (phi(K) as head and tail):
+// agg [BH][nblk][D][M], aggz [BH][nblk][D], blocks of tblk tokens.
+hipError_t launch_block_state_bf16(const void* k, const void* v, int BH, int N, int D, int M, int tblk, int nblk,
+                                   float* agg, float* aggz, hipStream_t stream);
 // Exclusive per-block prefix states (S, z) from a zero initial state (backward pass).
 hipError_t launch_block_prefix(const void* k, const void* v, int BH, int N, int D, int M, int bf16, int tblk,
                                int nblk, float* agg, float* aggz, hipStream_t stream);

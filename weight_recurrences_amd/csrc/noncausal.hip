@@ -50,11 +50,14 @@ struct alignas(16) StateSmem {
 };
 
 // ----------------------------------------------------------------------------
-// Block shares: part[bh][blk] = (sum_{j in blk} phi(k_j) v_j^T, sum_{j in blk} phi(k_j)).
+// Block shares: for slot = bh * nblk + blk,
+//   partS + slot * sS = sum_{j in blk} phi(k_j) v_j^T  ([D][M]),
+//   partz + slot * sz = sum_{j in blk} phi(k_j)        ([D]).
 // Grid: BH * nblk workgroups, blockIdx.x = bh * nblk + blk.
 template <int D, int M>
 __global__ __launch_bounds__(NT) void nc_state_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-                                                      int N, int tblk, int nblk, float* __restrict__ part) {
+                                                      int N, int tblk, int nblk, float* __restrict__ partS,
+                                                      float* __restrict__ partz, int sS, int sz) {
   using GG = G<D, M>;
   __shared__ StateSmem<D, M> sm;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
@@ -132,7 +135,7 @@ __global__ __launch_bounds__(NT) void nc_state_kernel(const bf16_t* __restrict__
     }
   }
 
-  float* dst = part + ((size_t)bh * nblk + blk) * GG::SZ;
+  float* dst = partS + ((size_t)bh * nblk + blk) * sS;
 #pragma unroll
   for (int u = 0; u < GG::TMW; ++u) {
     const int tm = w / GG::TD + GG::WPT * u;
@@ -140,8 +143,9 @@ __global__ __launch_bounds__(NT) void nc_state_kernel(const bf16_t* __restrict__
     for (int r = 0; r < 4; ++r) dst[(16 * td + 4 * g + r) * M + 16 * tm + n] = S[u][r];
   }
   if (w < GG::TD && n == 0) {
+    float* dz = partz + ((size_t)bh * nblk + blk) * sz;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dst[D * M + 16 * w + 4 * g + r] = Z[r];
+    for (int r = 0; r < 4; ++r) dz[16 * w + 4 * g + r] = Z[r];
   }
 }
 
@@ -335,7 +339,7 @@ static hipError_t impl(const void* q, const void* k, const void* v, void* o, int
   float* tot = part + (size_t)BH * p.ns * GG::SZ;
   const dim3 block(NT);
   hipLaunchKernelGGL((nc_state_kernel<D, M>), dim3((unsigned)p.ns * (unsigned)BH), block, 0, stream,
-                     (const bf16_t*)k, (const bf16_t*)v, N, p.ts, p.ns, part);
+                     (const bf16_t*)k, (const bf16_t*)v, N, p.ts, p.ns, part, part + D * M, GG::SZ, GG::SZ);
   if (p.ns > 1) {
     const int parts = (GG::SZ / 4 + NT - 1) / NT;
     hipLaunchKernelGGL((nc_reduce_kernel<D, M>), dim3((unsigned)(parts * BH)), block, 0, stream, part, p.ns, parts,
@@ -359,6 +363,25 @@ size_t noncausal_bf16_ws_bytes(int BH, int N, int D, int M) {
     case 6464: return nc::ws_bytes<64, 64>(BH, N);
     default: return 0;
   }
+}
+
+// Per-block increments of the causal state for bf16 inputs (agg [BH][nblk][D][M],
+// aggz [BH][nblk][D]; blocks of tblk tokens, tblk a multiple of 128).
+hipError_t launch_block_state_bf16(const void* k, const void* v, int BH, int N, int D, int M, int tblk, int nblk,
+                                   float* agg, float* aggz, hipStream_t stream) {
+  const dim3 grid((unsigned)nblk * (unsigned)BH), block(nc::NT);
+#define LA_NC_STATE(DD, MM)                                                                                  \
+  hipLaunchKernelGGL((nc::nc_state_kernel<DD, MM>), grid, block, 0, stream, (const bf16_t*)k, (const bf16_t*)v, \
+                     N, tblk, nblk, agg, aggz, DD * MM, DD)
+  switch (D * 100 + M) {
+    case 3232: LA_NC_STATE(32, 32); break;
+    case 3264: LA_NC_STATE(32, 64); break;
+    case 6432: LA_NC_STATE(64, 32); break;
+    case 6464: LA_NC_STATE(64, 64); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef LA_NC_STATE
+  return hipGetLastError();
 }
 
 hipError_t launch_noncausal_bf16(const void* q, const void* k, const void* v, void* o, int BH, int N, int D, int M,
