@@ -80,8 +80,8 @@ struct alignas(16) Smem {
     bf16_t Kl[CH * D];  // phase 1: phi(K) tail of the current chunk
     bf16_t St[M * D];   // phase 3: S^T operand of a state
   } u;
-  bf16_t Zh[D];         // phase 3: z of that state as a bf16 head
-  bf16_t Zl[D];         //          and tail
+  bf16_t Zh[2][D];      // phase 3: z of a state as a bf16 head (double-buffered)
+  bf16_t Zl[2][D];      //          and tail
   int status;
 };
 
@@ -324,40 +324,42 @@ __device__ __forceinline__ void snap_take(Snap<D, M>& s, const Tiles<D, M>& t) {
 
 // A state as the phase-3 operands: S^T in bf16 (each wave writes its tiles) and
 // z as a bf16 head and tail, so that z . phi(q) keeps float32-level accuracy.
-// l_wr = lane_off<UK>(n, 4 g).
+// l_wr = lane_off<UK>(n, 4 g).  st: the S^T tile (row-major [M][D], swizzled as
+// any tile of D columns); zh, zl: the z head and tail.
 template <int D, int M>
-__device__ __forceinline__ void put_operand(Smem<D, M>& sm, const u32x2 (&S)[G<D, M>::TMW], const f32x4& Z, int w,
-                                            int n, int g, uint32_t l_wr) {
+__device__ __forceinline__ void put_operand(bf16_t* st, bf16_t* zh, bf16_t* zl, const u32x2 (&S)[G<D, M>::TMW],
+                                            const f32x4& Z, int w, int n, int g, uint32_t l_wr) {
   using GG = G<D, M>;
 #pragma unroll
   for (int u = 0; u < GG::TMW; ++u) {
     int tdd, tm;
     tile_coords<D, M>(w, u, tdd, tm);
-    *reinterpret_cast<u32x2*>(tile_at<GG::UK>(sm.u.St, l_wr, 16 * tm, 16 * tdd)) = S[u];
+    *reinterpret_cast<u32x2*>(tile_at<GG::UK>(st, l_wr, 16 * tm, 16 * tdd)) = S[u];
   }
   if (w < GG::TD && n == 0) {
     const uint32_t h0 = cvt_pk(Z[0], Z[1]), h1 = cvt_pk(Z[2], Z[3]);
-    *reinterpret_cast<u32x2*>(&sm.Zh[16 * w + 4 * g]) = u32x2{h0, h1};
-    *reinterpret_cast<u32x2*>(&sm.Zl[16 * w + 4 * g]) =
+    *reinterpret_cast<u32x2*>(&zh[16 * w + 4 * g]) = u32x2{h0, h1};
+    *reinterpret_cast<u32x2*>(&zl[16 * w + 4 * g]) =
         u32x2{cvt_pk(Z[0] - lo_of(h0), Z[1] - hi_of(h0)), cvt_pk(Z[2] - lo_of(h1), Z[3] - hi_of(h1))};
   }
 }
 
 // num^T += S^T phi(Q)^T and den += z^T phi(Q)^T for one wave's 16 query columns,
-// with (S, z) the operands in LDS; l_rd = lane_off<UK>(n, 8 g).
+// with (S, z) the operands written by put_operand; l_rd = lane_off<UK>(n, 8 g).
 template <int D, int M>
-__device__ __forceinline__ void state_read(const Smem<D, M>& sm, const bf16x8 (&qf)[D / 32], f32x4 (&numT)[M / 16],
-                                           f32x4& den, int g, uint32_t l_rd) {
+__device__ __forceinline__ void state_read(const bf16_t* st, const bf16_t* zh, const bf16_t* zl,
+                                           const bf16x8 (&qf)[D / 32], f32x4 (&numT)[M / 16], f32x4& den, int g,
+                                           uint32_t l_rd) {
   using GG = G<D, M>;
 #pragma unroll
   for (int s = 0; s < D / 32; ++s) {
 #pragma unroll
     for (int tm = 0; tm < GG::TM; ++tm) {
-      const bf16x8 as = as_bf16x8(*reinterpret_cast<const u32x4*>(tile_at<GG::UK>((const bf16_t*)sm.u.St, l_rd, 16 * tm, 32 * s)));
+      const bf16x8 as = as_bf16x8(*reinterpret_cast<const u32x4*>(tile_at<GG::UK>(st, l_rd, 16 * tm, 32 * s)));
       numT[tm] = mma(as, qf[s], numT[tm]);
     }
-    den = mma(as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.Zh[32 * s + 8 * g])), qf[s], den);
-    den = mma(as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.Zl[32 * s + 8 * g])), qf[s], den);
+    den = mma(as_bf16x8(*reinterpret_cast<const u32x4*>(&zh[32 * s + 8 * g])), qf[s], den);
+    den = mma(as_bf16x8(*reinterpret_cast<const u32x4*>(&zl[32 * s + 8 * g])), qf[s], den);
   }
 }
 
@@ -499,9 +501,13 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       if (c >= nch) break;
+      // The local prefix of chunk c >= 2 goes into the K rows of chunk c - 2 (no
+      // wave reads them after chunk c - 2, and every wave has passed chunk c - 1's
+      // barrier since), chunk 1's into the dedicated tile, and z alternates
+      // between two buffers: one barrier per chunk.
+      bf16_t* st = c >= 2 ? sm.K + (size_t)(c - 2) * CH * D : sm.u.St;
       if (c > 0) {
-        __syncthreads();  // the previous readers of the operand tiles are done
-        put_operand<D, M>(sm, snap[c].S, snap[c].Z, w, n, g, l_wr);
+        put_operand<D, M>(st, sm.Zh[c & 1], sm.Zl[c & 1], snap[c].S, snap[c].Z, w, n, g, l_wr);
         __syncthreads();
       }
 #pragma unroll
@@ -553,7 +559,7 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
         }
       }
       // Local prefix of the block at the chunk start.
-      if (c > 0) state_read<D, M>(sm, qf[c], numT[c], den, g, l_rd);
+      if (c > 0) state_read<D, M>(st, sm.Zh[c & 1], sm.Zl[c & 1], qf[c], numT[c], den, g, l_rd);
       dsum[c] = den[0];
     }
   }
@@ -679,13 +685,16 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
   if (!o) return;
 
   // ---------------- phase 3b: add the prefix of earlier blocks, store ----------------
+  // P goes into the K rows of chunk 2 and z buffer 0 (last read by chunk 2 of
+  // phase 3a; a later block has passed the look-back's barriers since).
   const bool have_p = b > 0 || S0 != nullptr;
+  bf16_t* st_p = sm.K + (size_t)2 * CH * D;
   if (have_p) {
-    __syncthreads();  // phase 3a's readers of the operand tiles are done
+    if (b == 0) __syncthreads();  // no look-back barrier after phase 3a
     u32x2 ps[GG::TMW];
 #pragma unroll
     for (int u = 0; u < GG::TMW; ++u) ps[u] = u32x2{cvt_pk(P.S[u][0], P.S[u][1]), cvt_pk(P.S[u][2], P.S[u][3])};
-    put_operand<D, M>(sm, ps, P.Z, w, n, g, l_wr);
+    put_operand<D, M>(st_p, sm.Zh[0], sm.Zl[0], ps, P.Z, w, n, g, l_wr);
     __syncthreads();
   }
   bf16_t* oh = o + (size_t)bh * N * M;
@@ -695,7 +704,7 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
     float den = dsum[c];
     if (have_p) {
       f32x4 dd{0.f, 0.f, 0.f, 0.f};
-      state_read<D, M>(sm, qf[c], numT[c], dd, g, l_rd);
+      state_read<D, M>(st_p, sm.Zh[0], sm.Zl[0], qf[c], numT[c], dd, g, l_rd);
       den += dd[0];
     }
     // o_i = num_i / den_i for query i = 16w + n: lane (n, g) holds the four
