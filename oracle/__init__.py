@@ -60,6 +60,7 @@ def _load():
             lib.oracle_noncausal.argtypes = [_D, _D, _D, _i64, _i64, _i64, _i64, _D, _D, _D]
             lib.oracle_decode_step.argtypes = [_D, _D, _D, _i64, _i64, _i64, _D, _D, _D]
             lib.oracle_deltanet.argtypes = [_D, _D, _D, _D, _i64, _i64, _i64, _i64, _D, _D, _D]
+            lib.oracle_softmax_decode.argtypes = [_D, _D, _D, _i64, _i64, _i64, _i64, _i64, _D]
             _lib = lib
     return _lib
 
@@ -186,6 +187,26 @@ def deltanet(q, k, v, beta, W0=None):
     W = np.empty((B, H, M, D))
     _load().oracle_deltanet(_p(q), _p(k), _p(v), _p(beta), B * H, N, D, M, _p(W0), _p(o), _p(W))
     return o, W
+
+
+def softmax_decode(q, k, v, Kc, Vc, L):
+    """Softmax attention decode step over a key/value cache ([TR] eq.(2), App. C.1):
+    the new key and value are appended at row L of float64 copies of the caches and
+    o = softmax(q K^T / sqrt(D)) V over rows 0..L.
+    q, k: [B,H,D]; v: [B,H,M]; Kc: [B,H,Lmax,D]; Vc: [B,H,Lmax,M].
+    Returns (o [B,H,M], Kc_new, Vc_new) float64."""
+    q, k, v = f64(q), f64(k), f64(v)
+    Kc = f64(Kc).copy()
+    Vc = f64(Vc).copy()
+    B, H, D = q.shape
+    M = v.shape[-1]
+    Lmax = Kc.shape[2]
+    assert 0 <= L < Lmax and Kc.shape == (B, H, Lmax, D) and Vc.shape == (B, H, Lmax, M)
+    Kc[:, :, L] = k
+    Vc[:, :, L] = v
+    o = np.empty((B, H, M))
+    _load().oracle_softmax_decode(_p(q), _p(Kc), _p(Vc), B * H, L, Lmax, D, M, _p(o))
+    return o, Kc, Vc
 
 
 from .gradients import causal_bwd  # noqa: E402  (fp64 autograd of the forward definition)

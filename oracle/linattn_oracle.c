@@ -20,6 +20,11 @@
  *         capacity limit, on the new update rule ("改進與更新") and on
  *         normalisation ("歸一化").
  *
+ * The softmax decode step (oracle_softmax_decode) is the comparison baseline the
+ * first page measures the recurrent form against: softmax attention, [TR] §3.1
+ * eq.(2), evaluated for one new token over a cache of the earlier tokens' keys
+ * and values ([TR] Appendix C.1, "stateful softmax").
+ *
  * Layouts (row-major, contiguous, double precision):
  *   q, k : [BH, N, D]     v, o : [BH, N, M]
  *   S    : [BH, D, M]     z    : [BH, D]        W : [BH, M, D]
@@ -276,5 +281,42 @@ void oracle_deltanet(const double* q, const double* k, const double* v, const do
     }
     if (W_out) memcpy(W_out + h * M * D, W, sizeof(double) * (size_t)(M * D));
     free(W); free(kh); free(qh); free(vbar);
+  }
+}
+
+/* Softmax attention for one new token over a key/value cache: the "stateful
+ * softmax" of [TR] Appendix C.1 (the keys and values of earlier tokens are kept
+ * rather than recomputed), with the attention of [TR] §3.1 eq.(2),
+ *   o = softmax(q K^T / sqrt(D)) V,
+ * over rows 0..L of the cache, where row L holds the new token's key and value
+ * (the caller appends them).  The largest score is subtracted before the
+ * exponentials, which leaves the weights unchanged.
+ * q: [BH, D]; Kc: [BH, Lmax, D]; Vc: [BH, Lmax, M]; o: [BH, M]. */
+void oracle_softmax_decode(const double* q, const double* Kc, const double* Vc, i64 BH, i64 L, i64 Lmax, i64 D,
+                           i64 M, double* o) {
+#pragma omp parallel for schedule(static)
+  for (i64 h = 0; h < BH; ++h) {
+    const double* qh = q + h * D;
+    const double* Kh = Kc + h * Lmax * D;
+    const double* Vh = Vc + h * Lmax * M;
+    double* w = (double*)malloc(sizeof(double) * (size_t)(L + 1));
+    double mx = -INFINITY;
+    for (i64 j = 0; j <= L; ++j) {
+      double s = 0.0;
+      for (i64 d = 0; d < D; ++d) s += qh[d] * Kh[j * D + d];
+      w[j] = s / sqrt((double)D);
+      if (w[j] > mx) mx = w[j];
+    }
+    double tot = 0.0;
+    for (i64 j = 0; j <= L; ++j) {
+      w[j] = exp(w[j] - mx);
+      tot += w[j];
+    }
+    for (i64 m = 0; m < M; ++m) {
+      double acc = 0.0;
+      for (i64 j = 0; j <= L; ++j) acc += w[j] * Vh[j * M + m];
+      o[h * M + m] = acc / tot;
+    }
+    free(w);
   }
 }

@@ -457,3 +457,79 @@ def test_bwd_invariants_of_the_normalised_form():
     dq2, dk2, _ = oracle.causal_bwd(q, k, v + np.array([0.7, -1.3, 2.0]), dO)
     assert mat_rel_err(dq2, dq) < 1e-12 and mat_rel_err(dk2, dk) < 1e-12
     np.testing.assert_allclose(dv.sum(axis=2), dO.sum(axis=2), rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------ softmax decode baseline
+# The "stateful softmax" comparison baseline ([TR] Appendix C.1): softmax
+# attention, [TR] §3.1 eq.(2), of one new token over a key/value cache.
+
+def _cache(B, H, L, Lmax, D, M, seed):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, H, D))
+    k = rng.standard_normal((B, H, D))
+    v = rng.standard_normal((B, H, M))
+    Kc = rng.standard_normal((B, H, Lmax, D))
+    Vc = rng.standard_normal((B, H, Lmax, M))
+    return q, k, v, Kc, Vc
+
+
+@pytest.mark.parametrize("D,M", [(4, 3), (8, 8), (32, 64)])
+def test_softmax_decode_matches_bruteforce(D, M):
+    q, k, v, Kc, Vc = _cache(2, 2, 9, 12, D, M, seed=D + M)
+    o, K2, V2 = oracle.softmax_decode(q, k, v, Kc, Vc, 9)
+    for b in range(2):
+        for h in range(2):
+            ref = brute.softmax_row(list(q[b, h]), [list(r) for r in K2[b, h, :10]], [list(r) for r in V2[b, h, :10]])
+            assert np.abs(o[b, h] - np.array(ref)).max() < 1e-12
+    # the append writes exactly the new row and leaves the others
+    assert np.array_equal(K2[:, :, 9], k) and np.array_equal(V2[:, :, 9], v)
+    assert np.array_equal(np.delete(K2, 9, axis=2), np.delete(Kc, 9, axis=2))
+
+
+def test_softmax_decode_first_token_returns_value():
+    q, k, v, Kc, Vc = _cache(3, 2, 0, 4, 8, 5, seed=1)
+    o, _, _ = oracle.softmax_decode(q, k, v, Kc, Vc, 0)
+    assert np.array_equal(o, v)
+
+
+def test_softmax_decode_constant_keys_give_mean():
+    q, k, v, Kc, Vc = _cache(2, 3, 7, 10, 16, 6, seed=2)
+    Kc[:, :, :7] = k[:, :, None, :]
+    o, _, V2 = oracle.softmax_decode(q, k, v, Kc, Vc, 7)
+    assert np.abs(o - V2[:, :, :8].mean(axis=2)).max() < 1e-12
+
+
+def test_softmax_decode_shift_and_scale_properties():
+    q, k, v, Kc, Vc = _cache(2, 2, 11, 16, 8, 4, seed=3)
+    o, _, V2 = oracle.softmax_decode(q, k, v, Kc, Vc, 11)
+    # adding one vector to every key adds the same constant to every score
+    u = np.random.default_rng(4).standard_normal(8)
+    o2, _, _ = oracle.softmax_decode(q, k + u, v, Kc + u, Vc, 11)
+    assert np.abs(o2 - o).max() < 1e-12
+    # outputs are convex combinations of the values
+    lo, hi = V2[:, :, :12].min(axis=2), V2[:, :, :12].max(axis=2)
+    assert (o >= lo - 1e-12).all() and (o <= hi + 1e-12).all()
+    # affine in the values
+    o3, _, _ = oracle.softmax_decode(q, k, 2.0 * v - 1.0, Kc, 2.0 * Vc - 1.0, 11)
+    assert np.abs(o3 - (2.0 * o - 1.0)).max() < 1e-12
+
+
+def test_softmax_decode_dominant_key_and_scaling():
+    # q = a e_0 with key e_0 at row 3 and zero keys elsewhere: the weight of row 3
+    # against each other row is exp(a / sqrt(D)); with a / sqrt(D) = 60 the output
+    # is v_3 to within exp(-60) relative.
+    D, M, L = 16, 4, 6
+    q, k, v, Kc, Vc = _cache(1, 1, L, 8, D, M, seed=5)
+    Kc[:] = 0.0
+    k[:] = 0.0
+    Kc[0, 0, 3, 0] = 1.0
+    q[:] = 0.0
+    q[0, 0, 0] = 60.0 * math.sqrt(D)
+    o, _, _ = oracle.softmax_decode(q, k, v, Kc, Vc, L)
+    assert np.abs(o[0, 0] - Vc[0, 0, 3]).max() < 1e-20 * np.abs(Vc).max() + 1e-24
+    # with score gap exactly log 3 between row 3 and the six others: weight 3/9
+    q[0, 0, 0] = math.log(3.0) * math.sqrt(D)
+    o, _, V2 = oracle.softmax_decode(q, k, v, Kc, Vc, L)
+    others = [j for j in range(L + 1) if j != 3]
+    expect = (3.0 * V2[0, 0, 3] + V2[0, 0, others].sum(axis=0)) / 9.0
+    assert np.abs(o[0, 0] - expect).max() < 1e-12
