@@ -140,6 +140,21 @@ int linattn_decode_step(const void* q, const void* k, const void* v, void* o,
                         float* S, float* z, int B, int H, int D, int M, int dtype,
                         void* stream);
 
+/* Softmax attention decode step over a key/value cache: the "stateful softmax"
+ * baseline the recurrent form is compared with ("Transformers are RNNs",
+ * translated page, Appendix C.1), with the attention of §3.1 eq.(2):
+ *   Kc[L] <- k, Vc[L] <- v,  o = softmax(q Kc[0..L]^T / sqrt(D)) Vc[0..L],
+ * for B*H independent heads.  Its cost grows with L, unlike the fixed-size
+ * state of linattn_decode_step.
+ * q, k: [B,H,D]; v, o: [B,H,M]; Kc: [B,H,Lmax,D]; Vc: [B,H,Lmax,M], all in
+ * dtype, caller-owned; rows 0..L-1 of the caches hold the earlier tokens and
+ * row L is written.  0 <= L < Lmax (else LINATTN_ERR_SHAPE).  Arithmetic is
+ * float32; o is rounded to dtype.  o must not overlap q, k, v, Kc or Vc; the
+ * caches must not overlap each other or q, k, v. */
+int softmax_decode_step(const void* q, const void* k, const void* v, void* o,
+                        void* Kc, void* Vc, int B, int H, int L, int Lmax,
+                        int D, int M, int dtype, void* stream);
+
 /* Delta-rule fast-weight memory over a sequence, for every (b, h), i = 1..N:
  *   kh = phi(k_i)/sum_c phi(k_i)_c,  qh = phi(q_i)/sum_c phi(q_i)_c,
  *   vbar = W kh,  W <- W + beta_i (v_i - vbar) kh^T,  o_i = W qh

@@ -83,6 +83,15 @@ def qkv_beta(B, H, N, D, M, *, dtype=torch.float32, scale=1.0, seed=0):
     return q, k, v, beta
 
 
+def kv_cache(B, H, L, D, M, *, dtype=torch.bfloat16, scale=1.0, seed=0):
+    """Key and value caches of L earlier tokens for the softmax decode baseline:
+    Kc [B,H,L,D], Vc [B,H,L,M], i.i.d. N(0,1)*scale."""
+    g = _gen(seed)
+    Kc = _draw(g, (B, H, L, D), scale, dtype)
+    Vc = _draw(g, (B, H, L, M), scale, dtype)
+    return Kc, Vc
+
+
 def decode_steps(B, H, D, M, T, *, dtype=torch.bfloat16, scale=1.0, seed=0):
     """Fresh per-step inputs for T decode steps: q, k [T,B,H,D]; v [T,B,H,M]."""
     g = _gen(seed)

@@ -223,3 +223,27 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 1, 4, 32)
     with pytest.raises(ValueError, match="GPU"):
         la.causal(x, x, x)
+
+
+@no_gpu
+def test_softmax_decode_validation(lib):
+    f = lib.softmax_decode_step
+    # q, k, v, o small; caches far apart (fake device addresses, never dereferenced)
+    args = [Q, K, V, O, S0, SO, 256, 16, 700, 1536, 64, 64, 1, None]
+    bad = list(args); bad[4] = None
+    assert f(*bad) == NULL
+    bad = list(args); bad[8] = 1536        # L must be below Lmax
+    assert f(*bad) == SHAPE
+    bad = list(args); bad[8] = -1
+    assert f(*bad) == SHAPE
+    bad = list(args); bad[12] = 5
+    assert f(*bad) == DTYPE
+    bad = list(args); bad[10] = 48
+    assert f(*bad) == UNSUP
+    bad = list(args); bad[3] = S0 + 64     # o inside the key cache
+    assert f(*bad) == ALIAS
+    bad = list(args); bad[5] = S0 + 4096   # value cache overlaps the key cache
+    assert f(*bad) == ALIAS
+    bad = list(args); bad[0] = Q + 8
+    assert f(*bad) == ALIGN
+    assert f(None, None, None, None, None, None, 0, 16, 0, 1, 64, 64, 1, None) == OK

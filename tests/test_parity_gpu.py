@@ -470,3 +470,60 @@ def test_causal_bwd_long_workload_sampled_head():
         for got, ref, name in ((dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv")):
             e = _grad_err(got[sel], ref, scale)
             assert e < 1e-2, (b, h, name, e)
+
+
+# ---------------------------------------------------------------- softmax decode baseline
+
+def _softmax_inputs(B, H, L, Lmax, D, M, dtype, seed):
+    q, k, v = synth.decode_steps(B, H, D, M, 1, dtype=dtype, seed=seed)
+    Kc, Vc = synth.kv_cache(B, H, Lmax, D, M, dtype=dtype, seed=seed + 1)
+    return q[0], k[0], v[0], Kc, Vc
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("D,M", [(32, 32), (32, 64), (64, 32), (64, 64)])
+@pytest.mark.parametrize("L", [0, 1, 31, 32, 33, 127, 128, 129, 1000])
+def test_softmax_decode_ragged(dtype, D, M, L):
+    say("softmax decode", dtype, D, M, L)
+    q, k, v, Kc, Vc = _softmax_inputs(2, 3, L, L + 5, D, M, dtype, seed=L * 3 + D + M)
+    Kg, Vg = gpu(Kc, Vc)
+    o = la.softmax_decode_step(*gpu(q, k, v), Kg, Vg, L)
+    ro, rK, rV = oracle.softmax_decode(q, k, v, Kc, Vc, L)
+    assert row_rel_err(host(o), ro) < TOL[dtype]
+    # row L now holds k and v; every other row is unchanged
+    assert torch.equal(host(Kg)[:, :, L], k) and torch.equal(host(Vg)[:, :, L], v)
+    keep = [j for j in range(L + 5) if j != L]
+    assert torch.equal(host(Kg)[:, :, keep], Kc[:, :, keep]) and torch.equal(host(Vg)[:, :, keep], Vc[:, :, keep])
+
+
+def test_softmax_decode_steps_append():
+    """A prefill cache, then steps that each append and attend: every output
+    against the oracle run on the caches it has built itself."""
+    B, H, D, M, P, T = 3, 4, 64, 64, 37, 70
+    dtype = torch.bfloat16
+    Kc, Vc = synth.kv_cache(B, H, P + T, D, M, dtype=dtype, seed=11)
+    sq, sk, sv = synth.decode_steps(B, H, D, M, T, dtype=dtype, seed=12)
+    Kg, Vg = gpu(Kc, Vc)
+    rK, rV = Kc, Vc
+    for t in range(T):
+        say("softmax decode step", t)
+        o = la.softmax_decode_step(*gpu(sq[t], sk[t], sv[t]), Kg, Vg, P + t)
+        ro, rK, rV = oracle.softmax_decode(sq[t], sk[t], sv[t], rK, rV, P + t)
+        assert row_rel_err(host(o), ro) < 2e-2
+    assert torch.equal(host(Kg).double(), torch.from_numpy(rK)) and torch.equal(host(Vg).double(), torch.from_numpy(rV))
+
+
+def test_softmax_decode_workload_shape():
+    """The decode workload's shape: 256 sequences x 16 heads, D = M = 64, bf16, at
+    the first and last context lengths of its 512 + 1024 tokens (every head)."""
+    w = synth.WORKLOADS["decode"]
+    Lmax = w.N + w.steps
+    Kc, Vc = synth.kv_cache(w.B, w.H, Lmax, w.D, w.M, dtype=w.dtype, seed=w.seed + 70)
+    Kg, Vg = gpu(Kc, Vc)
+    sq, sk, sv = synth.decode_steps(w.B, w.H, w.D, w.M, 2, dtype=w.dtype, seed=w.seed + 71)
+    for t, L in enumerate([w.N, Lmax - 1]):
+        say("softmax decode workload", L)
+        o = la.softmax_decode_step(*gpu(sq[t], sk[t], sv[t]), Kg, Vg, L)
+        ro, _, _ = oracle.softmax_decode(sq[t], sk[t], sv[t], Kc, Vc, L)
+        Kc[:, :, L], Vc[:, :, L] = sk[t], sv[t]
+        assert row_rel_err(host(o), ro) < 2e-2

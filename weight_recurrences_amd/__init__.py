@@ -178,6 +178,31 @@ def decode_step(q, k, v, S, z, *, out=None):
     return o
 
 
+def softmax_decode_step(q, k, v, Kc, Vc, L, *, out=None):
+    """Softmax attention decode step over a key/value cache (the stateful-softmax
+    baseline, eq.(2)): k, v are written to row L of the caches and
+    o = softmax(q Kc[0..L]^T / sqrt(D)) Vc[0..L] is returned.
+
+    q, k: [B,H,D]; v: [B,H,M]; Kc: [B,H,Lmax,D]; Vc: [B,H,Lmax,M], all of one
+    dtype (float32 or bfloat16).  Returns o [B,H,M] in that dtype.
+    """
+    lib = load()
+    dev = _dev(q, k, v, Kc, Vc)
+    B, H, D = q.shape
+    M = v.shape[-1]
+    Lmax = Kc.shape[2]
+    if k.shape != q.shape or v.shape[:2] != q.shape[:2] or Kc.shape != (B, H, Lmax, D) or Vc.shape != (B, H, Lmax, M):
+        raise ValueError("q, k [B,H,D]; v [B,H,M]; Kc [B,H,Lmax,D]; Vc [B,H,Lmax,M]")
+    if len({t.dtype for t in (q, k, v, Kc, Vc)}) != 1:
+        raise ValueError("q, k, v and the caches must share one dtype")
+    dt = _dtype_code(q)
+    o = out if out is not None else torch.empty((B, H, M), dtype=q.dtype, device=dev)
+    rc = lib.softmax_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(Kc), _ptr(Vc), B, H, int(L), Lmax, D, M, dt,
+                                 _stream(dev))
+    check(rc, "softmax_decode_step")
+    return o
+
+
 def deltanet_workspace_bytes(B, H, N, D, M, dtype) -> int:
     return int(load().deltanet_workspace_bytes(B, H, N, D, M, _DT[dtype]))
 

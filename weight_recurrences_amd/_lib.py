@@ -40,6 +40,7 @@ SIGNATURES = {
     "deltanet_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "deltanet_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "deltanet_decode_step": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
+    "softmax_decode_step": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "linattn_status_str": (ctypes.c_char_p, [_i]),
     "linattn_abi_version": (_i, []),
 }
@@ -56,7 +57,7 @@ def header_functions() -> list[str]:
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
-    return sorted({n for n in names if n.startswith(("linattn_", "deltanet_"))})
+    return sorted({n for n in names if n.startswith(("linattn_", "deltanet_", "softmax_"))})
 
 
 def load():

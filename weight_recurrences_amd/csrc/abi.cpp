@@ -174,6 +174,27 @@ int linattn_decode_step(const void* q, const void* k, const void* v, void* o, fl
   return hip_status(la::launch_decode(q, k, v, o, S, z, (int)BH, D, M, dtype == LINATTN_BF16, (hipStream_t)stream));
 }
 
+int softmax_decode_step(const void* q, const void* k, const void* v, void* o, void* Kc, void* Vc, int B, int H,
+                        int L, int Lmax, int D, int M, int dtype, void* stream) {
+  int st = check_shape(B, H, Lmax, D, M, dtype);
+  if (st) return st;
+  if (L < 0 || L >= Lmax) return LINATTN_ERR_SHAPE;
+  const long long BH = (long long)B * H, es = esize(dtype);
+  if (BH == 0) return LINATTN_OK;
+  if (!q || !k || !v || !o || !Kc || !Vc) return LINATTN_ERR_NULL;
+  if ((st = check_align({q, k, v, o, Kc, Vc}))) return st;
+  const Span sq(q, BH * D * es), sk(k, BH * D * es), sv(v, BH * M * es), so(o, BH * M * es);
+  const Span sK(Kc, BH * Lmax * D * es), sV(Vc, BH * Lmax * M * es);
+  for (const Span& x : {sq, sk, sv, sK, sV})
+    if (so.overlaps(x)) return LINATTN_ERR_ALIAS;
+  for (const Span& x : {sq, sk, sv, sV})
+    if (sK.overlaps(x)) return LINATTN_ERR_ALIAS;
+  for (const Span& x : {sq, sk, sv})
+    if (sV.overlaps(x)) return LINATTN_ERR_ALIAS;
+  return hip_status(la::launch_softmax_decode(q, k, v, o, Kc, Vc, (int)BH, L, Lmax, D, M, dtype == LINATTN_BF16,
+                                              (hipStream_t)stream));
+}
+
 size_t deltanet_workspace_bytes(int B, int H, int N, int D, int M, int dtype) {
   if (check_shape(B, H, N, D, M, dtype) != LINATTN_OK) return 0;
   return la::deltanet_ws_bytes(B * H, N, D, M);

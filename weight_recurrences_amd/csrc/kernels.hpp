@@ -36,6 +36,10 @@ hipError_t launch_noncausal(const void* q, const void* k, const void* v, void* o
 size_t noncausal_bf16_ws_bytes(int BH, int N, int D, int M);
 hipError_t launch_noncausal_bf16(const void* q, const void* k, const void* v, void* o, int BH, int N, int D, int M,
                                  void* ws, hipStream_t stream);
+// Softmax attention decode step over a key/value cache (the comparison baseline):
+// appends k, v at row L of Kc [BH][Lmax][D], Vc [BH][Lmax][M] and attends over rows 0..L.
+hipError_t launch_softmax_decode(const void* q, const void* k, const void* v, void* o, void* Kc, void* Vc, int BH,
+                                 int L, int Lmax, int D, int M, int bf16, hipStream_t stream);
 // Per-block state increments for bf16 inputs on bf16 MFMA (phi(K) as head and tail):
 // agg [BH][nblk][D][M], aggz [BH][nblk][D], blocks of tblk tokens.
 hipError_t launch_block_state_bf16(const void* k, const void* v, int BH, int N, int D, int M, int tblk, int nblk,
