@@ -6,7 +6,8 @@ accumulation and state, B=2 H=16 N=32768 D=M=64 — one step is one full
 ``linattn_causal_fwd`` over the batch (every kernel of the causal path).
 Other workloads (``--workload``): noncausal_long, decode (prefill + 1024
 single-token steps on 256x16 states), deltanet, deltanet_decode (the same for the
-delta-rule memory), causal_mid, and copy (a 1 GiB device copy that calibrates
+delta-rule memory), softmax_decode (the same steps as softmax attention over a
+key/value cache, the comparison baseline), causal_mid, and copy (a 1 GiB device copy that calibrates
 the HBM counters).
 
 Prints ONE JSON line.  Inputs are synthetic (seeded N(0,1), the recipe of the
@@ -14,7 +15,10 @@ synth module), copied to the GPU before the timed region.  Timing: W untimed
 warm-up steps, then K timed steps launched back to back and bracketed by a
 device synchronisation; HIP events at both ends of the timed region are recorded
 on the stream the library launches on (torch's current stream, passed to the C
-ABI), and the average launch duration is the region over its launches.  The CPU baseline is
+ABI), and the average launch duration is the region over its launches.  The default
+warm-up is long enough (>= 50 ms of back-to-back launches) for the GPU's clocks
+to settle: the first ~100 launches of the causal kernel after idle run up to 15%
+slower than the steady state.  The CPU baseline is
 the oracle timed on the host cores on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -46,6 +50,7 @@ WORKLOAD_SOURCES = {
     "decode": ["decode.hip", "common.hpp"],
     "deltanet": ["deltanet.hip", "deltanet_chunk.hip", "common.hpp"],
     "deltanet_decode": ["deltanet.hip", "common.hpp"],
+    "softmax_decode": ["softmax_decode.hip", "common.hpp"],
 }
 
 
@@ -92,7 +97,7 @@ def time_oracle(workload, inputs, budget_s: float = 20.0):
     threads = len(os.sched_getaffinity(0))
     oracle.set_threads(threads)
     w = workload
-    if w.name == "decode":
+    if w.name == "decode" and len(inputs) == 6:
         q, k, v, sq, sk, sv = inputs
         nh = w.B * w.H
         # sample: all states, prefill + the first T steps
@@ -123,6 +128,26 @@ def time_oracle(workload, inputs, budget_s: float = 20.0):
         dt = time.perf_counter() - t0
         return {"value": nh * w.N / dt, "unit": "tokens/s", "cores": torch.get_num_threads(), "kind": "oracle",
                 "sample": f"{nh} of {w.B * w.H} heads, all {w.N} tokens (fp64 autograd), {dt:.1f} s, {cpu_model()}"}
+    if w.name == "decode" and len(inputs) == 7:  # softmax decode over the growing cache
+        import numpy as np
+        pq, pk, pv, sq, sk, sv, _ = inputs
+        nh = w.B * w.H
+        Lmax = w.N + w.steps
+        Kc = np.zeros((w.B, w.H, Lmax, w.D))
+        Vc = np.zeros((w.B, w.H, Lmax, w.M))
+        Kc[:, :, :w.N] = oracle.f64(pk)
+        Vc[:, :, :w.N] = oracle.f64(pv)
+        t0 = time.perf_counter()
+        T = 0
+        while T < w.steps:
+            _, Kc, Vc = oracle.softmax_decode(sq[T], sk[T], sv[T], Kc, Vc, w.N + T)
+            T += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+        return {"value": nh * T / dt, "unit": "head-tokens/s", "cores": threads, "kind": "oracle",
+                "sample": f"the first {T} of {w.steps} steps (cache of {w.N}+ tokens) on all {nh} heads, {dt:.1f} s, "
+                          f"{cpu_model()}"}
     if w.name == "deltanet_decode":
         q, k, v, beta, sq, sk, sv, sb = inputs
         nh = w.B * w.H
@@ -171,14 +196,26 @@ def time_oracle(workload, inputs, budget_s: float = 20.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default per workload: 100 for the sequence workloads, 20 for decode, "
+                         "5 for softmax_decode)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default per workload: enough back-to-back work, >= 50 ms, for "
+                         "the GPU's clocks to settle; a few launches after idle run up to 15%% slower)")
     ap.add_argument("--workload", default="causal_long",
                     choices=["causal_long", "causal_bwd_long", "noncausal_long", "decode", "deltanet", "deltanet_decode",
+                             "softmax_decode",
                              "causal_mid", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--oracle-budget", type=float, default=20.0)
     args = ap.parse_args()
+
+    long_steps = {"decode": (20, 5), "deltanet_decode": (20, 5), "softmax_decode": (5, 2), "copy": (20, 5)}
+    d_steps, d_warm = long_steps.get(args.workload, (100, 300))
+    if args.steps is None:
+        args.steps = d_steps
+    if args.warmup is None:
+        args.warmup = d_warm
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -219,7 +256,8 @@ def main():
                           "ms_per_step": ms, "higher_is_better": True, "bytes_per_copy": nbytes}), flush=True)
         return
 
-    wname = "causal_long" if args.workload in ("noncausal_long", "causal_bwd_long") else args.workload
+    wname = {"noncausal_long": "causal_long", "causal_bwd_long": "causal_long",
+             "softmax_decode": "decode"}.get(args.workload, args.workload)
     w = synth.WORKLOADS[wname]
     inputs = synth.workload_inputs(w)
     K, Wm = args.steps, args.warmup
@@ -278,6 +316,40 @@ def main():
         alg_bytes = w.B * w.H * per_head_token       # per launch (one decode step)
         unit = "head-tokens/s"
         launches_per_step = w.steps
+    elif args.workload == "softmax_decode":
+        # The decode workload's inputs: its 512 prefill tokens fill the key/value
+        # cache, then each of the 1024 steps appends one token and attends over
+        # the whole cache (L = 512 .. 1535).
+        pq, pk, pv, sq, sk, sv = inputs
+        Lmax = w.N + w.steps
+        Kc = torch.zeros(w.B, w.H, Lmax, w.D, dtype=w.dtype, device=dev)
+        Vc = torch.zeros(w.B, w.H, Lmax, w.M, dtype=w.dtype, device=dev)
+        Kc[:, :, :w.N] = pk.to(dev)
+        Vc[:, :, :w.N] = pv.to(dev)
+        sq, sk, sv = sq.to(dev), sk.to(dev), sv.to(dev)
+        o = torch.empty(w.steps, w.B, w.H, w.M, dtype=w.dtype, device=dev)
+
+        def step():
+            for t in range(w.steps):
+                la.softmax_decode_step(sq[t], sk[t], sv[t], Kc, Vc, w.N + t, out=o[t])
+        kernel = "softmax_decode_step (softmax_decode_kernel)"
+        units = w.B * w.H * w.steps
+        es = 2
+        # per head and step: read the L cached rows and q, k, v; write row L and o
+        rows = sum(w.N + t for t in range(w.steps)) / w.steps
+        per_head_step = (rows * (w.D + w.M) + 2 * w.D + 2 * w.M + (w.D + w.M)) * es
+        alg_bytes = int(w.B * w.H * per_head_step)   # per launch, averaged over the 1024 steps
+        unit = "head-tokens/s"
+        launches_per_step = w.steps
+
+        # the linear decode step on the same inputs, for the ratio
+        S0, z0 = la.causal(pq.to(dev), pk.to(dev), pv.to(dev), output=False)
+        S, z = S0.clone(), z0.clone()
+        ol = torch.empty_like(o)
+
+        def linear_step():
+            for t in range(w.steps):
+                la.decode_step(sq[t], sk[t], sv[t], S, z, out=ol[t])
     elif args.workload == "deltanet_decode":
         q, k, v, beta, sq, sk, sv, sb = inputs
         q, k, v, beta = q.to(dev), k.to(dev), v.to(dev), beta.to(dev)
@@ -335,6 +407,19 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel,
                 "algorithmic_bytes_per_launch": alg_bytes, "launch_ms": round(launch_ms, 5)}
+    if args.workload == "softmax_decode":
+        for _ in range(Wm):
+            linear_step()
+        a, b = events(2)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(K):
+            linear_step()
+        b.record(stream)
+        torch.cuda.synchronize()
+        lin_ms = a.elapsed_time(b) / K
+        roofline["linear_decode_same_inputs"] = {"ms_per_step": round(lin_ms, 4),
+                                                  "softmax_over_linear_time": round(ms_per_step / lin_ms, 2)}
     if args.workload == "deltanet":
         flops = units * (6 * w.D * w.M + 6 * w.D)
         roofline["alu"] = {"achieved_tflops": round(flops / (launch_ms / 1e3) / 1e12, 3),
@@ -342,7 +427,8 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = time_oracle(w, inputs, args.oracle_budget)
+        cpu = time_oracle(w, tuple(inputs) + (("softmax",) if args.workload == "softmax_decode" else ()),
+                          args.oracle_budget)
 
     names = {
         "causal_long": f"causal_long: causal linear attention (phi=elu+1), bf16 in/out, fp32 state, "
@@ -356,9 +442,11 @@ def main():
         "deltanet": f"deltanet: delta-rule fast weights, fp32, B={w.B} H={w.H} N={w.N} D=M={w.D}",
         "deltanet_decode": f"deltanet_decode: delta-rule decode, {w.B}x{w.H} memories D=M={w.D}, {w.steps} "
                            f"single-token bf16 steps after a {w.N}-token prefill",
+        "softmax_decode": f"softmax_decode: softmax attention decode over a key/value cache (comparison baseline), "
+                          f"{w.B}x{w.H} heads D=M={w.D}, {w.steps} single-token bf16 steps after a {w.N}-token cache",
     }
     dtype = {"causal_long": "bf16", "causal_bwd_long": "bf16", "noncausal_long": "bf16", "decode": "bf16", "causal_mid": "f32",
-             "deltanet": "f32", "deltanet_decode": "bf16"}[args.workload]
+             "deltanet": "f32", "deltanet_decode": "bf16", "softmax_decode": "bf16"}[args.workload]
     line = {
         "metric": METRIC if args.workload == "causal_long" else f"{args.workload} {unit}",
         "value": value, "unit": unit, "n_gpus": 1, "steps": K, "warmup": Wm,
