@@ -1,5 +1,6 @@
 """CPU oracle (fp64) for causal linear attention, its non-causal and decode
-forms, and the fast-weight delta rule.
+forms, the same forms with other feature maps (DPFP-nu, degree-2 polynomial),
+the fast-weight delta rule and the softmax decode baseline.
 
 TEST INFRASTRUCTURE ONLY: the test suite, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package; the GPU library
@@ -61,6 +62,13 @@ def _load():
             lib.oracle_decode_step.argtypes = [_D, _D, _D, _i64, _i64, _i64, _D, _D, _D]
             lib.oracle_deltanet.argtypes = [_D, _D, _D, _D, _i64, _i64, _i64, _i64, _D, _D, _D]
             lib.oracle_softmax_decode.argtypes = [_D, _D, _D, _i64, _i64, _i64, _i64, _i64, _D]
+            lib.oracle_fmap_dim.restype = _i64
+            lib.oracle_fmap_dim.argtypes = [ctypes.c_int, ctypes.c_int, _i64]
+            lib.oracle_fmap.argtypes = [_D, _i64, ctypes.c_int, ctypes.c_int, _D]
+            lib.oracle_fmap_causal.argtypes = [_D, _D, _D, _i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int,
+                                               _D, _D, _D, _D, _D]
+            lib.oracle_fmap_noncausal.argtypes = [_D, _D, _D, _i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int,
+                                                  _D, _D, _D]
             _lib = lib
     return _lib
 
@@ -207,6 +215,57 @@ def softmax_decode(q, k, v, Kc, Vc, L):
     o = np.empty((B, H, M))
     _load().oracle_softmax_decode(_p(q), _p(Kc), _p(Vc), B * H, L, Lmax, D, M, _p(o))
     return o, Kc, Vc
+
+
+# Feature maps other than elu + 1 (the C oracle's fmap codes).
+DPFP = 1   # DPFP-nu, C = 2 nu D  ([FWP], the DPFP paragraph and its figure)
+POLY2 = 2  # degree-2 polynomial, C = D^2  ([TR] §3.2.1)
+
+
+def fmap_dim(fmap: int, nu: int, D: int) -> int:
+    """Feature dimension C of the map (0 for an unknown map)."""
+    return int(_load().oracle_fmap_dim(int(fmap), int(nu), int(D)))
+
+
+def feature_map(x, fmap: int, nu: int = 0):
+    """phi(x) for every row of x [..., D]; returns float64 [..., C]."""
+    x = f64(x)
+    D = x.shape[-1]
+    C = fmap_dim(fmap, nu, D)
+    rows = np.ascontiguousarray(x.reshape(-1, D))
+    out = np.empty((rows.shape[0], C))
+    lib = _load()
+    for r in range(rows.shape[0]):
+        lib.oracle_fmap(_p(rows[r]), D, int(fmap), int(nu), _p(out[r]))
+    return out.reshape(x.shape[:-1] + (C,))
+
+
+def fmap_causal(q, k, v, fmap: int, nu: int = 0, S0=None, z0=None, want_output=True):
+    """Recurrent causal form, eq.(10)-(12), with the feature map ``fmap``.
+    Returns (o or None [B,H,N,M], S [B,H,C,M], z [B,H,C]) float64."""
+    q, k, v, B, H, N, D, M = _split4(q, k, v)
+    C = fmap_dim(fmap, nu, D)
+    S0, z0 = f64(S0), f64(z0)
+    if S0 is not None:
+        assert S0.shape == (B, H, C, M) and z0.shape == (B, H, C)
+    o = np.empty((B, H, N, M)) if want_output else None
+    S = np.empty((B, H, C, M))
+    z = np.empty((B, H, C))
+    _load().oracle_fmap_causal(_p(q), _p(k), _p(v), B * H, N, D, M, int(fmap), int(nu), _p(S0), _p(z0),
+                               _p(o), _p(S), _p(z))
+    return o, S, z
+
+
+def fmap_noncausal(q, k, v, fmap: int, nu: int = 0):
+    """Non-causal form, eq.(5)-(6), with the feature map ``fmap``.
+    Returns (o [B,H,N,M], S [B,H,C,M], z [B,H,C]) float64."""
+    q, k, v, B, H, N, D, M = _split4(q, k, v)
+    C = fmap_dim(fmap, nu, D)
+    o = np.empty((B, H, N, M))
+    S = np.empty((B, H, C, M))
+    z = np.empty((B, H, C))
+    _load().oracle_fmap_noncausal(_p(q), _p(k), _p(v), B * H, N, D, M, int(fmap), int(nu), _p(o), _p(S), _p(z))
+    return o, S, z
 
 
 from .gradients import causal_bwd  # noqa: E402  (fp64 autograd of the forward definition)

@@ -1,6 +1,7 @@
 /*
  * CPU oracle for causal linear attention, its non-causal and RNN (decode) forms,
- * and the fast-weight delta rule.
+ * the same forms with other feature maps, the fast-weight delta rule and the
+ * softmax decode baseline.
  *
  * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the CPU
  * baseline leg of the benchmark may load this library.  The GPU library never
@@ -19,6 +20,11 @@
  *         Programmers" (Schlag, Irie, Schmidhuber, 2021): the paragraphs on the
  *         capacity limit, on the new update rule ("改進與更新") and on
  *         normalisation ("歸一化").
+ *
+ * The oracle_fmap_* functions repeat the causal and non-causal forms with the
+ * other feature maps the pages name: DPFP-nu ([FWP], the DPFP paragraph) and
+ * the degree-2 polynomial map ([TR] §3.2.1); the definitions are stated above
+ * oracle_fmap_dim.
  *
  * The softmax decode step (oracle_softmax_decode) is the comparison baseline the
  * first page measures the recurrent form against: softmax attention, [TR] §3.1
@@ -318,5 +324,120 @@ void oracle_softmax_decode(const double* q, const double* Kc, const double* Vc, 
       o[h * M + m] = acc / tot;
     }
     free(w);
+  }
+}
+
+/* ---- Other feature maps ---------------------------------------------------
+ * [TR] §3.2.1 allows any feature map phi: R^D -> R^C in place of elu + 1; the
+ * cost becomes O(N C M).  Two maps the pages name are built:
+ *
+ * fmap = 1, DPFP-nu ([FWP], the DPFP paragraph and the figure it describes:
+ *   a deterministic, parameter-free map that raises the dot-product dimension;
+ *   in two dimensions each input has one non-zero output among four, and the
+ *   four quadrants land on mutually orthogonal directions).  The formula is
+ *   not printed; the reading taken is
+ *     r = (relu(x_0..x_{D-1}), relu(-x_0..-x_{D-1}))              in R^{2D},
+ *     phi(x)_{(n-1) 2D + i} = r_i * r_{(i + n) mod 2D},  i < 2D,  n = 1..nu,
+ *   so C = 2 nu D.
+ * fmap = 2, degree-2 polynomial kernel ([TR] §3.2.1: an exact finite feature
+ *   map, cost O(N D^2 M)): phi(x)_{a D + b} = x_a x_b, C = D^2, so that
+ *   phi(q).phi(k) = (q.k)^2.
+ *
+ * With phi of dimension C the causal and non-causal forms are eq.(8)-(12) and
+ * eq.(5)-(6) unchanged: S has shape [C, M] and z [C]. */
+
+i64 oracle_fmap_dim(int fmap, int nu, i64 D) {
+  if (fmap == 1) return 2 * (i64)nu * D;
+  if (fmap == 2) return D * D;
+  return 0;
+}
+
+void oracle_fmap(const double* x, i64 D, int fmap, int nu, double* out) {
+  if (fmap == 1) {
+    const i64 R = 2 * D;
+    for (int n = 1; n <= nu; ++n)
+      for (i64 i = 0; i < R; ++i) {
+        const i64 j = (i + n) % R;
+        const double ri = i < D ? (x[i] > 0.0 ? x[i] : 0.0) : (x[i - D] < 0.0 ? -x[i - D] : 0.0);
+        const double rj = j < D ? (x[j] > 0.0 ? x[j] : 0.0) : (x[j - D] < 0.0 ? -x[j - D] : 0.0);
+        out[(n - 1) * R + i] = ri * rj;
+      }
+  } else if (fmap == 2) {
+    for (i64 a = 0; a < D; ++a)
+      for (i64 b = 0; b < D; ++b) out[a * D + b] = x[a] * x[b];
+  }
+}
+
+/* Recurrent causal form, eq.(10)-(12), with the feature map fmap:
+ *   S_i = S_{i-1} + phi(k_i) v_i^T,  z_i = z_{i-1} + phi(k_i),
+ *   o_i = phi(q_i)^T S_i / phi(q_i)^T z_i.
+ * S0/z0 ([BH, C, M], [BH, C]) may be NULL (zero start); o, S_out, z_out may be NULL. */
+void oracle_fmap_causal(const double* q, const double* k, const double* v, i64 BH, i64 N, i64 D, i64 M,
+                        int fmap, int nu, const double* S0, const double* z0,
+                        double* o, double* S_out, double* z_out) {
+  const i64 C = oracle_fmap_dim(fmap, nu, D);
+#pragma omp parallel for schedule(dynamic)
+  for (i64 h = 0; h < BH; ++h) {
+    double* S = (double*)malloc(sizeof(double) * (size_t)(C * M));
+    double* z = (double*)malloc(sizeof(double) * (size_t)C);
+    double* pk = (double*)malloc(sizeof(double) * (size_t)C);
+    double* pq = (double*)malloc(sizeof(double) * (size_t)C);
+    for (i64 e = 0; e < C * M; ++e) S[e] = S0 ? S0[h * C * M + e] : 0.0;
+    for (i64 c = 0; c < C; ++c) z[c] = z0 ? z0[h * C + c] : 0.0;
+    for (i64 i = 0; i < N; ++i) {
+      const double* vi = v + (h * N + i) * M;
+      oracle_fmap(k + (h * N + i) * D, D, fmap, nu, pk);
+      for (i64 c = 0; c < C; ++c)
+        for (i64 m = 0; m < M; ++m) S[c * M + m] += pk[c] * vi[m];
+      for (i64 c = 0; c < C; ++c) z[c] += pk[c];
+      if (o) {
+        oracle_fmap(q + (h * N + i) * D, D, fmap, nu, pq);
+        double den = 0.0;
+        for (i64 c = 0; c < C; ++c) den += pq[c] * z[c];
+        double* oi = o + (h * N + i) * M;
+        for (i64 m = 0; m < M; ++m) {
+          double num = 0.0;
+          for (i64 c = 0; c < C; ++c) num += pq[c] * S[c * M + m];
+          oi[m] = num / den;
+        }
+      }
+    }
+    if (S_out) memcpy(S_out + h * C * M, S, sizeof(double) * (size_t)(C * M));
+    if (z_out) memcpy(z_out + h * C, z, sizeof(double) * (size_t)C);
+    free(S); free(z); free(pk); free(pq);
+  }
+}
+
+/* Non-causal form, eq.(5)-(6), with the feature map fmap: S = sum_j phi(k_j) v_j^T,
+ * z = sum_j phi(k_j) over all N tokens, then o_i = phi(q_i)^T S / phi(q_i)^T z. */
+void oracle_fmap_noncausal(const double* q, const double* k, const double* v, i64 BH, i64 N, i64 D, i64 M,
+                           int fmap, int nu, double* o, double* S_out, double* z_out) {
+  const i64 C = oracle_fmap_dim(fmap, nu, D);
+#pragma omp parallel for schedule(dynamic)
+  for (i64 h = 0; h < BH; ++h) {
+    double* S = (double*)calloc((size_t)(C * M), sizeof(double));
+    double* z = (double*)calloc((size_t)C, sizeof(double));
+    double* p = (double*)malloc(sizeof(double) * (size_t)C);
+    for (i64 j = 0; j < N; ++j) {
+      const double* vj = v + (h * N + j) * M;
+      oracle_fmap(k + (h * N + j) * D, D, fmap, nu, p);
+      for (i64 c = 0; c < C; ++c)
+        for (i64 m = 0; m < M; ++m) S[c * M + m] += p[c] * vj[m];
+      for (i64 c = 0; c < C; ++c) z[c] += p[c];
+    }
+    for (i64 i = 0; i < N; ++i) {
+      oracle_fmap(q + (h * N + i) * D, D, fmap, nu, p);
+      double den = 0.0;
+      for (i64 c = 0; c < C; ++c) den += p[c] * z[c];
+      double* oi = o + (h * N + i) * M;
+      for (i64 m = 0; m < M; ++m) {
+        double num = 0.0;
+        for (i64 c = 0; c < C; ++c) num += p[c] * S[c * M + m];
+        oi[m] = num / den;
+      }
+    }
+    if (S_out) memcpy(S_out + h * C * M, S, sizeof(double) * (size_t)(C * M));
+    if (z_out) memcpy(z_out + h * C, z, sizeof(double) * (size_t)C);
+    free(S); free(z); free(p);
   }
 }

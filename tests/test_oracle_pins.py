@@ -533,3 +533,151 @@ def test_softmax_decode_dominant_key_and_scaling():
     others = [j for j in range(L + 1) if j != 3]
     expect = (3.0 * V2[0, 0, 3] + V2[0, 0, others].sum(axis=0)) / 9.0
     assert np.abs(o[0, 0] - expect).max() < 1e-12
+
+
+# ------------------------------------------------ other feature maps
+# [TR] §3.2.1: any feature map phi of dimension C; the degree-2 polynomial
+# kernel has an exact one with C = D^2.  [FWP] DPFP paragraph: DPFP-nu raises
+# the dot-product dimension to 2 nu D (formula not printed; reading in the
+# oracle's header).
+
+FMAPS = [(oracle.DPFP, 1), (oracle.DPFP, 2), (oracle.DPFP, 3), (oracle.POLY2, 0)]
+FM_GOLD = json.load(open(os.path.join(HERE, "golden", "feature_maps.json")))
+
+
+def _sim_fn(fmap, nu):
+    if fmap == oracle.DPFP:
+        return lambda a, b: brute.dpfp_sim(a, b, nu)
+    return brute.poly2_sim
+
+
+@pytest.mark.parametrize("case", FM_GOLD["dpfp"], ids=lambda c: c["name"])
+def test_dpfp_golden(case):
+    got = oracle.feature_map(np.array(case["x"]), oracle.DPFP, case["nu"])
+    assert np.array_equal(got, np.array(case["phi"]))
+
+
+@pytest.mark.parametrize("case", FM_GOLD["poly2"], ids=lambda c: c["name"])
+def test_poly2_golden(case):
+    got = oracle.feature_map(np.array(case["x"]), oracle.POLY2)
+    assert np.array_equal(got, np.array(case["phi"]))
+
+
+@pytest.mark.parametrize("case", FM_GOLD["causal"], ids=lambda c: c["name"])
+def test_fmap_causal_golden(case):
+    fmap = oracle.DPFP if case["fmap"] == "dpfp" else oracle.POLY2
+    q, k, v = (np.array(case[x])[None, None] for x in ("q", "k", "v"))
+    o, _, _ = oracle.fmap_causal(q, k, v, fmap, case["nu"])
+    np.testing.assert_allclose(o[0, 0], np.array(case["o"]), rtol=1e-14, atol=0)
+
+
+def test_fmap_dimensions():
+    for D in (2, 3, 32, 64):
+        for nu in (1, 2, 3):
+            assert oracle.fmap_dim(oracle.DPFP, nu, D) == 2 * nu * D
+        assert oracle.fmap_dim(oracle.POLY2, 0, D) == D * D
+    assert oracle.fmap_dim(7, 1, 64) == 0
+
+
+def test_poly2_closed_form():
+    # phi(q).phi(k) = (q.k)^2: numpy's dot, squared, against the feature vectors
+    for D, seed in ((5, 1), (32, 2), (64, 3)):
+        q, k = rnd((8, D), seed), rnd((8, D), seed + 10)
+        fq, fk = oracle.feature_map(q, oracle.POLY2), oracle.feature_map(k, oracle.POLY2)
+        expect = np.einsum("id,jd->ij", q, k) ** 2
+        np.testing.assert_allclose(fq @ fk.T, expect, rtol=1e-12, atol=1e-12)
+
+
+def test_dpfp_properties():
+    x = rnd((50, 6), 4)
+    for nu in (1, 2, 3):
+        f = oracle.feature_map(x, oracle.DPFP, nu)
+        assert f.shape == (50, 12 * nu) and (f >= 0).all()
+        # degree-2 homogeneity for c > 0
+        np.testing.assert_allclose(oracle.feature_map(2.5 * x, oracle.DPFP, nu), 6.25 * f, rtol=1e-14)
+        # x -> -x swaps the two halves of r: each 2D block turns by D
+        fneg = oracle.feature_map(-x, oracle.DPFP, nu)
+        blocks = f.reshape(50, nu, 12)
+        np.testing.assert_array_equal(fneg.reshape(50, nu, 12), np.roll(blocks, -6, axis=2))
+        # DPFP-nu extends DPFP-(nu-1)
+        if nu > 1:
+            np.testing.assert_array_equal(f[:, :12 * (nu - 1)], oracle.feature_map(x, oracle.DPFP, nu - 1))
+    # the figure: a generic 2-d point has exactly one non-zero of four, and the
+    # non-zero slot is its quadrant, so points in different quadrants are orthogonal
+    p = rnd((200, 2), 5)
+    f = oracle.feature_map(p, oracle.DPFP, 1)
+    assert ((f > 0).sum(axis=1) == 1).all()
+    quad = np.where(p[:, 0] > 0, np.where(p[:, 1] > 0, 0, 3), np.where(p[:, 1] > 0, 1, 2))
+    assert np.array_equal(f.argmax(axis=1), quad)
+    np.testing.assert_allclose(f.max(axis=1), np.abs(p[:, 0] * p[:, 1]), rtol=1e-15)
+
+
+def test_dpfp_pair_sum_agrees_with_features():
+    # the pair-sum form of the brute force against the feature vectors of the C oracle
+    q, k = rnd((6, 5), 6), rnd((6, 5), 7)
+    for nu in (1, 2, 3):
+        fq, fk = oracle.feature_map(q, oracle.DPFP, nu), oracle.feature_map(k, oracle.DPFP, nu)
+        for i in range(6):
+            for j in range(6):
+                assert abs(fq[i] @ fk[j] - brute.dpfp_sim(list(q[i]), list(k[j]), nu)) < 1e-12
+
+
+@pytest.mark.parametrize("fmap,nu", FMAPS)
+def test_fmap_causal_and_noncausal_match_bruteforce(fmap, nu):
+    B, H, N, D, M = 1, 2, 7, 4, 3
+    q, k, v = rnd((B, H, N, D), 8), rnd((B, H, N, D), 9), rnd((B, H, N, M), 10)
+    if fmap == oracle.DPFP:
+        q, k = np.abs(q) + 0.1, np.abs(k) + 0.1  # one quadrant: no all-zero weight row
+    o, S, z = oracle.fmap_causal(q, k, v, fmap, nu)
+    onc, Snc, znc = oracle.fmap_noncausal(q, k, v, fmap, nu)
+    for h in range(H):
+        args = ([list(r) for r in q[0, h]], [list(r) for r in k[0, h]], [list(r) for r in v[0, h]])
+        ref = np.array(brute.attention(*args, causal=True, sim_fn=_sim_fn(fmap, nu)))
+        refnc = np.array(brute.attention(*args, causal=False, sim_fn=_sim_fn(fmap, nu)))
+        assert np.abs(o[0, h] - ref).max() < 1e-12
+        assert np.abs(onc[0, h] - refnc).max() < 1e-12
+    # the last causal row sees every key; both forms end in the same state
+    np.testing.assert_allclose(o[:, :, -1], onc[:, :, -1], rtol=1e-12)
+    np.testing.assert_allclose(S, Snc, rtol=1e-12)
+    np.testing.assert_allclose(z, znc, rtol=1e-12)
+
+
+@pytest.mark.parametrize("fmap,nu", FMAPS)
+def test_fmap_state_split_and_sums(fmap, nu):
+    B, H, N, D, M = 2, 1, 20, 4, 5
+    q, k, v = rnd((B, H, N, D), 11), rnd((B, H, N, D), 12), rnd((B, H, N, M), 13)
+    o, S, z = oracle.fmap_causal(q, k, v, fmap, nu)
+    fk = oracle.feature_map(k, fmap, nu)
+    # S = phi(K)^T V and z = column sums of phi(K) (numpy matmul)
+    np.testing.assert_allclose(S, np.swapaxes(fk, -1, -2) @ v, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(z, fk.sum(axis=2), rtol=1e-12, atol=1e-12)
+    # carrying the state across a split reproduces the whole sequence
+    m = 9
+    o1, S1, z1 = oracle.fmap_causal(q[:, :, :m], k[:, :, :m], v[:, :, :m], fmap, nu)
+    o2, S2, z2 = oracle.fmap_causal(q[:, :, m:], k[:, :, m:], v[:, :, m:], fmap, nu, S0=S1, z0=z1)
+    np.testing.assert_allclose(np.concatenate([o1, o2], axis=2), o, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(S2, S, rtol=1e-12, atol=1e-12)
+
+
+def test_fmap_invariances():
+    B, H, N, D, M = 1, 2, 12, 6, 4
+    q, k, v = rnd((B, H, N, D), 14), rnd((B, H, N, D), 15), rnd((B, H, N, M), 16)
+    # polynomial: (q.k)^2 is even in q and scales as c^2 in every key
+    o, _, _ = oracle.fmap_causal(q, k, v, oracle.POLY2)
+    flip = np.where(np.arange(N)[None, None, :, None] % 2 == 0, -q, q)
+    o2, _, _ = oracle.fmap_causal(flip, 3.0 * k, v, oracle.POLY2)
+    np.testing.assert_allclose(o2, o, rtol=1e-10, atol=1e-12)
+    # DPFP: negating every q and k permutes both feature vectors alike; positive
+    # scaling of q cancels between numerator and denominator
+    qa, ka = np.abs(q) * np.sign(q[..., :1]), np.abs(k) * np.sign(q[..., :1])  # shared sign pattern
+    for nu in (1, 2, 3):
+        o, _, _ = oracle.fmap_causal(qa, ka, v, oracle.DPFP, nu)
+        o2, _, _ = oracle.fmap_causal(-2.0 * qa, -ka, v, oracle.DPFP, nu)
+        np.testing.assert_allclose(o2, o, rtol=1e-10, atol=1e-12)
+    # outputs are convex combinations of the values seen so far
+    for fmap, nu in FMAPS:
+        qa2, ka2 = (np.abs(q), np.abs(k)) if fmap == oracle.DPFP else (q, k)
+        o, _, _ = oracle.fmap_causal(qa2, ka2, v, fmap, nu)
+        lo = np.minimum.accumulate(v, axis=2)
+        hi = np.maximum.accumulate(v, axis=2)
+        assert (o >= lo - 1e-12).all() and (o <= hi + 1e-12).all()
