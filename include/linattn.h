@@ -13,6 +13,8 @@
  *   - causal backward: dq, dk, dv of the causal form (§3.3.1);
  *   - decode step: one step of the RNN form, state updated first and then read
  *                  (§3.4 eq.(16)-(20), without f_l and the residual);
+ *   - other feature maps: the causal and non-causal forms with DPFP-nu or the
+ *                  degree-2 polynomial map in place of elu + 1 (§3.2.1);
  *   - delta rule:  the fast-weight memory W (M x D) of "Linear Transformers Are
  *                  Secretly Fast Weight Programmers" (Schlag et al. 2021; news
  *                  summary, paragraphs on the update rule and normalisation):
@@ -154,6 +156,46 @@ int linattn_decode_step(const void* q, const void* k, const void* v, void* o,
 int softmax_decode_step(const void* q, const void* k, const void* v, void* o,
                         void* Kc, void* Vc, int B, int H, int L, int Lmax,
                         int D, int M, int dtype, void* stream);
+
+/* Feature maps other than elu + 1 for linattn_fmap_fwd. */
+typedef enum { LINATTN_FMAP_DPFP = 1, LINATTN_FMAP_POLY2 = 2 } linattn_fmap_t;
+
+/* Feature dimension C of a map: 2 nu D for LINATTN_FMAP_DPFP (nu = 1, 2 or 3),
+ * D^2 for LINATTN_FMAP_POLY2 (nu = 0); 0 for an unsupported map, nu or D. */
+int linattn_fmap_dim(int fmap, int nu, int D);
+
+/* Bytes of device workspace linattn_fmap_fwd needs (0 when none, or for invalid
+ * arguments, which the call then rejects). */
+size_t linattn_fmap_workspace_bytes(int B, int H, int N, int D, int M, int dtype, int fmap, int nu);
+
+/* Linear attention with another feature map phi: R^D -> R^C ("Transformers are
+ * RNNs", translated page, §3.2.1: any map of dimension C gives O(N C M) work):
+ *   LINATTN_FMAP_DPFP, order nu in {1, 2, 3} (DPFP-nu of "Linear Transformers
+ *     Are Secretly Fast Weight Programmers", news summary, DPFP paragraph;
+ *     the formula is not printed there, this is the reading built):
+ *     r = (relu(x), relu(-x)) in R^{2D},
+ *     phi(x)_{(n-1) 2D + i} = r_i r_{(i+n) mod 2D},  i < 2D,  n = 1..nu;
+ *   LINATTN_FMAP_POLY2, nu = 0 (degree-2 polynomial kernel, §3.2.1):
+ *     phi(x)_{a D + b} = x_a x_b, so phi(q).phi(k) = (q.k)^2.
+ * causal != 0: eq.(9)-(12) with this phi (inclusive mask), from the initial
+ *   state (S0, z0) ([B,H,C,M] and [B,H,C] float32; both NULL means zero).
+ * causal == 0: eq.(5)-(6) over all N keys; S0 and z0 must be NULL
+ *   (LINATTN_ERR_UNSUPPORTED otherwise).
+ * o:            [B,H,N,M] output, or NULL to compute the final state only.
+ * S_out, z_out: the final (causal) or total (non-causal) state, [B,H,C,M] and
+ *               [B,H,C] float32, or both NULL.  S_out may equal S0 (and z_out z0).
+ * ws, ws_bytes: device workspace of at least linattn_fmap_workspace_bytes();
+ *               contents need no initialisation and are clobbered.
+ * Products and sums are float32 for both dtypes.  No epsilon is added: a row
+ * whose weights are all zero (possible with DPFP when no query-key pair shares
+ * an active pair of components) gives 0/0 = NaN.
+ * Errors as for linattn_causal_fwd; an unknown fmap or nu is
+ * LINATTN_ERR_UNSUPPORTED.  o must not overlap q, k, v, S0, z0, S_out, z_out or
+ * ws. */
+int linattn_fmap_fwd(const void* q, const void* k, const void* v, void* o,
+                     int B, int H, int N, int D, int M, int dtype, int fmap, int nu, int causal,
+                     const float* S0, const float* z0, float* S_out, float* z_out,
+                     void* ws, size_t ws_bytes, void* stream);
 
 /* Delta-rule fast-weight memory over a sequence, for every (b, h), i = 1..N:
  *   kh = phi(k_i)/sum_c phi(k_i)_c,  qh = phi(q_i)/sum_c phi(q_i)_c,

@@ -48,6 +48,8 @@ WORKLOADS = {
     "decode": Workload("decode", 256, 16, 512, 64, 64, torch.bfloat16, 1.0, 1004, steps=1024),
     "deltanet": Workload("deltanet", 4, 8, 4096, 64, 64, torch.float32, 1.0, 1005),
     "deltanet_decode": Workload("deltanet_decode", 256, 16, 512, 64, 64, torch.bfloat16, 1.0, 1006, steps=1024),
+    # other feature maps (DPFP-nu, degree-2 polynomial) at the fast-weight page's d_key = 64
+    "fmap": Workload("fmap", 4, 8, 4096, 64, 64, torch.float32, 1.0, 1007),
 }
 
 

@@ -247,3 +247,43 @@ def test_softmax_decode_validation(lib):
     bad = list(args); bad[0] = Q + 8
     assert f(*bad) == ALIGN
     assert f(None, None, None, None, None, None, 0, 16, 0, 1, 64, 64, 1, None) == OK
+
+
+def fmapc(lib, q=Q, k=K, v=V, o=O, B=1, H=2, N=4096, D=64, M=64, dt=1, fm=1, nu=1, causal=1, s0=None, z0=None,
+          so=None, zo=None, ws=WSP, wsb=1 << 34):
+    return lib.linattn_fmap_fwd(q, k, v, o, B, H, N, D, M, dt, fm, nu, causal, s0, z0, so, zo, ws, wsb, None)
+
+
+def test_fmap_dims(lib):
+    assert lib.linattn_fmap_dim(1, 1, 64) == 128 and lib.linattn_fmap_dim(1, 3, 32) == 192
+    assert lib.linattn_fmap_dim(2, 0, 64) == 4096 and lib.linattn_fmap_dim(2, 0, 32) == 1024
+    for fm, nu, D in ((1, 0, 64), (1, 4, 64), (2, 1, 64), (3, 1, 64), (0, 0, 64), (1, 1, 48)):
+        assert lib.linattn_fmap_dim(fm, nu, D) == 0
+    # workspace: block records plus the totals; 0 for unsupported maps
+    assert lib.linattn_fmap_workspace_bytes(1, 2, 4096, 64, 64, 1, 1, 1) > 0
+    assert lib.linattn_fmap_workspace_bytes(1, 2, 4096, 64, 64, 1, 1, 4) == 0
+    assert lib.linattn_fmap_workspace_bytes(1, 2, 4096, 64, 48, 1, 2, 0) == 0
+
+
+@no_gpu
+def test_fmap_validation(lib):
+    assert fmapc(lib, fm=3) == UNSUP
+    assert fmapc(lib, nu=0) == UNSUP
+    assert fmapc(lib, fm=2, nu=1) == UNSUP
+    assert fmapc(lib, causal=0, s0=S0, z0=Z0) == UNSUP  # no initial state in the non-causal form
+    assert fmapc(lib, dt=2) == DTYPE
+    assert fmapc(lib, D=48) == UNSUP
+    assert fmapc(lib, N=-1) == SHAPE
+    assert fmapc(lib, k=None) == NULL
+    assert fmapc(lib, s0=S0) == NULL
+    assert fmapc(lib, q=Q + 8) == ALIGN
+    assert fmapc(lib, ws=None) == WS
+    need = lib.linattn_fmap_workspace_bytes(1, 2, 4096, 64, 64, 1, 1, 1)
+    assert fmapc(lib, wsb=need - 1) == WS
+    assert fmapc(lib, o=K + 64) == ALIAS
+    assert fmapc(lib, so=V, zo=ZO) == ALIAS
+    assert fmapc(lib, s0=S0, z0=Z0, so=S0 + 16, zo=ZO) == ALIAS
+    assert fmapc(lib, ws=Q) == ALIAS
+    # nothing to compute
+    assert fmapc(lib, B=0) == OK
+    assert fmapc(lib, q=None, k=None, v=None, o=None, N=0, ws=None, wsb=0) == OK

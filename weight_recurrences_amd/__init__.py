@@ -6,7 +6,8 @@ tensors' device.  torch provides device memory and streams, nothing else.
 
 Method: "Transformers are RNNs" (Katharopoulos et al., 2020), translated page
 "線性變換器" — phi = elu + 1 (§3.2.1 eq.(7)), causal form eq.(9)-(12),
-non-causal form eq.(5)-(6), RNN step eq.(16)-(20); delta-rule fast-weight
+non-causal form eq.(5)-(6), RNN step eq.(16)-(20), other feature maps
+(§3.2.1: degree-2 polynomial; DPFP-nu from the fast-weight summary); delta-rule fast-weight
 memory from the news summary of "Linear Transformers Are Secretly Fast Weight
 Programmers" (Schlag et al., 2021), update-rule and normalisation paragraphs.
 """
@@ -14,9 +15,9 @@ from __future__ import annotations
 
 import torch
 
-from ._lib import BF16, F32, LinAttnError, check, load
+from ._lib import BF16, F32, FMAP_DPFP, FMAP_POLY2, LinAttnError, check, load
 
-__all__ = ["causal", "causal_bwd", "causal_bwd_workspace_bytes", "noncausal", "decode_step", "deltanet", "deltanet_decode_step", "causal_workspace_bytes",
+__all__ = ["causal", "causal_bwd", "fmap", "fmap_dim", "fmap_workspace_bytes", "FMAP_DPFP", "FMAP_POLY2", "causal_bwd_workspace_bytes", "noncausal", "decode_step", "deltanet", "deltanet_decode_step", "causal_workspace_bytes",
            "noncausal_workspace_bytes", "deltanet_workspace_bytes", "LinAttnError", "abi_version"]
 
 _DT = {torch.float32: F32, torch.bfloat16: BF16}
@@ -105,6 +106,59 @@ def causal(q, k, v, *, state=None, return_state=False, output=True, out=None, wo
     rc = lib.linattn_causal_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, D, M, dt,
                                 _ptr(S0), _ptr(z0), _ptr(S), _ptr(z), _ptr(ws), need, _stream(dev))
     check(rc, "linattn_causal_fwd")
+    if not output:
+        return S, z
+    return (o, (S, z)) if return_state else o
+
+
+def fmap_dim(fmap: int, nu: int, D: int) -> int:
+    """Feature dimension C of DPFP-nu (2 nu D) or the polynomial map (D^2); 0 if unsupported."""
+    return int(load().linattn_fmap_dim(int(fmap), int(nu), int(D)))
+
+
+def fmap_workspace_bytes(B, H, N, D, M, dtype, fmap, nu=0) -> int:
+    return int(load().linattn_fmap_workspace_bytes(B, H, N, D, M, _DT[dtype], int(fmap), int(nu)))
+
+
+def fmap(q, k, v, feature_map, nu=0, *, causal=True, state=None, return_state=False, output=True, out=None,
+         workspace=None):
+    """Linear attention with another feature map (linattn_fmap_fwd):
+    ``feature_map`` is FMAP_DPFP (order ``nu`` in 1..3) or FMAP_POLY2 (nu = 0).
+
+    q, k: [B,H,N,D]; v: [B,H,N,M] (float32 or bfloat16).  causal selects
+    eq.(9)-(12) or eq.(5)-(6).  state: optional (S0 [B,H,C,M], z0 [B,H,C])
+    float32 (causal only).  Returns o, or (o, (S, z)) with return_state; with
+    output=False only the final (or total) state (S, z).
+    """
+    lib = load()
+    dev = _dev(q, k, v)
+    B, H, N, D = q.shape
+    M = v.shape[-1]
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v shapes/dtypes disagree")
+    dt = _dtype_code(q)
+    C = fmap_dim(feature_map, nu, D)
+    if C == 0:
+        raise LinAttnError(4, "linattn_fmap_fwd")
+    S0 = z0 = None
+    if state is not None:
+        S0, z0 = state
+        _dev(q, S0, z0)
+        if S0.dtype != torch.float32 or z0.dtype != torch.float32 or S0.shape != (B, H, C, M) or z0.shape != (B, H, C):
+            raise ValueError("state must be float32 S [B,H,C,M] and z [B,H,C]")
+    o = None
+    if output:
+        o = out if out is not None else torch.empty((B, H, N, M), dtype=q.dtype, device=dev)
+    S = z = None
+    if return_state or not output:
+        S = torch.empty((B, H, C, M), dtype=torch.float32, device=dev)
+        z = torch.empty((B, H, C), dtype=torch.float32, device=dev)
+    need = int(lib.linattn_fmap_workspace_bytes(B, H, N, D, M, dt, int(feature_map), int(nu)))
+    ws = _workspace(need, dev, workspace)
+    rc = lib.linattn_fmap_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, D, M, dt, int(feature_map), int(nu),
+                              1 if causal else 0, _ptr(S0), _ptr(z0), _ptr(S), _ptr(z), _ptr(ws), need,
+                              _stream(dev))
+    check(rc, "linattn_fmap_fwd")
     if not output:
         return S, z
     return (o, (S, z)) if return_state else o

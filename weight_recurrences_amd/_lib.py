@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(PKG, "liblinattn.so")
 HEADER = os.path.join(ROOT, "include", "linattn.h")
 
 F32, BF16 = 0, 1
+FMAP_DPFP, FMAP_POLY2 = 1, 2  # linattn_fmap_t
 STATUS = {
     0: "LINATTN_OK", 1: "LINATTN_ERR_NULL", 2: "LINATTN_ERR_SHAPE", 3: "LINATTN_ERR_DTYPE",
     4: "LINATTN_ERR_UNSUPPORTED", 5: "LINATTN_ERR_ALIGN", 6: "LINATTN_ERR_ALIAS",
@@ -41,6 +42,10 @@ SIGNATURES = {
     "deltanet_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "deltanet_decode_step": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
     "softmax_decode_step": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
+    "linattn_fmap_dim": (_i, [_i, _i, _i]),
+    "linattn_fmap_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
+    "linattn_fmap_fwd": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i,
+                              _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "linattn_status_str": (ctypes.c_char_p, [_i]),
     "linattn_abi_version": (_i, []),
 }

@@ -195,6 +195,69 @@ int softmax_decode_step(const void* q, const void* k, const void* v, void* o, vo
                                               (hipStream_t)stream));
 }
 
+int linattn_fmap_dim(int fmap, int nu, int D) {
+  if (D != 32 && D != 64) return 0;
+  if (fmap == LINATTN_FMAP_DPFP && nu >= 1 && nu <= 3) return la::featmap_dim(nu, D);
+  if (fmap == LINATTN_FMAP_POLY2 && nu == 0) return la::featmap_dim(4, D);
+  return 0;
+}
+
+}  // extern "C"
+
+namespace {
+// Internal map code of the kernels: DPFP-nu is nu (1..3), the polynomial map 4; 0 if unsupported.
+int fmap_code(int fmap, int nu) {
+  if (fmap == LINATTN_FMAP_DPFP && nu >= 1 && nu <= 3) return nu;
+  if (fmap == LINATTN_FMAP_POLY2 && nu == 0) return 4;
+  return 0;
+}
+}  // namespace
+
+extern "C" {
+
+size_t linattn_fmap_workspace_bytes(int B, int H, int N, int D, int M, int dtype, int fmap, int nu) {
+  if (check_shape(B, H, N, D, M, dtype) != LINATTN_OK) return 0;
+  const int code = fmap_code(fmap, nu);
+  if (!code) return 0;
+  return la::featmap_ws_bytes(code, B * H, N, D, M);
+}
+
+int linattn_fmap_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int D, int M,
+                     int dtype, int fmap, int nu, int causal, const float* S0, const float* z0, float* S_out,
+                     float* z_out, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_shape(B, H, N, D, M, dtype);
+  if (st) return st;
+  const int code = fmap_code(fmap, nu);
+  if (!code) return LINATTN_ERR_UNSUPPORTED;
+  if (!causal && (S0 || z0)) return LINATTN_ERR_UNSUPPORTED;
+  const long long BH = (long long)B * H, es = esize(dtype), C = la::featmap_dim(code, D);
+  const long long nq = BH * N * D * es, nv = BH * N * M * es;
+  if ((S0 == nullptr) != (z0 == nullptr)) return LINATTN_ERR_NULL;
+  if ((S_out == nullptr) != (z_out == nullptr)) return LINATTN_ERR_NULL;
+  if (BH * N > 0 && (!q || !k || !v)) return LINATTN_ERR_NULL;
+  if ((st = check_align({q, k, v, o, S0, z0, S_out, z_out, ws}))) return st;
+  if (BH * ((N + 63) / 64) * (C / 64) > (long long)INT32_MAX) return LINATTN_ERR_SHAPE;  // grid sizes
+  const size_t need = la::featmap_ws_bytes(code, (int)BH, N, D, M);
+  if (need > 0 && (!ws || ws_bytes < need)) return LINATTN_ERR_WORKSPACE;
+  const Span sq(q, nq), sk(k, nq), sv(v, nv), so(o, o ? nv : 0);
+  const Span sS0(S0, BH * C * M * 4), sz0(z0, BH * C * 4), sSo(S_out, BH * C * M * 4), szo(z_out, BH * C * 4);
+  const Span sws(ws, (long long)need);
+  for (const Span& x : {sq, sk, sv, sS0, sz0, sSo, szo, sws})
+    if (so.overlaps(x)) return LINATTN_ERR_ALIAS;
+  for (const Span& out : {sSo, szo})
+    for (const Span& x : {sq, sk, sv, sws})
+      if (out.overlaps(x)) return LINATTN_ERR_ALIAS;
+  if (sSo.overlaps(szo)) return LINATTN_ERR_ALIAS;
+  if ((sSo.overlaps(sS0) && !sSo.same(sS0)) || (szo.overlaps(sz0) && !szo.same(sz0))) return LINATTN_ERR_ALIAS;
+  if (sSo.overlaps(sz0) || szo.overlaps(sS0)) return LINATTN_ERR_ALIAS;
+  for (const Span& x : {sq, sk, sv, sS0, sz0})
+    if (sws.overlaps(x)) return LINATTN_ERR_ALIAS;
+  if (BH == 0) return LINATTN_OK;
+  if (N == 0 && !S_out) return LINATTN_OK;
+  return hip_status(la::launch_featmap(code, q, k, v, o, (int)BH, N, D, M, dtype == LINATTN_BF16, causal ? 1 : 0,
+                                       S0, z0, S_out, z_out, ws, (hipStream_t)stream));
+}
+
 size_t deltanet_workspace_bytes(int B, int H, int N, int D, int M, int dtype) {
   if (check_shape(B, H, N, D, M, dtype) != LINATTN_OK) return 0;
   return la::deltanet_ws_bytes(B * H, N, D, M);

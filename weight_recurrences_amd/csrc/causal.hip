@@ -796,6 +796,21 @@ hipError_t launch_block_prefix(const void* k, const void* v, int BH, int N, int 
   }
 }
 
+hipError_t launch_state_scan(float* agg, float* aggz, int BHs, int nblk, int DM, int D, const float* S_init,
+                             const float* z_init, float* S_tot, float* z_tot, int exclusive, hipStream_t stream) {
+  const dim3 sgrid((unsigned)((DM + D + NT - 1) / NT) * (unsigned)BHs);
+  hipLaunchKernelGGL(state_scan_kernel, sgrid, dim3(NT), 0, stream, agg, aggz, nblk, DM, D, S_init, z_init, S_tot,
+                     z_tot, exclusive);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_copy(const float* S_init, const float* z_init, float* S_out, float* z_out, long long nS,
+                             long long nz, hipStream_t stream) {
+  const unsigned nb = (unsigned)(((nS > nz ? nS : nz) + NT - 1) / NT);
+  hipLaunchKernelGGL(state_copy_kernel, dim3(nb), dim3(NT), 0, stream, S_init, z_init, S_out, z_out, nS, nz);
+  return hipGetLastError();
+}
+
 // bf16 causal calls take the single-pass kernel unless LINATTN_CAUSAL_BF16_PATH=blocked
 // selects the three-kernel path (kept for comparisons).
 static bool bf16_fused() {

@@ -1,0 +1,376 @@
+// Linear attention with the other feature maps the pages name, on gfx950:
+// DPFP-nu and the degree-2 polynomial map.
+//
+// "Transformers are RNNs" (Katharopoulos et al., 2020), translated page
+// "線性變換器", §3.2.1: a feature map phi of dimension C makes attention
+// O(N C M) work, and the degree-2 polynomial kernel has an exact map with
+// C = D^2.  News summary of "Linear Transformers Are Secretly Fast Weight
+// Programmers", DPFP paragraph: a deterministic, parameter-free map that raises
+// the dot-product dimension to 2 nu D.  The maps (the DPFP formula is not
+// printed; this is the reading taken):
+//   DPFP-nu: r = (relu(x), relu(-x)) in R^{2D},
+//            phi(x)_{(n-1) 2D + i} = r_i r_{(i+n) mod 2D},  n = 1..nu;
+//   POLY2:   phi(x)_{a D + b} = x_a x_b,  so phi(q).phi(k) = (q.k)^2.
+// The attention is eq.(8)-(12) (causal) and eq.(5)-(6) (non-causal) with phi.
+//
+// Work split.  The C features are cut into slices of FS = 64; a slice of phi is
+// itself a feature map, and numerator and denominator are sums over slices.
+//   1. fm_state_kernel (head, block of tblk tokens, slice s): the block's state
+//      increment dS_s = phi_s(K)^T V, dz_s = column sums of phi_s(K).
+//   2. the block scan of the elu + 1 path: exclusive prefix per block (causal)
+//      or the total (non-causal), starting from S0.
+//   3. fm_out_kernel (head, chunk of 64 queries):
+//        num_i = sum_s phi_s(q_i)^T S_s + sum_{j in block, j <= i} sim(q_i, k_j) v_j
+//        den_i = sum_s phi_s(q_i)^T z_s + sum_{j in block, j <= i} sim(q_i, k_j)
+//      with (S_s, z_s) the prefix state at the block start, o_i = num_i / den_i.
+//      DPFP: the block is the chunk (tblk = 64) and sim is summed slice by slice
+//      from the features.  POLY2: sim = (q.k)^2 from a D-long dot product, so
+//      blocks hold several chunks and fewer prefix states are written.
+// Products run on fp32 MFMA (v_mfma_f32_16x16x4_f32) with fp32 features; bf16
+// inputs are widened on load and outputs are rounded to the input dtype.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace la {
+namespace fm {
+
+constexpr int NT = 256;  // threads per workgroup (4 waves)
+constexpr int CH = 64;   // tokens per chunk
+constexpr int FS = 64;   // features per slice
+constexpr int POLY2 = 4; // template code of the polynomial map; DPFP-nu is coded nu (1..3)
+
+template <int FM, int D>
+constexpr int fdim() {
+  return FM == POLY2 ? D * D : 2 * FM * D;
+}
+
+// Feature c of phi(x) for a row x of D floats (in LDS).
+template <int FM, int D>
+__device__ __forceinline__ float feature(const float* x, int c) {
+  if constexpr (FM == POLY2) {
+    return x[c / D] * x[c % D];
+  } else {
+    constexpr int R = 2 * D;
+    const int n = c / R + 1, i = c % R, j = (i + n) % R;
+    const float xi = x[i < D ? i : i - D], xj = x[j < D ? j : j - D];
+    const float ri = i < D ? (xi > 0.f ? xi : 0.f) : (xi < 0.f ? -xi : 0.f);
+    const float rj = j < D ? (xj > 0.f ? xj : 0.f) : (xj < 0.f ? -xj : 0.f);
+    return ri * rj;
+  }
+}
+
+// F[r][f] = phi_{s FS + f}(X[r]) for the 64 rows of a chunk; each thread makes 16
+// features of one row.  X has row stride XS floats, F row stride FSP.
+template <int FM, int D, int XS, int FSP>
+__device__ __forceinline__ void build_phi(float* F, const float* X, int s, int tid) {
+  const int r = tid >> 2, f0 = (tid & 3) * 16;
+  const float* x = X + r * XS;
+  float* out = F + r * FSP + f0;
+#pragma unroll
+  for (int e = 0; e < 16; e += 4) {
+    const int c = s * FS + f0 + e;
+    *reinterpret_cast<float4*>(out + e) =
+        float4{feature<FM, D>(x, c), feature<FM, D>(x, c + 1), feature<FM, D>(x, c + 2), feature<FM, D>(x, c + 3)};
+  }
+}
+
+// Rows [0, nv) of a row-major [.][W] tensor starting at src, widened to float
+// into LDS (row stride DS floats); rows nv..63 become zeros.
+template <typename T, int W, int DS>
+__device__ __forceinline__ void load_rows(float* dst, const T* src, int nv, int tid) {
+  constexpr int G = CH * W / 4;  // groups of four elements
+  static_assert(G % NT == 0, "whole groups per thread");
+#pragma unroll
+  for (int u = 0; u < G / NT; ++u) {
+    const int e = (u * NT + tid) * 4, r = e / W, c = e % W;
+    const float4 x = r < nv ? load4<T>(src + (size_t)r * W + c) : float4{0.f, 0.f, 0.f, 0.f};
+    *reinterpret_cast<float4*>(dst + r * DS + c) = x;
+  }
+}
+
+// ---- 1. block state increments ---------------------------------------------
+// grid: BH * nblk * NS, blockIdx.x = (bh * nblk + blk) * NS + s.
+// agg [BH * NS][nblk][FS][M], aggz [BH * NS][nblk][FS].
+template <typename T, int D, int M, int FM>
+__global__ __launch_bounds__(NT) void fm_state_kernel(const T* __restrict__ k, const T* __restrict__ v, int N,
+                                                      int tblk, int nblk, float* __restrict__ agg,
+                                                      float* __restrict__ aggz) {
+  constexpr int NS = fdim<FM, D>() / FS, TM = M / 16;
+  // Strides: rows read by k-slot g step 16 banks (FSA, VS), raw rows 4 banks (KS).
+  constexpr int KS = D + 4, FSA = FS + 16, VS = M + 16;
+  __shared__ float Kr[CH * KS];
+  __shared__ float Fk[CH * FSA];
+  __shared__ float Vs[CH * VS];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
+  const int s = blockIdx.x % NS, rest = blockIdx.x / NS, blk = rest % nblk, bh = rest / nblk;
+  const int t0 = blk * tblk, t1 = min(N, t0 + tblk);
+  const T* kh = k + (size_t)bh * N * D;
+  const T* vh = v + (size_t)bh * N * M;
+  f32x4 acc[TM];
+#pragma unroll
+  for (int vb = 0; vb < TM; ++vb) acc[vb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float zacc = 0.f;
+  for (int c0 = t0; c0 < t1; c0 += CH) {
+    const int nv = min(CH, t1 - c0);
+    __syncthreads();  // the previous chunk's readers are done
+    load_rows<T, D, KS>(Kr, kh + (size_t)c0 * D, nv, tid);
+    load_rows<T, M, VS>(Vs, vh + (size_t)c0 * M, nv, tid);
+    __syncthreads();
+    build_phi<FM, D, KS, FSA>(Fk, Kr, s, tid);
+    __syncthreads();
+    // dS^T tile rows = features 16w.., columns = values; k-slot = token.
+#pragma unroll 4
+    for (int t = 0; t < CH / 4; ++t) {
+      const float a = Fk[(4 * t + g) * FSA + 16 * w + n];
+#pragma unroll
+      for (int vb = 0; vb < TM; ++vb) acc[vb] = mma(a, Vs[(4 * t + g) * VS + 16 * vb + n], acc[vb]);
+    }
+    if (tid < FS) {
+      float zs = 0.f;
+      for (int r = 0; r < CH; ++r) zs += Fk[r * FSA + tid];
+      zacc += zs;
+    }
+  }
+  // acc[vb]: lane (n, g) holds features 16w + 4g + i of value column 16 vb + n.
+  const size_t rec = (size_t)(bh * NS + s) * nblk + blk;
+  float* S = agg + rec * FS * M;
+#pragma unroll
+  for (int vb = 0; vb < TM; ++vb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) S[(16 * w + 4 * g + i) * M + 16 * vb + n] = acc[vb][i];
+  if (tid < FS) aggz[rec * FS + tid] = zacc;
+}
+
+// ---- 3. outputs --------------------------------------------------------------
+template <int D, int M, int FM>
+struct OutSmem {
+  static constexpr int XS = D + 4, FQ = FS + 4, VS = M + 4, SS = M + 16;
+  float Qr[CH * XS];                       // raw queries of the chunk
+  float Kr[CH * XS];                       // raw keys of the current key chunk
+  float Fq[CH * FQ];                       // phi_s(Q)
+  float Fk[FM == POLY2 ? 4 : CH * FQ];     // phi_s(K) (DPFP only)
+  float Vs[CH * VS];                       // values of the current key chunk
+  float Ss[FS * SS];                       // prefix state slice S_s
+  float zs[FS];                            // prefix z slice
+};
+
+// grid: BH * nqc, blockIdx.x = bh * nqc + qc (nqc = ceil(N / 64) query chunks).
+// pre/prez: causal, the exclusive block prefixes [BH * NS][nblk][FS][M] / [FS];
+// non-causal, the totals [BH * NS][FS][M] / [FS].
+template <typename T, int D, int M, int FM>
+__global__ __launch_bounds__(NT) void fm_out_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                    const T* __restrict__ v, T* __restrict__ o, int N, int tblk,
+                                                    int nblk, const float* __restrict__ pre,
+                                                    const float* __restrict__ prez, int causal) {
+  using SM = OutSmem<D, M, FM>;
+  constexpr int NS = fdim<FM, D>() / FS, TM = M / 16;
+  constexpr int XS = SM::XS, FQ = SM::FQ, VS = SM::VS, SS = SM::SS;
+  __shared__ SM sm;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
+  const int nqc = (N + CH - 1) / CH;
+  const int qc = blockIdx.x % nqc, bh = blockIdx.x / nqc;
+  const int q0 = qc * CH, nq = min(CH, N - q0);
+  const int blk = causal ? q0 / tblk : 0, npre = causal ? nblk : 1;
+  const T* qh = q + (size_t)bh * N * D;
+  const T* kh = k + (size_t)bh * N * D;
+  const T* vh = v + (size_t)bh * N * M;
+  const float* Sb = pre + ((size_t)bh * NS * npre + blk) * FS * M;  // slice s at + s * npre * FS * M
+  const float* zb = prez + ((size_t)bh * NS * npre + blk) * FS;
+
+  load_rows<T, D, XS>(sm.Qr, qh + (size_t)q0 * D, nq, tid);
+  if constexpr (FM != POLY2) {
+    if (causal) {  // the block is this chunk: its keys and values
+      load_rows<T, D, XS>(sm.Kr, kh + (size_t)q0 * D, nq, tid);
+      load_rows<T, M, VS>(sm.Vs, vh + (size_t)q0 * M, nq, tid);
+    }
+  }
+  f32x4 num[TM];  // num^T tiles: lane (n, g) holds values 16 vb + 4g + i of query 16w + n
+#pragma unroll
+  for (int vb = 0; vb < TM; ++vb) num[vb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;  // partial over the features (or keys) this lane's k-slots cover
+
+  for (int s = 0; s < NS; ++s) {
+    __syncthreads();  // raw rows stored; the previous slice's readers are done
+    const float* Ssrc = Sb + (size_t)s * npre * FS * M;
+#pragma unroll
+    for (int u = 0; u < FS * M / 4 / NT; ++u) {
+      const int e = (u * NT + tid) * 4, f = e / M, c = e % M;
+      *reinterpret_cast<float4*>(&sm.Ss[f * SS + c]) = *reinterpret_cast<const float4*>(Ssrc + e);
+    }
+    if (tid < FS) sm.zs[tid] = zb[(size_t)s * npre * FS + tid];
+    build_phi<FM, D, XS, FQ>(sm.Fq, sm.Qr, s, tid);
+    if constexpr (FM != POLY2) {
+      if (causal) build_phi<FM, D, XS, FQ>(sm.Fk, sm.Kr, s, tid);
+    }
+    __syncthreads();
+    // Inter-block part: num^T += S_s^T phi_s(Q)^T, den += phi_s(Q) z_s.
+#pragma unroll 4
+    for (int t = 0; t < FS / 4; ++t) {
+      const float b = sm.Fq[(16 * w + n) * FQ + 4 * t + g];
+      den += b * sm.zs[4 * t + g];
+#pragma unroll
+      for (int vb = 0; vb < TM; ++vb) num[vb] = mma(sm.Ss[(4 * t + g) * SS + 16 * vb + n], b, num[vb]);
+    }
+    if constexpr (FM != POLY2) {
+      // Intra-chunk part of this slice: A^T = phi_s(K) phi_s(Q)^T (keys x queries),
+      // keys after the query masked; num^T += V^T A^T.  Key tiles above the
+      // wave's queries are all masked and skipped.
+      if (causal) {
+        for (int kb = 0; kb <= w; ++kb) {
+          f32x4 a{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+          for (int t = 0; t < FS / 4; ++t)
+            a = mma(sm.Fk[(16 * kb + n) * FQ + 4 * t + g], sm.Fq[(16 * w + n) * FQ + 4 * t + g], a);
+          if (kb == w) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (4 * g + i > n) a[i] = 0.f;
+          }
+          den += a[0] + a[1] + a[2] + a[3];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int vb = 0; vb < TM; ++vb)
+              num[vb] = mma(sm.Vs[(16 * kb + 4 * g + i) * VS + 16 * vb + n], a[i], num[vb]);
+        }
+      }
+    }
+  }
+
+  if constexpr (FM == POLY2) {
+    // Intra-block part: sim = (q.k)^2 for the block's keys up to this chunk.
+    if (causal) {
+      for (int kc0 = blk * tblk; kc0 <= q0; kc0 += CH) {
+        const int nk = min(CH, N - kc0);
+        __syncthreads();  // the previous key chunk's readers are done
+        load_rows<T, D, XS>(sm.Kr, kh + (size_t)kc0 * D, nk, tid);
+        load_rows<T, M, VS>(sm.Vs, vh + (size_t)kc0 * M, nk, tid);
+        __syncthreads();
+        const bool diag = kc0 == q0;
+        const int kbmax = diag ? w : 3;
+        for (int kb = 0; kb <= kbmax; ++kb) {
+          f32x4 a{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int t = 0; t < D / 4; ++t)
+            a = mma(sm.Kr[(16 * kb + n) * XS + 4 * t + g], sm.Qr[(16 * w + n) * XS + 4 * t + g], a);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) a[i] *= a[i];
+          if (diag && kb == w) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (4 * g + i > n) a[i] = 0.f;
+          }
+          den += a[0] + a[1] + a[2] + a[3];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int vb = 0; vb < TM; ++vb)
+              num[vb] = mma(sm.Vs[(16 * kb + 4 * g + i) * VS + 16 * vb + n], a[i], num[vb]);
+        }
+      }
+    }
+  }
+
+  den += __shfl_xor(den, 16);
+  den += __shfl_xor(den, 32);
+  if (16 * w + n < nq) {
+    T* orow = o + ((size_t)bh * N + q0 + 16 * w + n) * M + 4 * g;
+#pragma unroll
+    for (int vb = 0; vb < TM; ++vb)
+      store4<T>(orow + 16 * vb, float4{num[vb][0] / den, num[vb][1] / den, num[vb][2] / den, num[vb][3] / den});
+  }
+}
+
+// Tokens per block: the chunk for DPFP (its intra-block similarity is built from
+// the features, slice by slice); 256 for the polynomial map (intra-block
+// similarity from D-long dot products, fewer prefix states).
+template <int FM>
+static int block_tokens(int N) {
+  if constexpr (FM != POLY2) {
+    return CH;
+  } else {
+    const int cap = ((N + CH - 1) / CH) * CH;
+    return cap < 256 ? (cap > 0 ? cap : CH) : 256;
+  }
+}
+
+template <int FM>
+static size_t ws_bytes_t(int BH, int N, int D, int M) {
+  const int C = FM == POLY2 ? D * D : 2 * FM * D;
+  const int NS = C / FS;
+  const int tblk = block_tokens<FM>(N);
+  const size_t nblk = (size_t)((N + tblk - 1) / tblk);
+  // block records, then the totals of the non-causal form
+  return ((size_t)BH * NS * nblk * (FS * M + FS) + (size_t)BH * C * (M + 1)) * sizeof(float);
+}
+
+template <typename T, int D, int M, int FM>
+static hipError_t impl(const void* q, const void* k, const void* v, void* o, int BH, int N, int causal,
+                       const float* S0, const float* z0, float* S_out, float* z_out, void* ws, hipStream_t stream) {
+  constexpr int C = fdim<FM, D>(), NS = C / FS;
+  static_assert(C % FS == 0, "whole feature slices");
+  if (N == 0) {
+    if (S_out) return launch_state_copy(S0, z0, S_out, z_out, (long long)BH * C * M, (long long)BH * C, stream);
+    return hipSuccess;
+  }
+  const int tblk = block_tokens<FM>(N);
+  const int nblk = (N + tblk - 1) / tblk;
+  float* agg = (float*)ws;
+  float* aggz = agg + (size_t)BH * NS * nblk * FS * M;
+  float* Stot = aggz + (size_t)BH * NS * nblk * FS;
+  float* ztot = Stot + (size_t)BH * C * M;
+  hipLaunchKernelGGL((fm_state_kernel<T, D, M, FM>), dim3((unsigned)BH * (unsigned)nblk * (unsigned)NS), dim3(NT),
+                     0, stream, (const T*)k, (const T*)v, N, tblk, nblk, agg, aggz);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  float* St = S_out ? S_out : (causal ? nullptr : Stot);
+  float* zt = S_out ? z_out : (causal ? nullptr : ztot);
+  e = launch_state_scan(agg, aggz, BH * NS, nblk, FS * M, FS, S0, z0, St, zt, causal, stream);
+  if (e != hipSuccess || !o) return e;
+  const int nqc = (N + CH - 1) / CH;
+  hipLaunchKernelGGL((fm_out_kernel<T, D, M, FM>), dim3((unsigned)BH * (unsigned)nqc), dim3(NT), 0, stream,
+                     (const T*)q, (const T*)k, (const T*)v, (T*)o, N, tblk, nblk, causal ? agg : St,
+                     causal ? aggz : zt, causal);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int M>
+static hipError_t fm_entry(int map, const void* q, const void* k, const void* v, void* o, int BH, int N, int causal,
+                           const float* S0, const float* z0, float* S_out, float* z_out, void* ws,
+                           hipStream_t stream) {
+  switch (map) {
+    case 1: return impl<T, D, M, 1>(q, k, v, o, BH, N, causal, S0, z0, S_out, z_out, ws, stream);
+    case 2: return impl<T, D, M, 2>(q, k, v, o, BH, N, causal, S0, z0, S_out, z_out, ws, stream);
+    case 3: return impl<T, D, M, 3>(q, k, v, o, BH, N, causal, S0, z0, S_out, z_out, ws, stream);
+    case POLY2: return impl<T, D, M, POLY2>(q, k, v, o, BH, N, causal, S0, z0, S_out, z_out, ws, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace fm
+
+// map: 1..3 = DPFP-nu, 4 = degree-2 polynomial.
+int featmap_dim(int map, int D) { return map == fm::POLY2 ? D * D : (map >= 1 && map <= 3 ? 2 * map * D : 0); }
+
+size_t featmap_ws_bytes(int map, int BH, int N, int D, int M) {
+  if (BH <= 0 || N <= 0) return 0;
+  switch (map) {
+    case 1: return fm::ws_bytes_t<1>(BH, N, D, M);
+    case 2: return fm::ws_bytes_t<2>(BH, N, D, M);
+    case 3: return fm::ws_bytes_t<3>(BH, N, D, M);
+    case fm::POLY2: return fm::ws_bytes_t<fm::POLY2>(BH, N, D, M);
+    default: return 0;
+  }
+}
+
+hipError_t launch_featmap(int map, const void* q, const void* k, const void* v, void* o, int BH, int N, int D,
+                          int M, int bf16, int causal, const float* S0, const float* z0, float* S_out, float* z_out,
+                          void* ws, hipStream_t stream) {
+  if (bf16) {
+    LA_DISPATCH_DM(fm::fm_entry, bf16_t, map, q, k, v, o, BH, N, causal, S0, z0, S_out, z_out, ws, stream)
+  } else {
+    LA_DISPATCH_DM(fm::fm_entry, float, map, q, k, v, o, BH, N, causal, S0, z0, S_out, z_out, ws, stream)
+  }
+}
+
+}  // namespace la

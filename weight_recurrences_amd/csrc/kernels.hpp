@@ -58,6 +58,21 @@ hipError_t launch_causal_bwd_bf16(const void* q, const void* k, const void* v, c
                                   float* inv, float* b, float* suf, hipStream_t stream);
 // In-place exclusive suffix sums of per-block records of SZ floats (fixed order).
 hipError_t launch_suffix_scan(float* suf, int BH, int nblk, int SZ, hipStream_t stream);
+// Block scan of state records [BHs][nblk][DM] / [BHs][nblk][D]: exclusive prefix in
+// place when exclusive != 0, starting from (S_init, z_init) (NULL: zero); the
+// totals go to (S_tot, z_tot) when non-NULL.
+hipError_t launch_state_scan(float* agg, float* aggz, int BHs, int nblk, int DM, int D, const float* S_init,
+                             const float* z_init, float* S_tot, float* z_tot, int exclusive, hipStream_t stream);
+// (S_out, z_out) <- (S_init, z_init), or zeros when S_init is NULL.
+hipError_t launch_state_copy(const float* S_init, const float* z_init, float* S_out, float* z_out, long long nS,
+                             long long nz, hipStream_t stream);
+// Linear attention with another feature map (map 1..3 = DPFP-nu, 4 = degree-2
+// polynomial), causal or not; feature dimension and workspace.
+int featmap_dim(int map, int D);
+size_t featmap_ws_bytes(int map, int BH, int N, int D, int M);
+hipError_t launch_featmap(int map, const void* q, const void* k, const void* v, void* o, int BH, int N, int D,
+                          int M, int bf16, int causal, const float* S0, const float* z0, float* S_out, float* z_out,
+                          void* ws, hipStream_t stream);
 hipError_t launch_decode(const void* q, const void* k, const void* v, void* o, float* S, float* z, int BH, int D,
                          int M, int bf16, hipStream_t stream);
 hipError_t launch_deltanet(const void* q, const void* k, const void* v, const void* beta, void* o, int BH, int N,
