@@ -7,7 +7,9 @@ accumulation and state, B=2 H=16 N=32768 D=M=64 — one step is one full
 Other workloads (``--workload``): noncausal_long, decode (prefill + 1024
 single-token steps on 256x16 states), deltanet, deltanet_decode (the same for the
 delta-rule memory), softmax_decode (the same steps as softmax attention over a
-key/value cache, the comparison baseline), causal_mid, and copy (a 1 GiB device copy that calibrates
+key/value cache, the comparison baseline), fmap_dpfp1/2/3 and fmap_poly2 (causal
+linear attention with the DPFP-nu or degree-2 polynomial feature map, fp32,
+B=4 H=8 N=4096 D=M=64), causal_mid, and copy (a 1 GiB device copy that calibrates
 the HBM counters).
 
 Prints ONE JSON line.  Inputs are synthetic (seeded N(0,1), the recipe of the
@@ -51,7 +53,13 @@ WORKLOAD_SOURCES = {
     "deltanet": ["deltanet.hip", "deltanet_chunk.hip", "common.hpp"],
     "deltanet_decode": ["deltanet.hip", "common.hpp"],
     "softmax_decode": ["softmax_decode.hip", "common.hpp"],
+    "fmap_dpfp1": ["featmap.hip", "causal.hip", "common.hpp"],
+    "fmap_dpfp2": ["featmap.hip", "causal.hip", "common.hpp"],
+    "fmap_dpfp3": ["featmap.hip", "causal.hip", "common.hpp"],
+    "fmap_poly2": ["featmap.hip", "causal.hip", "common.hpp"],
 }
+# feature-map workloads: (linattn_fmap_t, nu)
+FMAPS = {"fmap_dpfp1": (1, 1), "fmap_dpfp2": (1, 2), "fmap_dpfp3": (1, 3), "fmap_poly2": (2, 0)}
 
 
 def source_hash(workload: str = None) -> str:
@@ -114,6 +122,21 @@ def time_oracle(workload, inputs, budget_s: float = 20.0):
         return {"value": nh * (w.N + T) / dt, "unit": "head-tokens/s", "cores": threads, "kind": "oracle",
                 "sample": f"prefill {w.N} tokens + {T} of {w.steps} steps on all {nh} states, {dt:.1f} s, "
                           f"{cpu_model()}"}
+    if w.name == "fmap":  # another feature map: one head, then as many heads as the budget allows
+        q, k, v, _, fm, nu = inputs
+        omap = {1: oracle.DPFP, 2: oracle.POLY2}[fm]
+        nh_all = w.B * w.H
+        q, k, v = (t.reshape(1, nh_all, w.N, -1) for t in (q, k, v))
+        t0 = time.perf_counter()
+        oracle.fmap_causal(q[:, :1], k[:, :1], v[:, :1], omap, nu)
+        one = time.perf_counter() - t0
+        nh = max(1, min(nh_all, int(budget_s * threads / max(one, 1e-6))))
+        nh = min(nh_all, max(threads, nh // threads * threads)) if nh >= threads else nh
+        t0 = time.perf_counter()
+        oracle.fmap_causal(q[:, :nh], k[:, :nh], v[:, :nh], omap, nu)
+        dt = time.perf_counter() - t0
+        return {"value": nh * w.N / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                "sample": f"{nh} of {nh_all} heads, all {w.N} tokens, {dt:.1f} s, {cpu_model()}"}
     if w.name == "causal_long" and len(inputs) == 4:  # backward: one head, then as many as the budget allows
         import torch
         from oracle import gradients
@@ -204,7 +227,7 @@ def main():
                          "the GPU's clocks to settle; a few launches after idle run up to 15%% slower)")
     ap.add_argument("--workload", default="causal_long",
                     choices=["causal_long", "causal_bwd_long", "noncausal_long", "decode", "deltanet", "deltanet_decode",
-                             "softmax_decode",
+                             "softmax_decode", *FMAPS,
                              "causal_mid", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--oracle-budget", type=float, default=20.0)
@@ -257,7 +280,7 @@ def main():
         return
 
     wname = {"noncausal_long": "causal_long", "causal_bwd_long": "causal_long",
-             "softmax_decode": "decode"}.get(args.workload, args.workload)
+             "softmax_decode": "decode", **{f: "fmap" for f in FMAPS}}.get(args.workload, args.workload)
     w = synth.WORKLOADS[wname]
     inputs = synth.workload_inputs(w)
     K, Wm = args.steps, args.warmup
@@ -281,6 +304,18 @@ def main():
         units = w.B * w.H * w.N                      # tokens per step
         es = torch.tensor([], dtype=w.dtype).element_size()
         alg_bytes = units * (2 * w.D + 2 * w.M) * es  # read q, k, v; write o
+        unit = "tokens/s"
+        launches_per_step = 1
+    elif args.workload in FMAPS:
+        fm, nu = FMAPS[args.workload]
+        q, k, v = (t.to(dev) for t in inputs)
+        o = torch.empty(w.B, w.H, w.N, w.M, dtype=w.dtype, device=dev)
+        ws = torch.empty(max(1, la.fmap_workspace_bytes(w.B, w.H, w.N, w.D, w.M, w.dtype, fm, nu)),
+                         dtype=torch.uint8, device=dev)
+        step = lambda: la.fmap(q, k, v, fm, nu, out=o, workspace=ws)
+        kernel = "linattn_fmap_fwd (fm_state_kernel + state_scan_kernel + fm_out_kernel)"
+        units = w.B * w.H * w.N
+        alg_bytes = units * (2 * w.D + 2 * w.M) * 4
         unit = "tokens/s"
         launches_per_step = 1
     elif args.workload == "causal_bwd_long":
@@ -420,6 +455,17 @@ def main():
         lin_ms = a.elapsed_time(b) / K
         roofline["linear_decode_same_inputs"] = {"ms_per_step": round(lin_ms, 4),
                                                   "softmax_over_linear_time": round(ms_per_step / lin_ms, 2)}
+    if args.workload in FMAPS:
+        # The recurrent form's arithmetic with C features: S update 2CM, numerator
+        # 2CM, z C, denominator 2C, the map itself C.  fp32 matrix work dominates.
+        C = la.fmap_dim(fm, nu, w.D)
+        flops = units * (4 * C * w.M + 4 * C)
+        tflops = flops / (launch_ms / 1e3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(tflops, 3), "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tflops / FP32_PEAK_TFLOPS, 4), "traffic": traffic, "kernel": kernel,
+                    "algorithmic_flops_per_launch": flops, "feature_dim": C, "launch_ms": round(launch_ms, 5),
+                    "hbm": {"achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                            "frac": round(achieved / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": alg_bytes}}
     if args.workload == "deltanet":
         flops = units * (6 * w.D * w.M + 6 * w.D)
         roofline["alu"] = {"achieved_tflops": round(flops / (launch_ms / 1e3) / 1e12, 3),
@@ -427,8 +473,10 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = time_oracle(w, tuple(inputs) + (("softmax",) if args.workload == "softmax_decode" else ()),
-                          args.oracle_budget)
+        extra = ("softmax",) if args.workload == "softmax_decode" else ()
+        if args.workload in FMAPS:
+            extra = ("fmap",) + FMAPS[args.workload]
+        cpu = time_oracle(w, tuple(inputs) + extra, args.oracle_budget)
 
     names = {
         "causal_long": f"causal_long: causal linear attention (phi=elu+1), bf16 in/out, fp32 state, "
@@ -444,9 +492,13 @@ def main():
                            f"single-token bf16 steps after a {w.N}-token prefill",
         "softmax_decode": f"softmax_decode: softmax attention decode over a key/value cache (comparison baseline), "
                           f"{w.B}x{w.H} heads D=M={w.D}, {w.steps} single-token bf16 steps after a {w.N}-token cache",
+        **{f: f"{f}: causal linear attention with the "
+              f"{'DPFP-%d' % FMAPS[f][1] if FMAPS[f][0] == 1 else 'degree-2 polynomial'} feature map "
+              f"(C={la.fmap_dim(*FMAPS[f], w.D)}), fp32, B={w.B} H={w.H} N={w.N} D=M={w.D}" for f in FMAPS},
     }
     dtype = {"causal_long": "bf16", "causal_bwd_long": "bf16", "noncausal_long": "bf16", "decode": "bf16", "causal_mid": "f32",
-             "deltanet": "f32", "deltanet_decode": "bf16", "softmax_decode": "bf16"}[args.workload]
+             "deltanet": "f32", "deltanet_decode": "bf16", "softmax_decode": "bf16",
+             **{f: "f32" for f in FMAPS}}[args.workload]
     line = {
         "metric": METRIC if args.workload == "causal_long" else f"{args.workload} {unit}",
         "value": value, "unit": unit, "n_gpus": 1, "steps": K, "warmup": Wm,
