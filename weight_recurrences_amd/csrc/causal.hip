@@ -631,7 +631,21 @@ __global__ __launch_bounds__(NT) void state_scan_kernel(float* agg, float* aggz,
   float* base = (isz ? aggz : agg) + (size_t)bh * nblk * len + x;
   const float* init = isz ? z_init : S_init;
   float run = init ? init[(size_t)bh * len + x] : 0.f;
-  for (int b = 0; b < nblk; ++b) {
+  // Eight records per round are loaded before any is written, so the loads are
+  // in flight together; the sums still run in block order.
+  constexpr int U = 8;
+  int b = 0;
+  for (; b + U <= nblk; b += U) {
+    float t[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) t[u] = base[(size_t)(b + u) * len];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (exclusive) base[(size_t)(b + u) * len] = run;
+      run += t[u];
+    }
+  }
+  for (; b < nblk; ++b) {
     const float t = base[(size_t)b * len];
     if (exclusive) base[(size_t)b * len] = run;
     run += t;

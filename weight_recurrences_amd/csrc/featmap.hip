@@ -28,6 +28,8 @@
 //      blocks hold several chunks and fewer prefix states are written.
 // Products run on fp32 MFMA (v_mfma_f32_16x16x4_f32) with fp32 features; bf16
 // inputs are widened on load and outputs are rounded to the input dtype.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -59,19 +61,18 @@ __device__ __forceinline__ float feature(const float* x, int c) {
   }
 }
 
-// F[r][f] = phi_{s FS + f}(X[r]) for the 64 rows of a chunk; each thread makes 16
-// features of one row.  X has row stride XS floats, F row stride FSP.
-template <int FM, int D, int XS, int FSP>
-__device__ __forceinline__ void build_phi(float* F, const float* X, int s, int tid) {
-  const int r = tid >> 2, f0 = (tid & 3) * 16;
-  const float* x = X + r * XS;
-  float* out = F + r * FSP + f0;
-#pragma unroll
-  for (int e = 0; e < 16; e += 4) {
-    const int c = s * FS + f0 + e;
-    *reinterpret_cast<float4*>(out + e) =
-        float4{feature<FM, D>(x, c), feature<FM, D>(x, c + 1), feature<FM, D>(x, c + 2), feature<FM, D>(x, c + 3)};
-  }
+// DPFP feature c = s FS + 4t + g of a raw row x (D floats), with the slice's
+// terms hoisted: base = (s FS) mod 2D and gn = g + n, n the order the slice
+// belongs to.  Then i = base + 4t + g and j = i + n (mod 2D); r_i is relu(x) on
+// the first half of r and relu(-x) on the second, so the half is bit D of the
+// index and the component is the index mod D.
+template <int D>
+__device__ __forceinline__ float dpfp_feat(const float* x, int t, int base_g, int base_gn) {
+  const int i = base_g + 4 * t, e = base_gn + 4 * t;
+  const float xi = x[i & (D - 1)], xj = x[e & (D - 1)];
+  const float ri = fmaxf((i & D) ? -xi : xi, 0.f);
+  const float rj = fmaxf((e & D) ? -xj : xj, 0.f);
+  return ri * rj;
 }
 
 // Rows [0, nv) of a row-major [.][W] tensor starting at src, widened to float
@@ -89,84 +90,108 @@ __device__ __forceinline__ void load_rows(float* dst, const T* src, int nv, int 
 }
 
 // ---- 1. block state increments ---------------------------------------------
-// grid: BH * nblk * NS, blockIdx.x = (bh * nblk + blk) * NS + s.
+// grid: BH * nblk * (NS / SG), blockIdx.x = (bh * nblk + blk) * (NS / SG) + sg;
+// the workgroup covers slices sg*SG .. sg*SG + SG - 1 of one block, so the
+// block's keys and values are read once for SG slices.
 // agg [BH * NS][nblk][FS][M], aggz [BH * NS][nblk][FS].
+// Tile: rows = the 16 features 16w.. of the slice, columns = values, k-slot =
+// token; features are formed from the raw key rows as the operand is read, and
+// the lane's operands also give its share of z (tokens 4t + g).
+template <int NS>
+constexpr int slice_group() {
+  return NS <= 8 ? NS : 8;
+}
+
 template <typename T, int D, int M, int FM>
 __global__ __launch_bounds__(NT) void fm_state_kernel(const T* __restrict__ k, const T* __restrict__ v, int N,
                                                       int tblk, int nblk, float* __restrict__ agg,
                                                       float* __restrict__ aggz) {
-  constexpr int NS = fdim<FM, D>() / FS, TM = M / 16;
-  // Strides: rows read by k-slot g step 16 banks (FSA, VS), raw rows 4 banks (KS).
-  constexpr int KS = D + 4, FSA = FS + 16, VS = M + 16;
+  constexpr int NS = fdim<FM, D>() / FS, SG = slice_group<NS>(), TM = M / 16;
+  static_assert(NS % SG == 0, "whole slice groups");
+  // Row strides of 16 banks: the four k-slot groups g read four different rows.
+  constexpr int KS = D + 16, VS = M + 16;
   __shared__ float Kr[CH * KS];
-  __shared__ float Fk[CH * FSA];
   __shared__ float Vs[CH * VS];
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
-  const int s = blockIdx.x % NS, rest = blockIdx.x / NS, blk = rest % nblk, bh = rest / nblk;
+  const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform: its tests are scalar branches
+  const int sg = blockIdx.x % (NS / SG), rest = blockIdx.x / (NS / SG), blk = rest % nblk, bh = rest / nblk;
   const int t0 = blk * tblk, t1 = min(N, t0 + tblk);
   const T* kh = k + (size_t)bh * N * D;
   const T* vh = v + (size_t)bh * N * M;
-  f32x4 acc[TM];
+  f32x4 acc[SG][TM];
+  float zp[SG];
 #pragma unroll
-  for (int vb = 0; vb < TM; ++vb) acc[vb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float zacc = 0.f;
+  for (int j = 0; j < SG; ++j) {
+    zp[j] = 0.f;
+#pragma unroll
+    for (int vb = 0; vb < TM; ++vb) acc[j][vb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   for (int c0 = t0; c0 < t1; c0 += CH) {
     const int nv = min(CH, t1 - c0);
     __syncthreads();  // the previous chunk's readers are done
     load_rows<T, D, KS>(Kr, kh + (size_t)c0 * D, nv, tid);
     load_rows<T, M, VS>(Vs, vh + (size_t)c0 * M, nv, tid);
     __syncthreads();
-    build_phi<FM, D, KS, FSA>(Fk, Kr, s, tid);
-    __syncthreads();
-    // dS^T tile rows = features 16w.., columns = values; k-slot = token.
-#pragma unroll 4
+#pragma unroll 2
     for (int t = 0; t < CH / 4; ++t) {
-      const float a = Fk[(4 * t + g) * FSA + 16 * w + n];
+      const float* kr = Kr + (4 * t + g) * KS;
+      float bv[TM];
 #pragma unroll
-      for (int vb = 0; vb < TM; ++vb) acc[vb] = mma(a, Vs[(4 * t + g) * VS + 16 * vb + n], acc[vb]);
-    }
-    if (tid < FS) {
-      float zs = 0.f;
-      for (int r = 0; r < CH; ++r) zs += Fk[r * FSA + tid];
-      zacc += zs;
+      for (int vb = 0; vb < TM; ++vb) bv[vb] = Vs[(4 * t + g) * VS + 16 * vb + n];
+#pragma unroll
+      for (int j = 0; j < SG; ++j) {
+        const float a = feature<FM, D>(kr, (sg * SG + j) * FS + 16 * w + n);
+        zp[j] += a;
+#pragma unroll
+        for (int vb = 0; vb < TM; ++vb) acc[j][vb] = mma(a, bv[vb], acc[j][vb]);
+      }
     }
   }
-  // acc[vb]: lane (n, g) holds features 16w + 4g + i of value column 16 vb + n.
-  const size_t rec = (size_t)(bh * NS + s) * nblk + blk;
-  float* S = agg + rec * FS * M;
+  // acc[j][vb]: lane (n, g) holds features 16w + 4g + i of value column 16 vb + n.
 #pragma unroll
-  for (int vb = 0; vb < TM; ++vb)
+  for (int j = 0; j < SG; ++j) {
+    const size_t rec = (size_t)(bh * NS + sg * SG + j) * nblk + blk;
+    float* S = agg + rec * FS * M;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) S[(16 * w + 4 * g + i) * M + 16 * vb + n] = acc[vb][i];
-  if (tid < FS) aggz[rec * FS + tid] = zacc;
+    for (int vb = 0; vb < TM; ++vb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[(16 * w + 4 * g + i) * M + 16 * vb + n] = acc[j][vb][i];
+    float z = zp[j];
+    z += __shfl_xor(z, 16);
+    z += __shfl_xor(z, 32);
+    if (g == 0) aggz[rec * FS + 16 * w + n] = z;
+  }
 }
 
 // ---- 3. outputs --------------------------------------------------------------
-template <int D, int M, int FM>
+template <int D, int M>
 struct OutSmem {
-  static constexpr int XS = D + 4, FQ = FS + 4, VS = M + 4, SS = M + 16;
-  float Qr[CH * XS];                       // raw queries of the chunk
-  float Kr[CH * XS];                       // raw keys of the current key chunk
-  float Fq[CH * FQ];                       // phi_s(Q)
-  float Fk[FM == POLY2 ? 4 : CH * FQ];     // phi_s(K) (DPFP only)
-  float Vs[CH * VS];                       // values of the current key chunk
-  float Ss[FS * SS];                       // prefix state slice S_s
-  float zs[FS];                            // prefix z slice
+  static constexpr int XS = D + 4, VS = M + 4, SS = M + 16;
+  float Qr[CH * XS];  // raw queries of the chunk
+  float Kr[CH * XS];  // raw keys of the current key chunk
+  float Vs[CH * VS];  // values of the current key chunk
+  float Ss[FS * SS];  // prefix state slice S_s
+  float zs[FS];       // prefix z slice
 };
 
 // grid: BH * nqc, blockIdx.x = bh * nqc + qc (nqc = ceil(N / 64) query chunks).
 // pre/prez: causal, the exclusive block prefixes [BH * NS][nblk][FS][M] / [FS];
 // non-causal, the totals [BH * NS][FS][M] / [FS].
+// Features are formed from the raw rows as MFMA operands are read.  The tiles
+// are transposed, rows = values or keys and columns = the wave's 16 queries,
+// so a score tile is already the B operand of the value product.
 template <typename T, int D, int M, int FM>
 __global__ __launch_bounds__(NT) void fm_out_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                     const T* __restrict__ v, T* __restrict__ o, int N, int tblk,
                                                     int nblk, const float* __restrict__ pre,
                                                     const float* __restrict__ prez, int causal) {
-  using SM = OutSmem<D, M, FM>;
+  using SM = OutSmem<D, M>;
   constexpr int NS = fdim<FM, D>() / FS, TM = M / 16;
-  constexpr int XS = SM::XS, FQ = SM::FQ, VS = SM::VS, SS = SM::SS;
+  constexpr int XS = SM::XS, VS = SM::VS, SS = SM::SS;
+  constexpr int PF = FS * M / 4 / NT;  // float4 groups of a state slice per thread
   __shared__ SM sm;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform: its tests are scalar branches
   const int nqc = (N + CH - 1) / CH;
   const int qc = blockIdx.x % nqc, bh = blockIdx.x / nqc;
   const int q0 = qc * CH, nq = min(CH, N - q0);
@@ -176,56 +201,80 @@ __global__ __launch_bounds__(NT) void fm_out_kernel(const T* __restrict__ q, con
   const T* vh = v + (size_t)bh * N * M;
   const float* Sb = pre + ((size_t)bh * NS * npre + blk) * FS * M;  // slice s at + s * npre * FS * M
   const float* zb = prez + ((size_t)bh * NS * npre + blk) * FS;
+  const size_t sstride = (size_t)npre * FS * M;
+  const bool intra_dpfp = FM != POLY2 && causal;
 
+  // The first state slice is requested before the raw rows, so both are in flight.
+  f32x4 pf[PF];
+#pragma unroll
+  for (int u = 0; u < PF; ++u) pf[u] = *reinterpret_cast<const f32x4*>(Sb + (u * NT + tid) * 4);
+  float pz = tid < FS ? zb[tid] : 0.f;
   load_rows<T, D, XS>(sm.Qr, qh + (size_t)q0 * D, nq, tid);
-  if constexpr (FM != POLY2) {
-    if (causal) {  // the block is this chunk: its keys and values
-      load_rows<T, D, XS>(sm.Kr, kh + (size_t)q0 * D, nq, tid);
-      load_rows<T, M, VS>(sm.Vs, vh + (size_t)q0 * M, nq, tid);
-    }
+  if (intra_dpfp) {  // the block is this chunk: its keys and values
+    load_rows<T, D, XS>(sm.Kr, kh + (size_t)q0 * D, nq, tid);
+    load_rows<T, M, VS>(sm.Vs, vh + (size_t)q0 * M, nq, tid);
   }
   f32x4 num[TM];  // num^T tiles: lane (n, g) holds values 16 vb + 4g + i of query 16w + n
 #pragma unroll
   for (int vb = 0; vb < TM; ++vb) num[vb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 at[4];  // DPFP: score tiles A^T (keys 16 kb.. x the wave's queries), summed over slices
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) at[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
   float den = 0.f;  // partial over the features (or keys) this lane's k-slots cover
+  const float* qrow = sm.Qr + (16 * w + n) * XS;
 
-  for (int s = 0; s < NS; ++s) {
-    __syncthreads();  // raw rows stored; the previous slice's readers are done
-    const float* Ssrc = Sb + (size_t)s * npre * FS * M;
+  // The slice loop is compiled once per wave index W, so the key tiles a wave
+  // scores (kb <= W) are known at compile time and its accumulators stay in place.
+  auto slices = [&](auto wc) {
+    constexpr int W = decltype(wc)::value;
+    for (int s = 0; s < NS; ++s) {
+      __syncthreads();  // raw rows stored; the previous slice's readers are done
 #pragma unroll
-    for (int u = 0; u < FS * M / 4 / NT; ++u) {
-      const int e = (u * NT + tid) * 4, f = e / M, c = e % M;
-      *reinterpret_cast<float4*>(&sm.Ss[f * SS + c]) = *reinterpret_cast<const float4*>(Ssrc + e);
-    }
-    if (tid < FS) sm.zs[tid] = zb[(size_t)s * npre * FS + tid];
-    build_phi<FM, D, XS, FQ>(sm.Fq, sm.Qr, s, tid);
-    if constexpr (FM != POLY2) {
-      if (causal) build_phi<FM, D, XS, FQ>(sm.Fk, sm.Kr, s, tid);
-    }
-    __syncthreads();
-    // Inter-block part: num^T += S_s^T phi_s(Q)^T, den += phi_s(Q) z_s.
+      for (int u = 0; u < PF; ++u) {
+        const int e = (u * NT + tid) * 4, f = e / M, c = e % M;
+        *reinterpret_cast<f32x4*>(&sm.Ss[f * SS + c]) = pf[u];
+      }
+      if (tid < FS) sm.zs[tid] = pz;
+      if (s + 1 < NS) {  // next slice in flight during this one
+#pragma unroll
+        for (int u = 0; u < PF; ++u)
+          pf[u] = *reinterpret_cast<const f32x4*>(Sb + (size_t)(s + 1) * sstride + (u * NT + tid) * 4);
+        if (tid < FS) pz = zb[(size_t)(s + 1) * npre * FS + tid];
+      }
+      __syncthreads();
+      // Inter-block part: num^T += S_s^T phi_s(Q)^T, den += phi_s(Q) z_s; for DPFP
+      // also the slice's share of the chunk's scores.
+      const int base = (s * FS) & (2 * D - 1), order = (s * FS) / (2 * D) + 1;
+      const int base_g = base + g, base_gn = base + g + order;
 #pragma unroll 4
-    for (int t = 0; t < FS / 4; ++t) {
-      const float b = sm.Fq[(16 * w + n) * FQ + 4 * t + g];
-      den += b * sm.zs[4 * t + g];
+      for (int t = 0; t < FS / 4; ++t) {
+        const int c = s * FS + 4 * t + g;
+        float b;
+        if constexpr (FM == POLY2) {
+          b = feature<FM, D>(qrow, c);
+        } else {
+          b = dpfp_feat<D>(qrow, t, base_g, base_gn);
+        }
+        den += b * sm.zs[4 * t + g];
 #pragma unroll
-      for (int vb = 0; vb < TM; ++vb) num[vb] = mma(sm.Ss[(4 * t + g) * SS + 16 * vb + n], b, num[vb]);
+        for (int vb = 0; vb < TM; ++vb) num[vb] = mma(sm.Ss[(4 * t + g) * SS + 16 * vb + n], b, num[vb]);
+        if (intra_dpfp) {
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+            if (kb <= W) at[kb] = mma(dpfp_feat<D>(sm.Kr + (16 * kb + n) * XS, t, base_g, base_gn), b, at[kb]);
+        }
+      }
     }
-    if constexpr (FM != POLY2) {
-      // Intra-chunk part of this slice: A^T = phi_s(K) phi_s(Q)^T (keys x queries),
-      // keys after the query masked; num^T += V^T A^T.  Key tiles above the
-      // wave's queries are all masked and skipped.
-      if (causal) {
-        for (int kb = 0; kb <= w; ++kb) {
-          f32x4 a{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-          for (int t = 0; t < FS / 4; ++t)
-            a = mma(sm.Fk[(16 * kb + n) * FQ + 4 * t + g], sm.Fq[(16 * w + n) * FQ + 4 * t + g], a);
-          if (kb == w) {
+
+    if (intra_dpfp) {
+      // Keys after the query are masked; num^T += V^T A^T, den += column sums of A^T.
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (4 * g + i > n) a[i] = 0.f;
-          }
+      for (int kb = 0; kb < 4; ++kb) {
+        f32x4 a = at[kb];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (kb == W && 4 * g + i > n) a[i] = 0.f;
+        if (kb <= W) {
           den += a[0] + a[1] + a[2] + a[3];
 #pragma unroll
           for (int i = 0; i < 4; ++i)
@@ -234,6 +283,16 @@ __global__ __launch_bounds__(NT) void fm_out_kernel(const T* __restrict__ q, con
               num[vb] = mma(sm.Vs[(16 * kb + 4 * g + i) * VS + 16 * vb + n], a[i], num[vb]);
         }
       }
+    }
+  };
+  if constexpr (FM == POLY2) {
+    slices(std::integral_constant<int, 3>{});  // no DPFP scores: one copy
+  } else {
+    switch (w) {
+      case 0: slices(std::integral_constant<int, 0>{}); break;
+      case 1: slices(std::integral_constant<int, 1>{}); break;
+      case 2: slices(std::integral_constant<int, 2>{}); break;
+      default: slices(std::integral_constant<int, 3>{}); break;
     }
   }
 
@@ -252,7 +311,7 @@ __global__ __launch_bounds__(NT) void fm_out_kernel(const T* __restrict__ q, con
           f32x4 a{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int t = 0; t < D / 4; ++t)
-            a = mma(sm.Kr[(16 * kb + n) * XS + 4 * t + g], sm.Qr[(16 * w + n) * XS + 4 * t + g], a);
+            a = mma(sm.Kr[(16 * kb + n) * XS + 4 * t + g], qrow[4 * t + g], a);
 #pragma unroll
           for (int i = 0; i < 4; ++i) a[i] *= a[i];
           if (diag && kb == w) {
@@ -319,7 +378,8 @@ static hipError_t impl(const void* q, const void* k, const void* v, void* o, int
   float* aggz = agg + (size_t)BH * NS * nblk * FS * M;
   float* Stot = aggz + (size_t)BH * NS * nblk * FS;
   float* ztot = Stot + (size_t)BH * C * M;
-  hipLaunchKernelGGL((fm_state_kernel<T, D, M, FM>), dim3((unsigned)BH * (unsigned)nblk * (unsigned)NS), dim3(NT),
+  hipLaunchKernelGGL((fm_state_kernel<T, D, M, FM>),
+                     dim3((unsigned)BH * (unsigned)nblk * (unsigned)(NS / slice_group<NS>())), dim3(NT),
                      0, stream, (const T*)k, (const T*)v, N, tblk, nblk, agg, aggz);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
