@@ -184,7 +184,7 @@ template <typename T, int D, int M, int FM>
 __global__ __launch_bounds__(NT) void fm_out_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                     const T* __restrict__ v, T* __restrict__ o, int N, int tblk,
                                                     int nblk, const float* __restrict__ pre,
-                                                    const float* __restrict__ prez, int causal) {
+                                                    const float* __restrict__ prez, int causal, int BHN) {
   using SM = OutSmem<D, M>;
   constexpr int NS = fdim<FM, D>() / FS, TM = M / 16;
   constexpr int XS = SM::XS, VS = SM::VS, SS = SM::SS;
@@ -193,7 +193,18 @@ __global__ __launch_bounds__(NT) void fm_out_kernel(const T* __restrict__ q, con
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform: its tests are scalar branches
   const int nqc = (N + CH - 1) / CH;
-  const int qc = blockIdx.x % nqc, bh = blockIdx.x / nqc;
+  // Workgroup ids go round-robin over the 8 XCDs.  With G = tblk / 64 query
+  // chunks per block (causal), the ids are remapped so that G consecutive chunks,
+  // which read the same prefix state, run on one XCD and share its L2; the grid
+  // is padded to whole groups of 8 G and the padding exits at once.
+  const int G = causal ? tblk / CH : 1;
+  int L = blockIdx.x;
+  if (G > 1) {
+    const int xcd = L & 7, kx = L >> 3;
+    L = ((kx / G) * 8 + xcd) * G + kx % G;
+  }
+  if (L >= BHN) return;
+  const int qc = L % nqc, bh = L / nqc;
   const int q0 = qc * CH, nq = min(CH, N - q0);
   const int blk = causal ? q0 / tblk : 0, npre = causal ? nblk : 1;
   const T* qh = q + (size_t)bh * N * D;
@@ -388,9 +399,12 @@ static hipError_t impl(const void* q, const void* k, const void* v, void* o, int
   e = launch_state_scan(agg, aggz, BH * NS, nblk, FS * M, FS, S0, z0, St, zt, causal, stream);
   if (e != hipSuccess || !o) return e;
   const int nqc = (N + CH - 1) / CH;
-  hipLaunchKernelGGL((fm_out_kernel<T, D, M, FM>), dim3((unsigned)BH * (unsigned)nqc), dim3(NT), 0, stream,
-                     (const T*)q, (const T*)k, (const T*)v, (T*)o, N, tblk, nblk, causal ? agg : St,
-                     causal ? aggz : zt, causal);
+  const long long BHN = (long long)BH * nqc;              // query chunks
+  const long long grp = causal && tblk > CH ? 8LL * (tblk / CH) : 1;
+  const long long nwg = (BHN + grp - 1) / grp * grp;      // padded to whole XCD groups
+  hipLaunchKernelGGL((fm_out_kernel<T, D, M, FM>), dim3((unsigned)nwg), dim3(NT), 0, stream, (const T*)q,
+                     (const T*)k, (const T*)v, (T*)o, N, tblk, nblk, causal ? agg : St, causal ? aggz : zt, causal,
+                     (int)BHN);
   return hipGetLastError();
 }
 
