@@ -230,6 +230,9 @@ def main():
                              "softmax_decode", *FMAPS,
                              "causal_mid", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flush", action="store_true",
+                    help="cold caches: write a 1 GiB buffer before every launch and time each launch with its own "
+                         "events (the default times back-to-back launches)")
     ap.add_argument("--oracle-budget", type=float, default=20.0)
     args = ap.parse_args()
 
@@ -341,9 +344,12 @@ def main():
         S, z = S0.clone(), z0.clone()
         o = torch.empty(w.steps, w.B, w.H, w.M, dtype=w.dtype, device=dev)
 
+        def launch(t):
+            la.decode_step(sq[t], sk[t], sv[t], S, z, out=o[t])
+
         def step():
             for t in range(w.steps):
-                la.decode_step(sq[t], sk[t], sv[t], S, z, out=o[t])
+                launch(t)
         kernel = "linattn_decode_step (decode_step_kernel)"
         units = w.B * w.H * w.steps                  # head-tokens per step (1024 decode steps)
         es = 2
@@ -364,9 +370,12 @@ def main():
         sq, sk, sv = sq.to(dev), sk.to(dev), sv.to(dev)
         o = torch.empty(w.steps, w.B, w.H, w.M, dtype=w.dtype, device=dev)
 
+        def launch(t):
+            la.softmax_decode_step(sq[t], sk[t], sv[t], Kc, Vc, w.N + t, out=o[t])
+
         def step():
             for t in range(w.steps):
-                la.softmax_decode_step(sq[t], sk[t], sv[t], Kc, Vc, w.N + t, out=o[t])
+                launch(t)
         kernel = "softmax_decode_step (softmax_decode_kernel)"
         units = w.B * w.H * w.steps
         es = 2
@@ -393,9 +402,12 @@ def main():
         W = W0.clone()
         o = torch.empty(w.steps, w.B, w.H, w.M, dtype=w.dtype, device=dev)
 
+        def launch(t):
+            la.deltanet_decode_step(sq[t], sk[t], sv[t], sb[t], W, out=o[t])
+
         def step():
             for t in range(w.steps):
-                la.deltanet_decode_step(sq[t], sk[t], sv[t], sb[t], W, out=o[t])
+                launch(t)
         kernel = "deltanet_decode_step (deltanet_step_kernel)"
         units = w.B * w.H * w.steps                  # head-tokens per step (1024 decode steps)
         es = 2
@@ -415,6 +427,9 @@ def main():
         unit = "tokens/s"
         launches_per_step = 1
 
+    if launches_per_step == 1:
+        launch = lambda t: step()
+
     for _ in range(Wm):
         step()
     torch.cuda.synchronize()
@@ -426,13 +441,31 @@ def main():
     t_start, t_end = events(2)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    t_start.record(stream)
-    for _ in range(K):
-        step()
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = t_start.elapsed_time(t_end)
+    if args.flush:
+        # Cold caches: a 1 GiB buffer (4x the Infinity Cache, 32x the L2s) is
+        # written before every launch, outside the launch's own pair of events;
+        # the time is the sum of the launches' intervals.
+        flush_buf = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        pairs = []
+        for _ in range(K):
+            for t in range(launches_per_step):
+                flush_buf.fill_(1.0)
+                a, b = events(2)
+                a.record(stream)
+                launch(t)
+                b.record(stream)
+                pairs.append((a, b))
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        total_ms = sum(a.elapsed_time(b) for a, b in pairs)
+    else:
+        t_start.record(stream)
+        for _ in range(K):
+            step()
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        total_ms = t_start.elapsed_time(t_end)
     launch_ms = total_ms / (K * launches_per_step)
 
     ms_per_step = total_ms / K
@@ -442,7 +475,7 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel,
                 "algorithmic_bytes_per_launch": alg_bytes, "launch_ms": round(launch_ms, 5)}
-    if args.workload == "softmax_decode":
+    if args.workload == "softmax_decode" and not args.flush:
         for _ in range(Wm):
             linear_step()
         a, b = events(2)
@@ -508,6 +541,8 @@ def main():
         "config": {"workload": names[args.workload], "B": w.B, "H": w.H, "N": w.N, "D": w.D, "M": w.M,
                    "parallelism": "single GPU"},
         "roofline": roofline,
+        "timing": ("cold: 1 GiB written before every launch, per-launch events summed" if args.flush
+                   else "back-to-back launches between two events"),
         "cpu_baseline": cpu,
         "wall_s": round(wall, 4),
         "source_hash": source_hash(args.workload),

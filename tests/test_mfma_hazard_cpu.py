@@ -21,7 +21,11 @@ MIN_DISTANCE = 5
 @pytest.mark.skipif(HIPCC is None, reason="hipcc not available")
 @pytest.mark.parametrize("src,pattern", [("causal_fused.hip", "causal_fused_kernel"),
                                          ("noncausal.hip", "nc_"),
-                                         ("causal_bwd_bf16.hip", "bf16_kernel")])
+                                         ("causal_bwd_bf16.hip", "bf16_kernel"),
+                                         ("featmap.hip", "fm_"),
+                                         ("causal.hip", "kernel"),
+                                         ("causal_bwd.hip", "kernel"),
+                                         ("deltanet_chunk.hip", "kernel")])
 def test_mfma_results_not_read_early(src, pattern):
     with tempfile.TemporaryDirectory() as d:
         asm = os.path.join(d, "k.s")
