@@ -41,9 +41,27 @@ constexpr int CH = 64;   // tokens per chunk
 constexpr int FS = 64;   // features per slice
 constexpr int POLY2 = 4; // template code of the polynomial map; DPFP-nu is coded nu (1..3)
 
+// The polynomial map's features are symmetric (x_a x_b = x_b x_a).  Inside the
+// kernels it is carried by the pairs a <= b only, in groups of 16: group (a, h)
+// holds b = 16h .. 16h + 15 for h >= a / 16, the key-side features weighted 2
+// for b > a, 1 for b = a and 0 for b < a, so that
+//   sum_{a <= b, grouped} q_a q_b (w_ab k_a k_b) = (q.k)^2.
+// Groups run h-major: group index gi = 8 h (h + 1) + a, a < 16 (h + 1).
+template <int D>
+constexpr int p2_groups() {
+  return 8 * (D / 16) * (D / 16 + 1);
+}
+
+// Internal feature dimension (what the kernels and the block records carry).
 template <int FM, int D>
 constexpr int fdim() {
-  return FM == POLY2 ? D * D : 2 * FM * D;
+  return FM == POLY2 ? 16 * p2_groups<D>() : 2 * FM * D;
+}
+
+// (a, h) of polynomial group gi (uniform; D <= 64 gives h <= 3).
+__device__ __forceinline__ void p2_group(int gi, int& a, int& h) {
+  h = gi >= 96 ? 3 : (gi >= 48 ? 2 : (gi >= 16 ? 1 : 0));
+  a = gi - 8 * h * (h + 1);
 }
 
 // Feature c of phi(x) for a row x of D floats (in LDS).
@@ -98,8 +116,10 @@ __device__ __forceinline__ void load_rows(float* dst, const T* src, int nv, int 
 // token; features are formed from the raw key rows as the operand is read, and
 // the lane's operands also give its share of z (tokens 4t + g).
 template <int NS>
-constexpr int slice_group() {
-  return NS <= 8 ? NS : 8;
+constexpr int slice_group() {  // the largest divisor of NS up to 8
+  int g = NS < 8 ? NS : 8;
+  while (NS % g) --g;
+  return g;
 }
 
 template <typename T, int D, int M, int FM>
@@ -120,11 +140,20 @@ __global__ __launch_bounds__(NT) void fm_state_kernel(const T* __restrict__ k, c
   const T* vh = v + (size_t)bh * N * M;
   f32x4 acc[SG][TM];
   float zp[SG];
+  int pa[SG], pb[SG];  // polynomial: the lane's pair (a, b) per slice of the group
+  float pw[SG];        // and its weight
 #pragma unroll
   for (int j = 0; j < SG; ++j) {
     zp[j] = 0.f;
 #pragma unroll
     for (int vb = 0; vb < TM; ++vb) acc[j][vb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (FM == POLY2) {  // wave w holds group 4 s + w of slice s
+      int a, h;
+      p2_group(4 * (sg * SG + j) + w, a, h);
+      pa[j] = a;
+      pb[j] = 16 * h + n;
+      pw[j] = pb[j] > a ? 2.f : (pb[j] == a ? 1.f : 0.f);
+    }
   }
   for (int c0 = t0; c0 < t1; c0 += CH) {
     const int nv = min(CH, t1 - c0);
@@ -140,7 +169,12 @@ __global__ __launch_bounds__(NT) void fm_state_kernel(const T* __restrict__ k, c
       for (int vb = 0; vb < TM; ++vb) bv[vb] = Vs[(4 * t + g) * VS + 16 * vb + n];
 #pragma unroll
       for (int j = 0; j < SG; ++j) {
-        const float a = feature<FM, D>(kr, (sg * SG + j) * FS + 16 * w + n);
+        float a;
+        if constexpr (FM == POLY2) {
+          a = pw[j] * kr[pa[j]] * kr[pb[j]];
+        } else {
+          a = feature<FM, D>(kr, (sg * SG + j) * FS + 16 * w + n);
+        }
         zp[j] += a;
 #pragma unroll
         for (int vb = 0; vb < TM; ++vb) acc[j][vb] = mma(a, bv[vb], acc[j][vb]);
@@ -257,12 +291,22 @@ __global__ __launch_bounds__(NT) void fm_out_kernel(const T* __restrict__ q, con
       // also the slice's share of the chunk's scores.
       const int base = (s * FS) & (2 * D - 1), order = (s * FS) / (2 * D) + 1;
       const int base_g = base + g, base_gn = base + g + order;
+      float pqa[4];  // polynomial: q_a of the slice's four groups, and their first b
+      int pb0[4];
+      if constexpr (FM == POLY2) {
+#pragma unroll
+        for (int tg = 0; tg < 4; ++tg) {
+          int a, h;
+          p2_group(4 * s + tg, a, h);
+          pqa[tg] = qrow[a];
+          pb0[tg] = 16 * h + g;
+        }
+      }
 #pragma unroll 4
       for (int t = 0; t < FS / 4; ++t) {
-        const int c = s * FS + 4 * t + g;
         float b;
         if constexpr (FM == POLY2) {
-          b = feature<FM, D>(qrow, c);
+          b = pqa[t >> 2] * qrow[pb0[t >> 2] + 4 * (t & 3)];
         } else {
           b = dpfp_feat<D>(qrow, t, base_g, base_gn);
         }
@@ -351,6 +395,67 @@ __global__ __launch_bounds__(NT) void fm_out_kernel(const T* __restrict__ q, con
   }
 }
 
+// Polynomial map, full state [BH][D*D][M] (+ z [BH][D*D]) -> grouped state
+// [BH][CI][M] (+ [BH][CI]): pair (a, b), a < b, takes S_ab + S_ba; a = b takes
+// S_aa; the zero-weight slots (b < a inside a group) are 0.  Then
+// sum_{grouped} q_a q_b S'_ab = sum_{a,b} q_a q_b S_ab for any S.
+// grid: ceil(BH * CI * (M + 1) / NT); element e = (bh * CI + c) * (M + 1) + m, m = M is z.
+template <int D, int M>
+__global__ __launch_bounds__(NT) void p2_fold_kernel(const float* __restrict__ S, const float* __restrict__ z,
+                                                     float* __restrict__ Sf, float* __restrict__ zf, long long n) {
+  constexpr int CI = fdim<POLY2, D>();
+  const long long e = (long long)blockIdx.x * NT + threadIdx.x;
+  if (e >= n) return;
+  const int m = (int)(e % (M + 1));
+  const long long bc = e / (M + 1);
+  const int c = (int)(bc % CI);
+  const long long bh = bc / CI;
+  int a, h;
+  p2_group(c >> 4, a, h);
+  const int b = 16 * h + (c & 15);
+  float r = 0.f;
+  if (m < M) {
+    const float* Sh = S + bh * D * D * M;
+    if (b > a) r = Sh[(a * D + b) * M + m] + Sh[(b * D + a) * M + m];
+    else if (b == a) r = Sh[(a * D + a) * M + m];
+    Sf[bc * M + m] = r;
+  } else {
+    const float* zh = z + bh * D * D;
+    if (b > a) r = zh[a * D + b] + zh[b * D + a];
+    else if (b == a) r = zh[a * D + a];
+    zf[bc] = r;
+  }
+}
+
+// Grouped state back to the full layout: S_out_ab = S0_ab + (S'_tot - S'_0) at
+// the pair (min, max), divided by its weight (2 off the diagonal).  S0 and the
+// folded S'_0 may be NULL (zero start).  Every output element reads only its
+// own S0 element, so S_out may be S0.
+// grid: ceil(BH * D * D * (M + 1) / NT); element e = (bh * D * D + a * D + b) * (M + 1) + m.
+template <int D, int M>
+__global__ __launch_bounds__(NT) void p2_expand_kernel(const float* S0, const float* z0,
+                                                       const float* __restrict__ Sf0, const float* __restrict__ zf0,
+                                                       const float* __restrict__ Stot, const float* __restrict__ ztot,
+                                                       float* S_out, float* z_out, long long n) {
+  constexpr int CI = fdim<POLY2, D>();
+  const long long e = (long long)blockIdx.x * NT + threadIdx.x;
+  if (e >= n) return;
+  const int m = (int)(e % (M + 1));
+  const long long bab = e / (M + 1);
+  const int ab = (int)(bab % (D * D));
+  const long long bh = bab / (D * D);
+  const int a = ab / D, b = ab % D, lo = a < b ? a : b, hi = a < b ? b : a, h = hi >> 4;
+  const long long c = bh * CI + 16 * (8 * h * (h + 1) + lo) + (hi & 15);
+  const float inv_w = lo < hi ? 0.5f : 1.f;
+  if (m < M) {
+    const float d = Stot[c * M + m] - (Sf0 ? Sf0[c * M + m] : 0.f);
+    S_out[bab * M + m] = (S0 ? S0[bab * M + m] : 0.f) + d * inv_w;
+  } else {
+    const float d = ztot[c] - (zf0 ? zf0[c] : 0.f);
+    z_out[bab] = (z0 ? z0[bab] : 0.f) + d * inv_w;
+  }
+}
+
 // Tokens per block: the chunk for DPFP (its intra-block similarity is built from
 // the features, slice by slice); 256 for the polynomial map (intra-block
 // similarity from D-long dot products, fewer prefix states).
@@ -366,21 +471,22 @@ static int block_tokens(int N) {
 
 template <int FM>
 static size_t ws_bytes_t(int BH, int N, int D, int M) {
-  const int C = FM == POLY2 ? D * D : 2 * FM * D;
+  const int C = FM == POLY2 ? (D == 64 ? fdim<POLY2, 64>() : fdim<POLY2, 32>()) : 2 * FM * D;
   const int NS = C / FS;
   const int tblk = block_tokens<FM>(N);
   const size_t nblk = (size_t)((N + tblk - 1) / tblk);
-  // block records, then the totals of the non-causal form
-  return ((size_t)BH * NS * nblk * (FS * M + FS) + (size_t)BH * C * (M + 1)) * sizeof(float);
+  // block records, the totals, and (polynomial map) the folded initial state
+  const size_t totals = (size_t)BH * C * (M + 1);
+  return ((size_t)BH * NS * nblk * (FS * M + FS) + totals + (FM == POLY2 ? totals : 0)) * sizeof(float);
 }
 
 template <typename T, int D, int M, int FM>
 static hipError_t impl(const void* q, const void* k, const void* v, void* o, int BH, int N, int causal,
                        const float* S0, const float* z0, float* S_out, float* z_out, void* ws, hipStream_t stream) {
-  constexpr int C = fdim<FM, D>(), NS = C / FS;
+  constexpr int C = fdim<FM, D>(), NS = C / FS, CX = FM == POLY2 ? D * D : C;  // internal, external
   static_assert(C % FS == 0, "whole feature slices");
   if (N == 0) {
-    if (S_out) return launch_state_copy(S0, z0, S_out, z_out, (long long)BH * C * M, (long long)BH * C, stream);
+    if (S_out) return launch_state_copy(S0, z0, S_out, z_out, (long long)BH * CX * M, (long long)BH * CX, stream);
     return hipSuccess;
   }
   const int tblk = block_tokens<FM>(N);
@@ -389,21 +495,47 @@ static hipError_t impl(const void* q, const void* k, const void* v, void* o, int
   float* aggz = agg + (size_t)BH * NS * nblk * FS * M;
   float* Stot = aggz + (size_t)BH * NS * nblk * FS;
   float* ztot = Stot + (size_t)BH * C * M;
+  float* Sf0 = ztot + (size_t)BH * C;  // polynomial map: S0 folded onto the grouped pairs
+  float* zf0 = Sf0 + (size_t)BH * C * M;
   hipLaunchKernelGGL((fm_state_kernel<T, D, M, FM>),
                      dim3((unsigned)BH * (unsigned)nblk * (unsigned)(NS / slice_group<NS>())), dim3(NT),
                      0, stream, (const T*)k, (const T*)v, N, tblk, nblk, agg, aggz);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  float* St = S_out ? S_out : (causal ? nullptr : Stot);
-  float* zt = S_out ? z_out : (causal ? nullptr : ztot);
-  e = launch_state_scan(agg, aggz, BH * NS, nblk, FS * M, FS, S0, z0, St, zt, causal, stream);
-  if (e != hipSuccess || !o) return e;
+  if constexpr (FM == POLY2) {
+    // The scan runs on the grouped pairs: S0 is folded onto them first, and the
+    // grouped total is expanded to the full D x D layout for S_out.
+    if (S0) {
+      const long long n = (long long)BH * C * (M + 1);
+      hipLaunchKernelGGL((p2_fold_kernel<D, M>), dim3((unsigned)((n + NT - 1) / NT)), dim3(NT), 0, stream, S0, z0,
+                         Sf0, zf0, n);
+    }
+    const bool tot = S_out || !causal;
+    e = launch_state_scan(agg, aggz, BH * NS, nblk, FS * M, FS, S0 ? Sf0 : nullptr, S0 ? zf0 : nullptr,
+                          tot ? Stot : nullptr, tot ? ztot : nullptr, causal, stream);
+    if (e != hipSuccess) return e;
+    if (S_out) {
+      const long long n = (long long)BH * D * D * (M + 1);
+      hipLaunchKernelGGL((p2_expand_kernel<D, M>), dim3((unsigned)((n + NT - 1) / NT)), dim3(NT), 0, stream, S0,
+                         z0, S0 ? Sf0 : nullptr, S0 ? zf0 : nullptr, Stot, ztot, S_out, z_out, n);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  } else {
+    float* St = S_out ? S_out : (causal ? nullptr : Stot);
+    float* zt = S_out ? z_out : (causal ? nullptr : ztot);
+    e = launch_state_scan(agg, aggz, BH * NS, nblk, FS * M, FS, S0, z0, St, zt, causal, stream);
+    if (e != hipSuccess) return e;
+    Stot = St;
+    ztot = zt;
+  }
+  if (!o) return hipSuccess;
   const int nqc = (N + CH - 1) / CH;
   const long long BHN = (long long)BH * nqc;              // query chunks
   const long long grp = causal && tblk > CH ? 8LL * (tblk / CH) : 1;
   const long long nwg = (BHN + grp - 1) / grp * grp;      // padded to whole XCD groups
   hipLaunchKernelGGL((fm_out_kernel<T, D, M, FM>), dim3((unsigned)nwg), dim3(NT), 0, stream, (const T*)q,
-                     (const T*)k, (const T*)v, (T*)o, N, tblk, nblk, causal ? agg : St, causal ? aggz : zt, causal,
+                     (const T*)k, (const T*)v, (T*)o, N, tblk, nblk, causal ? agg : Stot, causal ? aggz : ztot, causal,
                      (int)BHN);
   return hipGetLastError();
 }
