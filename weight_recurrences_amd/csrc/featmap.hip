@@ -15,9 +15,6 @@
 //
 // Work split.  The C features are cut into slices of FS = 64; a slice of phi is
 // itself a feature map, and numerator and denominator are sums over slices.
-// The polynomial map is carried on its symmetric pairs a <= b (see p2_groups):
-// 2560 internal features at D = 64 instead of 4096, folded from and expanded
-// to the D x D state layout at the boundary.
 //   1. fm_state_kernel (head, block of tblk tokens, slice s): the block's state
 //      increment dS_s = phi_s(K)^T V, dz_s = column sums of phi_s(K).
 //   2. the block scan of the elu + 1 path: exclusive prefix per block (causal)
