@@ -295,6 +295,33 @@ def test_deltanet_ragged(dtype, D, M, N):
     assert mat_rel_err(host(W), rW) < 1e-4
 
 
+@pytest.mark.parametrize("D,M", [(32, 64), (64, 32), (64, 64)])
+@pytest.mark.parametrize("N", [1025, 1088, 1470, 2113])
+def test_deltanet_two_level_scan(D, M, N):
+    """Past 16 chunks the memory scan composes groups of 8 chunk maps: group counts
+    of 3 to 5 with a partial last group (1 to 7 chunks), from an initial memory,
+    with the final memory written over it."""
+    dtype = torch.float32
+    say("deltanet two-level", D, M, N)
+    q, k, v, beta = synth.qkv_beta(1, 3, N, D, M, dtype=dtype, seed=N + 7 * D + M)
+    W0 = torch.randn(1, 3, M, D, generator=torch.Generator().manual_seed(N)) * 0.1
+    qg, kg, vg, bg = gpu(q, k, v, beta)
+    Wg = W0.to(DEV)
+    o, W = la.deltanet(qg, kg, vg, bg, W0=Wg, return_state=True)
+    ro, rW = oracle.deltanet(q, k, v, beta, W0=W0)
+    assert row_rel_err(host(o), ro) < TOL[dtype]
+    assert mat_rel_err(host(W), rW) < 1e-4
+    # the final memory written over the initial one (W_out == W0), through the C ABI
+    lib = la._lib.load()
+    need = la.deltanet_workspace_bytes(1, 3, N, D, M, dtype)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    o2 = torch.empty_like(o)
+    rc = lib.deltanet_fwd(qg.data_ptr(), kg.data_ptr(), vg.data_ptr(), bg.data_ptr(), o2.data_ptr(), 1, 3, N, D, M,
+                          0, Wg.data_ptr(), Wg.data_ptr(), ws.data_ptr(), need, torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+    assert torch.equal(host(o2), host(o)) and torch.equal(host(Wg), host(W))
+
+
 def test_deltanet_workload():
     w = synth.WORKLOADS["deltanet"]
     say(w)

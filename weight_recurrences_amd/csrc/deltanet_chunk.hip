@@ -24,6 +24,9 @@
 //                   then A and Bc on MFMA; writes Kh, Wc, Uc, A, Bc.
 //   dn_scan_kernel  per head: W <- W A + Bc over the chunks, each wave a
 //                   16-row slice of W; writes the memory at every chunk start.
+//                   Long sequences take two levels: dn_compose_kernel composes
+//                   the maps of groups of 8 chunks in parallel, the scan runs
+//                   over the composed maps, then over each group's chunks.
 //   dn_out_kernel   per (head, chunk), in parallel: U = Uc - Wc W0^T, then
 //                   o = Qh W0^T + (Qh Kh^T, j <= i) U.
 //
@@ -185,15 +188,20 @@ __global__ __launch_bounds__(NT) void dn_prep_kernel(const T* __restrict__ k, co
 // Per chunk: W <- W A + Bc, i.e. W^T tile dt <- Bc^T tile dt + sum over k of
 // A[k][16 dt + i] W^T[k][m], with k = 16 dt' + 4 g + r.  A (shared by the
 // waves) is staged in LDS; each wave reads its Bc tiles from global memory.
+// The workgroup covers the chunks [grp * G, min(nch, grp * G + G)) of head bh
+// (blockIdx.x = bh * ng + grp, ng = ceil(nch / G)), starting from its own memory
+// W0 + blockIdx.x * M * D; records are indexed bh * nch + c.  One workgroup per
+// head (G = nch) is the plain scan.
 template <int D, int M>
 __global__ __launch_bounds__(NT) void dn_scan_kernel(const float* __restrict__ a_ws, const float* __restrict__ b_ws,
-                                                     const float* __restrict__ W0, int nch, float* __restrict__ ws_ws,
-                                                     float* __restrict__ W_out) {
-  using GG = G<D, M>;
+                                                     const float* __restrict__ W0, int nch, int G,
+                                                     float* __restrict__ ws_ws, float* __restrict__ W_out) {
+  using GG = dnc::G<D, M>;
   constexpr int AS = D + 4;  // A row stride: (4g + r) * AS = 16 g mod 64 banks at D = 64 (4 g at D = 32)
   __shared__ __attribute__((aligned(16))) float As[2][D * AS];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
-  const int bh = blockIdx.x, m0 = 16 * w;
+  const int ng = (nch + G - 1) / G, bh = blockIdx.x / ng, grp = blockIdx.x % ng, m0 = 16 * w;
+  const int c0 = grp * G, c1 = min(nch, c0 + G);
   const bool active = w < GG::TM;  // waves past M/16 only help staging
 
   f32x4 wt[GG::TD];
@@ -201,7 +209,7 @@ __global__ __launch_bounds__(NT) void dn_scan_kernel(const float* __restrict__ a
   for (int dt = 0; dt < GG::TD; ++dt)
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      wt[dt][r] = (W0 && active) ? W0[((size_t)bh * M + m0 + n) * D + 16 * dt + 4 * g + r] : 0.f;
+      wt[dt][r] = (W0 && active) ? W0[((size_t)blockIdx.x * M + m0 + n) * D + 16 * dt + 4 * g + r] : 0.f;
 
   // Register staging: A as float4 units of rows (all threads), this wave's Bc tiles.
   constexpr int NA4 = D * D / 4 / NT > 0 ? D * D / 4 / NT : 1;
@@ -219,11 +227,11 @@ __global__ __launch_bounds__(NT) void dn_scan_kernel(const float* __restrict__ a
       rb[dt] = active ? *reinterpret_cast<const f32x4*>(b_ws + rec * GG::BB + (size_t)(m0 + n) * D + 16 * dt + 4 * g)
                       : f32x4{0.f, 0.f, 0.f, 0.f};
   };
-  load_chunk(0);
+  load_chunk(c0);
 
-  for (int c = 0; c < nch; ++c) {
+  for (int c = c0; c < c1; ++c) {
     const size_t rec = (size_t)bh * nch + c;
-    float* Ab = As[c & 1];
+    float* Ab = As[(c - c0) & 1];
 #pragma unroll
     for (int i = 0; i < NA4; ++i) {
       const int u = tid + NT * i;
@@ -241,7 +249,7 @@ __global__ __launch_bounds__(NT) void dn_scan_kernel(const float* __restrict__ a
     // One barrier per chunk: buffer c & 1 is rewritten two chunks later, after
     // every wave has passed the next chunk's barrier.
     __syncthreads();
-    if (c + 1 < nch) load_chunk(c + 1);
+    if (c + 1 < c1) load_chunk(c + 1);
 #pragma unroll
     for (int dk = 0; dk < GG::TD; ++dk)
 #pragma unroll
@@ -255,7 +263,75 @@ __global__ __launch_bounds__(NT) void dn_scan_kernel(const float* __restrict__ a
   if (W_out && active) {
 #pragma unroll
     for (int dt = 0; dt < GG::TD; ++dt)
-      *reinterpret_cast<f32x4*>(W_out + ((size_t)bh * M + m0 + n) * D + 16 * dt + 4 * g) = wt[dt];
+      *reinterpret_cast<f32x4*>(W_out + ((size_t)blockIdx.x * M + m0 + n) * D + 16 * dt + 4 * g) = wt[dt];
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Composition of the chunk maps of one group: W -> W A_c + Bc_c for the chunks
+// [grp * G, min(nch, grp * G + G)) of head bh (blockIdx.x = bh * ng + grp) is
+// W -> W Ag + Bg with (Ag, Bg) <- (Ag A_c, Bg A_c + Bc_c) from the group's first
+// map.  Wave w holds rows 16 w.. of Ag (w < D / 16) and of Bg (w < M / 16) in the
+// scan's transposed layout, so every step is the scan's product.  Writes
+// ag [BH * ng][D][D] and bg [BH * ng][M][D].
+template <int D, int M>
+__global__ __launch_bounds__(NT) void dn_compose_kernel(const float* __restrict__ a_ws, const float* __restrict__ b_ws,
+                                                        int nch, int G, float* __restrict__ ag, float* __restrict__ bg) {
+  using GG = dnc::G<D, M>;
+  constexpr int AS = D + 4;
+  __shared__ __attribute__((aligned(16))) float As[2][D * AS];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
+  const int ng = (nch + G - 1) / G, bh = blockIdx.x / ng, grp = blockIdx.x % ng, r0 = 16 * w;
+  const int c0 = grp * G, c1 = min(nch, c0 + G);
+  const bool act_a = w < GG::TD, act_b = w < GG::TM;
+  f32x4 xa[GG::TD], xb[GG::TD];
+  {
+    const size_t rec = (size_t)bh * nch + c0;
+#pragma unroll
+    for (int dt = 0; dt < GG::TD; ++dt) {
+      xa[dt] = act_a ? *reinterpret_cast<const f32x4*>(a_ws + rec * GG::AA + (size_t)(r0 + n) * D + 16 * dt + 4 * g)
+                     : f32x4{0.f, 0.f, 0.f, 0.f};
+      xb[dt] = act_b ? *reinterpret_cast<const f32x4*>(b_ws + rec * GG::BB + (size_t)(r0 + n) * D + 16 * dt + 4 * g)
+                     : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  for (int c = c0 + 1; c < c1; ++c) {
+    const size_t rec = (size_t)bh * nch + c;
+    float* Ab = As[(c - c0) & 1];
+    for (int u = tid; u < D * D / 4; u += NT)
+      *reinterpret_cast<float4*>(&Ab[(u / (D / 4)) * AS + (u % (D / 4)) * 4]) =
+          *reinterpret_cast<const float4*>(a_ws + rec * GG::AA + 4 * u);
+    f32x4 acc_a[GG::TD], acc_b[GG::TD];
+#pragma unroll
+    for (int dt = 0; dt < GG::TD; ++dt) {
+      acc_a[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc_b[dt] = act_b ? *reinterpret_cast<const f32x4*>(b_ws + rec * GG::BB + (size_t)(r0 + n) * D + 16 * dt + 4 * g)
+                        : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // One barrier per chunk: buffer (c - c0) & 1 is rewritten two chunks later.
+    __syncthreads();
+#pragma unroll
+    for (int dk = 0; dk < GG::TD; ++dk)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int dt = 0; dt < GG::TD; ++dt) {
+          const float a = Ab[(16 * dk + 4 * g + r) * AS + 16 * dt + n];
+          acc_a[dt] = mma(a, xa[dk][r], acc_a[dt]);
+          acc_b[dt] = mma(a, xb[dk][r], acc_b[dt]);
+        }
+#pragma unroll
+    for (int dt = 0; dt < GG::TD; ++dt) {
+      xa[dt] = acc_a[dt];
+      xb[dt] = acc_b[dt];
+    }
+  }
+#pragma unroll
+  for (int dt = 0; dt < GG::TD; ++dt) {
+    if (act_a)
+      *reinterpret_cast<f32x4*>(ag + ((size_t)blockIdx.x * D + r0 + n) * D + 16 * dt + 4 * g) = xa[dt];
+    if (act_b)
+      *reinterpret_cast<f32x4*>(bg + ((size_t)blockIdx.x * M + r0 + n) * D + 16 * dt + 4 * g) = xb[dt];
   }
 }
 
@@ -340,11 +416,18 @@ __global__ __launch_bounds__(NT) void dn_out_kernel(const T* __restrict__ q, con
 
 // ----------------------------------------------------------------------------
 // Host side.
+// Chunks per group of the two-level scan (0: one serial scan per head).
+static int scan_group(int nch) { return nch > 16 ? 8 : 0; }
+
 template <int D, int M>
 static size_t ws_floats(int BH, int N) {
   using GG = G<D, M>;
   const size_t nch = (size_t)((N + C - 1) / C);
-  return (size_t)BH * nch * (GG::KH + GG::WC + GG::UC + GG::AA + GG::BB + GG::WS);
+  const int sg = scan_group((int)nch);
+  const size_t ng = sg ? (nch + sg - 1) / sg : 0;
+  // per chunk records, then per group: composed maps and the memory at the group start
+  return (size_t)BH * nch * (GG::KH + GG::WC + GG::UC + GG::AA + GG::BB + GG::WS) +
+         (size_t)BH * ng * (GG::AA + GG::BB + GG::WS);
 }
 
 template <typename T, int D, int M>
@@ -362,7 +445,23 @@ static hipError_t impl(const void* q, const void* k, const void* v, const void* 
   const dim3 block(NT), grid((unsigned)rec);
   hipLaunchKernelGGL((dn_prep_kernel<T, D, M>), grid, block, 0, stream, (const T*)k, (const T*)v, (const T*)beta, N,
                      nch, kh, wc, uc, aa, bb);
-  hipLaunchKernelGGL((dn_scan_kernel<D, M>), dim3((unsigned)BH), block, 0, stream, aa, bb, W0, nch, wsb, W_out);
+  const int sg = scan_group(nch);
+  if (!sg) {
+    hipLaunchKernelGGL((dn_scan_kernel<D, M>), dim3((unsigned)BH), block, 0, stream, aa, bb, W0, nch, nch, wsb, W_out);
+  } else {
+    // Two-level scan: the maps of each group of sg chunks are composed in
+    // parallel, a short serial scan over the composed maps gives the memory at
+    // every group start (and the final memory), and each group then replays its
+    // own chunks from there in parallel, writing the memory at every chunk start.
+    const int ng = (nch + sg - 1) / sg;
+    float* ag = wsb + rec * GG::WS;
+    float* bg = ag + (size_t)BH * ng * GG::AA;
+    float* wg = bg + (size_t)BH * ng * GG::BB;
+    hipLaunchKernelGGL((dn_compose_kernel<D, M>), dim3((unsigned)(BH * ng)), block, 0, stream, aa, bb, nch, sg, ag, bg);
+    hipLaunchKernelGGL((dn_scan_kernel<D, M>), dim3((unsigned)BH), block, 0, stream, ag, bg, W0, ng, ng, wg, W_out);
+    hipLaunchKernelGGL((dn_scan_kernel<D, M>), dim3((unsigned)(BH * ng)), block, 0, stream, aa, bb, wg, nch, sg, wsb,
+                       nullptr);
+  }
   hipLaunchKernelGGL((dn_out_kernel<T, D, M>), grid, block, 0, stream, (const T*)q, kh, wc, uc, wsb, N, nch, (T*)o);
   return hipGetLastError();
 }
