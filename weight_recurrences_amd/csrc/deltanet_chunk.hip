@@ -93,24 +93,23 @@ __global__ __launch_bounds__(NT) void dn_prep_kernel(const T* __restrict__ k, co
                                                      float* __restrict__ uc_ws, float* __restrict__ a_ws,
                                                      float* __restrict__ b_ws) {
   using GG = G<D, M>;
-  // Y = [Kh | V], one row per token: stride D + M + 4 keeps the column-slab reads
-  // of the G product free of bank conflicts for every (D, M).
-  constexpr int YS = D + M + 4;
-  constexpr int XS = D + M + 16;  // X = [Wc | Uc] row stride: (4kk + g) * XS = 16 g mod 64 banks
-  __shared__ __attribute__((aligned(16))) float Ys[C * YS];
-  // G (during the substitution), then X = [Wc | Uc] (for the A and Bc products)
-  __shared__ __attribute__((aligned(16))) float GXs[C * (GG::GS > XS ? GG::GS : XS)];
+  constexpr int W2 = D + M;       // columns of Y = [Kh | V] and of X = [Wc | Uc]
+  constexpr int XS = W2 + 16;     // X row stride: rows read by k-slot g step 16 banks
+  __shared__ __attribute__((aligned(16))) float Ks[C * GG::KS];  // Kh
+  __shared__ __attribute__((aligned(16))) float Gs[C * GG::GS];  // G = Kh Kh^T
+  __shared__ __attribute__((aligned(16))) float Xs[C * XS];      // Y, overwritten block by block by X
   __shared__ float Bs[C];
-  float* Gs = GXs;
-  float* Xs = GXs;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
   const int bh = blockIdx.x / nch, c = blockIdx.x % nch;
   const int t0 = c * C, nt = min(C, N - t0);
-  float* Ks = Ys;  // kh: columns [0, D)
-  load_rows<T, D, YS, true>(Ys, k + ((size_t)bh * N + t0) * D, nt, tid);
-  load_rows<T, M, YS, false>(Ys + D, v + ((size_t)bh * N + t0) * M, nt, tid);
+  load_rows<T, D, GG::KS, true>(Ks, k + ((size_t)bh * N + t0) * D, nt, tid);
+  load_rows<T, M, XS, false>(Xs + D, v + ((size_t)bh * N + t0) * M, nt, tid);
   if (tid < C) Bs[tid] = tid < nt ? ld_scalar<T>(beta + (size_t)bh * N + t0 + tid) : 0.f;
   __syncthreads();
+  for (int u = tid; u < C * D / 4; u += NT) {  // Y's Kh columns
+    const int row = u / (D / 4), c4 = (u % (D / 4)) * 4;
+    *reinterpret_cast<float4*>(&Xs[row * XS + c4]) = *reinterpret_cast<const float4*>(&Ks[row * GG::KS + c4]);
+  }
 
   // G = Kh Kh^T: wave w computes the row tile w against every column tile.
 #pragma unroll
@@ -118,47 +117,63 @@ __global__ __launch_bounds__(NT) void dn_prep_kernel(const T* __restrict__ k, co
     f32x4 acc{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < D / 4; ++kk)
-      acc = mma(Ks[(16 * w + n) * YS + 4 * kk + g], Ks[(16 * jt + n) * YS + 4 * kk + g], acc);
+      acc = mma(Ks[(16 * w + n) * GG::KS + 4 * kk + g], Ks[(16 * jt + n) * GG::KS + 4 * kk + g], acc);
 #pragma unroll
     for (int r = 0; r < 4; ++r) Gs[(16 * w + 4 * g + r) * GG::GS + 16 * jt + n] = acc[r];
   }
   __syncthreads();
 
-  // [Wc | Uc] = T [Kh | V]: x_t = beta_t (y_t - sum_{s<t} G[t][s] x_s), one column
-  // per thread, held in registers.  Right-looking order: once x_t is known it is
-  // removed from every later row at once (independent FMAs, and column t of G is
-  // its row t, G being symmetric).
-  const size_t rec = (size_t)bh * nch + c;
-  float x[C];
-  if (tid < D + M) {
+  // [Wc | Uc] = T [Kh | V], x_t = beta_t (y_t - sum_{s<t} G[t][s] x_s), in four
+  // blocks of 16 tokens.  Block i first takes the earlier blocks at once on MFMA,
+  // z = y - G[block i][blocks < i] X[blocks < i], in place in Xs; then one thread
+  // per column solves the 16 rows of the block, right-looking (G is symmetric, so
+  // column t of G is its row t).
 #pragma unroll
-    for (int t = 0; t < C; ++t) x[t] = Ys[t * YS + tid];
+  for (int bi = 0; bi < C / 16; ++bi) {
+    if (bi > 0) {
+      for (int ct = w; ct < W2 / 16; ct += 4) {
+        f32x4 acc;
 #pragma unroll
-    for (int t = 0; t < C; ++t) {
-      x[t] *= Bs[t];
+        for (int r = 0; r < 4; ++r) acc[r] = Xs[(16 * bi + 4 * g + r) * XS + 16 * ct + n];
+        for (int bj = 0; bj < bi; ++bj)
 #pragma unroll
-      for (int t2 = t + 1; t2 < C; ++t2) x[t2] -= Gs[t * GG::GS + t2] * x[t];
+          for (int kk = 0; kk < 4; ++kk)
+            acc = mma(-Gs[(16 * bi + n) * GG::GS + 16 * bj + 4 * kk + g],
+                      Xs[(16 * bj + 4 * kk + g) * XS + 16 * ct + n], acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Xs[(16 * bi + 4 * g + r) * XS + 16 * ct + n] = acc[r];
+      }
+      __syncthreads();
     }
-    if (tid < D) {
+    if (tid < W2) {
+      float z[16];
 #pragma unroll
-      for (int t = 0; t < C; ++t) wc_ws[rec * GG::WC + (size_t)t * D + tid] = x[t];
-    } else {
+      for (int t = 0; t < 16; ++t) z[t] = Xs[(16 * bi + t) * XS + tid];
 #pragma unroll
-      for (int t = 0; t < C; ++t) uc_ws[rec * GG::UC + (size_t)t * M + (tid - D)] = x[t];
+      for (int t = 0; t < 16; ++t) {
+        z[t] *= Bs[16 * bi + t];
+#pragma unroll
+        for (int t2 = t + 1; t2 < 16; ++t2) z[t2] -= Gs[(16 * bi + t) * GG::GS + 16 * bi + t2] * z[t];
+      }
+#pragma unroll
+      for (int t = 0; t < 16; ++t) Xs[(16 * bi + t) * XS + tid] = z[t];
     }
+    __syncthreads();
   }
-  // Kh for the output kernel.
+
+  const size_t rec = (size_t)bh * nch + c;
+  // Wc, Uc and Kh for the output kernel.
+  for (int u = tid; u < C * W2 / 4; u += NT) {
+    const int row = u / (W2 / 4), c4 = (u % (W2 / 4)) * 4;
+    const float4 x = *reinterpret_cast<const float4*>(&Xs[row * XS + c4]);
+    if (c4 < D) *reinterpret_cast<float4*>(&wc_ws[rec * GG::WC + (size_t)row * D + c4]) = x;
+    else *reinterpret_cast<float4*>(&uc_ws[rec * GG::UC + (size_t)row * M + c4 - D]) = x;
+  }
   float* khd = kh_ws + rec * GG::KH;
   for (int u = tid; u < C * D / 4; u += NT) {
     const int row = u / (D / 4), c4 = (u % (D / 4)) * 4;
-    *reinterpret_cast<float4*>(&khd[row * D + c4]) = *reinterpret_cast<const float4*>(&Ks[row * YS + c4]);
+    *reinterpret_cast<float4*>(&khd[row * D + c4]) = *reinterpret_cast<const float4*>(&Ks[row * GG::KS + c4]);
   }
-  __syncthreads();  // every read of G is done: its space takes X
-  if (tid < D + M) {
-#pragma unroll
-    for (int t = 0; t < C; ++t) Xs[t * XS + tid] = x[t];
-  }
-  __syncthreads();
 
   // The chunk's affine map: A = I - Wc^T Kh (D x D), Bc = Uc^T Kh (M x D).  The
   // TD * TD + TM * TD output tiles are dealt round robin to the waves; tile
@@ -172,7 +187,7 @@ __global__ __launch_bounds__(NT) void dn_prep_kernel(const T* __restrict__ k, co
     f32x4 acc{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < C / 4; ++kk)
-      acc = mma(Xs[(4 * kk + g) * XS + xcol + n], Ks[(4 * kk + g) * YS + 16 * jt + n], acc);
+      acc = mma(Xs[(4 * kk + g) * XS + xcol + n], Ks[(4 * kk + g) * GG::KS + 16 * jt + n], acc);
     float* dst = isa ? a_ws + rec * GG::AA : b_ws + rec * GG::BB;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
