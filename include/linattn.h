@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define LINATTN_ABI_VERSION 2
+#define LINATTN_ABI_VERSION 3  /* 2: deltanet_fwd takes a workspace; 3: the feature-map and softmax decode entry points */
 
 typedef enum { LINATTN_F32 = 0, LINATTN_BF16 = 1 } linattn_dtype_t;
 

@@ -37,7 +37,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.linattn_abi_version() == 2
+    assert lib.linattn_abi_version() == 3
     for code, name in _lib.STATUS.items():
         assert lib.linattn_status_str(code).decode() == name
     assert lib.linattn_status_str(99).decode() == "LINATTN_ERR_UNKNOWN"
