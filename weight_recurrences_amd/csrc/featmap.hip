@@ -200,13 +200,23 @@ __global__ __launch_bounds__(NT) void fm_state_kernel(const T* __restrict__ k, c
 // ---- 3. outputs --------------------------------------------------------------
 template <int D, int M>
 struct OutSmem {
-  static constexpr int XS = D + 4, VS = M + 4, SS = M + 16;
+  static constexpr int XS = D + 4, VS = M + 4;
   float Qr[CH * XS];  // raw queries of the chunk
   float Kr[CH * XS];  // raw keys of the current key chunk
-  float Vs[CH * VS];  // values of the current key chunk
-  float Ss[FS * SS];  // prefix state slice S_s
-  float zs[FS];       // prefix z slice
+  union {             // the state slices during the slice loop, the values after it
+    float Vs[CH * VS];
+    float Ss[FS * M];  // prefix state slice S_s, rows of M floats, swizzled by ss_col
+  };
+  float zs[FS];  // prefix z slice
 };
+
+// Column of element (f, c) of a state slice in LDS: the 16-float groups are XORed
+// by row so that the four rows a k-slot group g reads (4t + g) fall in four
+// different bank groups (M = 64: by f mod 4; M = 32: by bit 1 of f).
+template <int M>
+__device__ __forceinline__ int ss_col(int f, int c) {
+  return M == 64 ? c ^ ((f & 3) << 4) : c ^ (((f >> 1) & 1) << 4);
+}
 
 // grid: BH * nqc, blockIdx.x = bh * nqc + qc (nqc = ceil(N / 64) query chunks).
 // pre/prez: causal, the exclusive block prefixes [BH * NS][nblk][FS][M] / [FS];
@@ -221,7 +231,7 @@ __global__ __launch_bounds__(NT) void fm_out_kernel(const T* __restrict__ q, con
                                                     const float* __restrict__ prez, int causal, int BHN) {
   using SM = OutSmem<D, M>;
   constexpr int NS = fdim<FM, D>() / FS, TM = M / 16;
-  constexpr int XS = SM::XS, VS = SM::VS, SS = SM::SS;
+  constexpr int XS = SM::XS, VS = SM::VS;
   constexpr int PF = FS * M / 4 / NT;  // float4 groups of a state slice per thread
   __shared__ SM sm;
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, g = lane >> 4;
@@ -255,10 +265,7 @@ __global__ __launch_bounds__(NT) void fm_out_kernel(const T* __restrict__ q, con
   for (int u = 0; u < PF; ++u) pf[u] = *reinterpret_cast<const f32x4*>(Sb + (u * NT + tid) * 4);
   float pz = tid < FS ? zb[tid] : 0.f;
   load_rows<T, D, XS>(sm.Qr, qh + (size_t)q0 * D, nq, tid);
-  if (intra_dpfp) {  // the block is this chunk: its keys and values
-    load_rows<T, D, XS>(sm.Kr, kh + (size_t)q0 * D, nq, tid);
-    load_rows<T, M, VS>(sm.Vs, vh + (size_t)q0 * M, nq, tid);
-  }
+  if (intra_dpfp) load_rows<T, D, XS>(sm.Kr, kh + (size_t)q0 * D, nq, tid);  // the block is this chunk
   f32x4 num[TM];  // num^T tiles: lane (n, g) holds values 16 vb + 4g + i of query 16w + n
 #pragma unroll
   for (int vb = 0; vb < TM; ++vb) num[vb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -277,7 +284,7 @@ __global__ __launch_bounds__(NT) void fm_out_kernel(const T* __restrict__ q, con
 #pragma unroll
       for (int u = 0; u < PF; ++u) {
         const int e = (u * NT + tid) * 4, f = e / M, c = e % M;
-        *reinterpret_cast<f32x4*>(&sm.Ss[f * SS + c]) = pf[u];
+        *reinterpret_cast<f32x4*>(&sm.Ss[f * M + ss_col<M>(f, c)]) = pf[u];
       }
       if (tid < FS) sm.zs[tid] = pz;
       if (s + 1 < NS) {  // next slice in flight during this one
@@ -312,7 +319,8 @@ __global__ __launch_bounds__(NT) void fm_out_kernel(const T* __restrict__ q, con
         }
         den += b * sm.zs[4 * t + g];
 #pragma unroll
-        for (int vb = 0; vb < TM; ++vb) num[vb] = mma(sm.Ss[(4 * t + g) * SS + 16 * vb + n], b, num[vb]);
+        for (int vb = 0; vb < TM; ++vb)
+          num[vb] = mma(sm.Ss[(4 * t + g) * M + ss_col<M>(4 * t + g, 16 * vb + n)], b, num[vb]);
         if (intra_dpfp) {
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb)
@@ -322,6 +330,10 @@ __global__ __launch_bounds__(NT) void fm_out_kernel(const T* __restrict__ q, con
     }
 
     if (intra_dpfp) {
+      // The values replace the state slices in LDS.
+      __syncthreads();
+      load_rows<T, M, VS>(sm.Vs, vh + (size_t)q0 * M, nq, tid);
+      __syncthreads();
       // Keys after the query are masked; num^T += V^T A^T, den += column sums of A^T.
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
@@ -388,10 +400,11 @@ __global__ __launch_bounds__(NT) void fm_out_kernel(const T* __restrict__ q, con
   den += __shfl_xor(den, 16);
   den += __shfl_xor(den, 32);
   if (16 * w + n < nq) {
+    const float rd = __builtin_amdgcn_rcpf(den);  // 1 ulp; 0/0 rows stay NaN (0 * inf)
     T* orow = o + ((size_t)bh * N + q0 + 16 * w + n) * M + 4 * g;
 #pragma unroll
     for (int vb = 0; vb < TM; ++vb)
-      store4<T>(orow + 16 * vb, float4{num[vb][0] / den, num[vb][1] / den, num[vb][2] / den, num[vb][3] / den});
+      store4<T>(orow + 16 * vb, float4{num[vb][0] * rd, num[vb][1] * rd, num[vb][2] * rd, num[vb][3] * rd});
   }
 }
 
