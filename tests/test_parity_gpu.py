@@ -75,6 +75,28 @@ def test_causal_many_blocks_with_state(B, H, N):
     assert row_rel_err(host(o2), ro) < TOL[dtype]
 
 
+@pytest.mark.parametrize("B,H,N,exact", [(1, 8, 4096, False), (2, 3, 3000, True), (1, 16, 2304, False)])
+def test_causal_lookback_slow_path(monkeypatch, B, H, N, exact):
+    """With a look-back wait bound of 0 every block whose predecessors have not
+    published yet takes the slow path and computes their increments directly from
+    K and V; the results must still match the oracle (both variants, B*H a
+    multiple of 8 and not)."""
+    dtype, D, M = torch.bfloat16, 64, 64
+    say("causal look-back slow path", B, H, N, exact)
+    monkeypatch.setenv("LINATTN_LOOKBACK_SPIN_TICKS", "0")
+    q, k, v = synth.qkv(B, H, N, D, M, dtype=dtype, seed=N + H)
+    S0 = torch.randn(B, H, D, M, generator=torch.Generator().manual_seed(N)) * 2
+    z0 = torch.rand(B, H, D, generator=torch.Generator().manual_seed(N + 1)) * 4
+    ro, rS, rz = oracle.causal(q, k, v, S0=S0, z0=z0)
+    if exact:
+        o, (S, z) = la.causal(*gpu(q, k, v), state=gpu(S0, z0), return_state=True)
+        assert mat_rel_err(host(S), rS) < STATE_TOL[dtype]
+        assert mat_rel_err(host(z), rz, 1) < STATE_TOL[dtype]
+    else:
+        o = la.causal(*gpu(q, k, v), state=gpu(S0, z0))
+    assert row_rel_err(host(o), ro) < TOL[dtype]
+
+
 def test_causal_small_workload_all_rows_explicit():
     w = synth.WORKLOADS["causal_small"]
     say(w)

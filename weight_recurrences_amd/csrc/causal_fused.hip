@@ -43,6 +43,8 @@
 // LDS rows are 16-byte units XOR-swizzled by a function of the row (row_swz),
 // which keeps the row-major stores, the score-operand reads and the transposed
 // reads free of bank conflicts.
+#include <stdlib.h>
+
 #include <atomic>
 #include <chrono>
 
@@ -785,7 +787,13 @@ static hipError_t fused_impl(const void* q, const void* k, const void* v, void* 
     S0 = S0c;
     z0 = z0c;
   }
-  const unsigned long long spin_ticks = 20000;  // 200 us of the 100 MHz real-time counter
+  // The look-back's wait bound: 200 us of the 100 MHz real-time counter, or
+  // LINATTN_LOOKBACK_SPIN_TICKS (read at every launch).  A bound of 0 sends
+  // every block whose predecessors have not yet published to the slow path,
+  // which computes their increments directly: the tests use it to exercise that
+  // path; the results stay correct, only slower.
+  const char* spin_env = getenv("LINATTN_LOOKBACK_SPIN_TICKS");
+  const unsigned long long spin_ticks = spin_env ? strtoull(spin_env, nullptr, 10) : 20000ull;
   // Workgroups are dispatched to the XCDs round robin, so with BH a multiple of
   // 8 every block of a head (workgroup indices b * BH + h) runs on one XCD and
   // states are exchanged through its L2.
