@@ -9,7 +9,7 @@ single-token steps on 256x16 states), deltanet, deltanet_decode (the same for th
 delta-rule memory), softmax_decode (the same steps as softmax attention over a
 key/value cache, the comparison baseline), fmap_dpfp1/2/3 and fmap_poly2 (causal
 linear attention with the DPFP-nu or degree-2 polynomial feature map, fp32,
-B=4 H=8 N=4096 D=M=64), causal_mid, and copy (a 1 GiB device copy that calibrates
+B=4 H=8 N=4096 D=M=64), causal_mid, causal_small, and copy (a 1 GiB device copy that calibrates
 the HBM counters).
 
 Prints ONE JSON line.  Inputs are synthetic (seeded N(0,1), the recipe of the
@@ -212,6 +212,7 @@ def time_oracle(workload, inputs, budget_s: float = 20.0):
     dt = time.perf_counter() - t0
     toks = nb * w.H * w.N
     return {"value": toks / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "single_thread": {"value": w.N / one, "unit": "tokens/s", "sample": "one head on one thread"},
             "sample": f"{nb} of {w.B} batch entries ({nb * w.H} of {heads} heads, all {w.N} tokens), "
                       f"{dt:.1f} s, {cpu_model()}"}
 
@@ -228,7 +229,7 @@ def main():
     ap.add_argument("--workload", default="causal_long",
                     choices=["causal_long", "causal_bwd_long", "noncausal_long", "decode", "deltanet", "deltanet_decode",
                              "softmax_decode", *FMAPS,
-                             "causal_mid", "copy"])
+                             "causal_mid", "causal_small", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush", action="store_true",
                     help="cold caches: write a 1 GiB buffer before every launch and time each launch with its own "
@@ -291,7 +292,7 @@ def main():
     def events(n):
         return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
-    if args.workload in ("causal_long", "causal_mid", "noncausal_long"):
+    if args.workload in ("causal_long", "causal_mid", "causal_small", "noncausal_long"):
         q, k, v = (t.to(dev) for t in inputs)
         o = torch.empty(w.B, w.H, w.N, w.M, dtype=w.dtype, device=dev)
         if args.workload == "noncausal_long":
@@ -516,6 +517,7 @@ def main():
                        f"B={w.B} H={w.H} N={w.N} D=M={w.D}",
         "noncausal_long": f"noncausal_long: non-causal linear attention, bf16, B={w.B} H={w.H} N={w.N} D=M={w.D}",
         "causal_mid": f"causal_mid: causal linear attention, fp32, B={w.B} H={w.H} N={w.N} D=M={w.D}",
+        "causal_small": f"causal_small: causal linear attention, fp32, B={w.B} H={w.H} N={w.N} D=M={w.D} (launch-bound)",
         "causal_bwd_long": f"causal_bwd_long: backward of causal linear attention (dq, dk, dv), bf16 in/out, fp32 "
                            f"arithmetic, B={w.B} H={w.H} N={w.N} D=M={w.D}",
         "decode": f"decode: RNN-form decode, {w.B}x{w.H} states D=M={w.D}, {w.steps} single-token bf16 steps "
@@ -529,7 +531,7 @@ def main():
               f"{'DPFP-%d' % FMAPS[f][1] if FMAPS[f][0] == 1 else 'degree-2 polynomial'} feature map "
               f"(C={la.fmap_dim(*FMAPS[f], w.D)}), fp32, B={w.B} H={w.H} N={w.N} D=M={w.D}" for f in FMAPS},
     }
-    dtype = {"causal_long": "bf16", "causal_bwd_long": "bf16", "noncausal_long": "bf16", "decode": "bf16", "causal_mid": "f32",
+    dtype = {"causal_long": "bf16", "causal_bwd_long": "bf16", "noncausal_long": "bf16", "decode": "bf16", "causal_mid": "f32", "causal_small": "f32",
              "deltanet": "f32", "deltanet_decode": "bf16", "softmax_decode": "bf16",
              **{f: "f32" for f in FMAPS}}[args.workload]
     line = {
