@@ -15,6 +15,9 @@
 //
 // Work split.  The C features are cut into slices of FS = 64; a slice of phi is
 // itself a feature map, and numerator and denominator are sums over slices.
+// The polynomial map is carried on its symmetric pairs a <= b (p2_groups): 2560
+// internal features at D = 64 instead of 4096, folded from and expanded to the
+// D x D state layout at the boundary.
 //   1. fm_state_kernel (head, block of tblk tokens, slice s): the block's state
 //      increment dS_s = phi_s(K)^T V, dz_s = column sums of phi_s(K).
 //   2. the block scan of the elu + 1 path: exclusive prefix per block (causal)
@@ -64,19 +67,16 @@ __device__ __forceinline__ void p2_group(int gi, int& a, int& h) {
   a = gi - 8 * h * (h + 1);
 }
 
-// Feature c of phi(x) for a row x of D floats (in LDS).
+// DPFP feature c of a row x of D floats (in LDS), from its definition.
 template <int FM, int D>
 __device__ __forceinline__ float feature(const float* x, int c) {
-  if constexpr (FM == POLY2) {
-    return x[c / D] * x[c % D];
-  } else {
-    constexpr int R = 2 * D;
-    const int n = c / R + 1, i = c % R, j = (i + n) % R;
-    const float xi = x[i < D ? i : i - D], xj = x[j < D ? j : j - D];
-    const float ri = i < D ? (xi > 0.f ? xi : 0.f) : (xi < 0.f ? -xi : 0.f);
-    const float rj = j < D ? (xj > 0.f ? xj : 0.f) : (xj < 0.f ? -xj : 0.f);
-    return ri * rj;
-  }
+  static_assert(FM >= 1 && FM <= 3, "DPFP-nu");
+  constexpr int R = 2 * D;
+  const int n = c / R + 1, i = c % R, j = (i + n) % R;
+  const float xi = x[i < D ? i : i - D], xj = x[j < D ? j : j - D];
+  const float ri = i < D ? (xi > 0.f ? xi : 0.f) : (xi < 0.f ? -xi : 0.f);
+  const float rj = j < D ? (xj > 0.f ? xj : 0.f) : (xj < 0.f ? -xj : 0.f);
+  return ri * rj;
 }
 
 // DPFP feature c = s FS + 4t + g of a raw row x (D floats), with the slice's
