@@ -29,7 +29,7 @@ namespace smx {
 
 constexpr int NT = 256;  // threads per workgroup
 constexpr int KPR = 32;  // keys per round (4 waves x 8 groups of 8 lanes)
-constexpr int U = 4;     // rounds folded per rescale (loads in flight per lane)
+constexpr int U = 2;     // rounds folded per rescale (rows in flight per lane): 2 keeps 76 VGPRs, 6 waves per SIMD
 
 // E consecutive elements (16 or 8 bytes of bf16, 32 or 16 bytes of float32) as floats.
 template <int E>
