@@ -182,7 +182,7 @@ template <int D, int M>
 __global__ __launch_bounds__(NT) void nc_apply_kernel(const bf16_t* __restrict__ q, bf16_t* __restrict__ o, int N,
                                                       int tblk, int nblk, const float* __restrict__ tot) {
   using GG = G<D, M>;
-  constexpr int PF = 4;  // chunks of queries in flight per wave
+  constexpr int PF = 2;  // chunks of queries in flight per wave (2 keeps 120 VGPRs: more resident waves beat deeper queues)
   __shared__ __attribute__((aligned(16))) bf16_t St[M * D];  // S^T [m][d] in bf16, swizzled
   __shared__ __attribute__((aligned(16))) float Zs[D];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
