@@ -403,9 +403,15 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
 
   // ---------------- loads: K, V of the whole block, then its queries ----------------
   // Inputs are streamed with non-temporal loads, which leave the L2 to the
-  // published states and the outputs.  Keys past the end of the sequence read
-  // as bf16 -inf, whose phi is exactly 0, so they add nothing to the state or
-  // to a score; values past the end read as 0.
+  // published states and the outputs.  The loads carry no condition: rows past
+  // the end of the sequence re-read its last row.  (A conditional load becomes
+  // a branch whose join copies the loaded registers, and each copy waits for
+  // every load in flight, so the block's loads would go out in several
+  // round trips.)  When they are staged, keys past the end become bf16 -inf,
+  // whose phi is exactly 0, so they add nothing to the state or to a score, and
+  // values past the end become 0.  Queries past the end only feed output rows
+  // that are never stored; without an output the query loads re-read one key
+  // row and are not used.
   constexpr int KV = CH * D * 2 / 16 / NT;  // 16-byte vectors per thread per chunk
   constexpr int VV = CH * M * 2 / 16 / NT;
   constexpr uint32_t NEG_INF2 = 0xFF80FF80u;
@@ -415,28 +421,31 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
 #pragma unroll
     for (int i = 0; i < KV; ++i) {
       const int p = tid + NT * i, row = p / GG::UK, cu = p % GG::UK;
-      const int t = c * CH + row;
-      rk[c][i] = t < ntok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kh + (size_t)(t0 + t) * D + cu * 8))
-                          : u32x4{NEG_INF2, NEG_INF2, NEG_INF2, NEG_INF2};
+      const int t = min(c * CH + row, ntok - 1);
+      rk[c][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kh + (size_t)(t0 + t) * D + cu * 8));
     }
 #pragma unroll
     for (int i = 0; i < VV; ++i) {
       const int p = tid + NT * i, row = p / GG::UV, cu = p % GG::UV;
-      const int t = c * CH + row;
-      rv[c][i] = t < ntok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vh + (size_t)(t0 + t) * M + cu * 8)) : u32x4{0u, 0u, 0u, 0u};
+      const int t = min(c * CH + row, ntok - 1);
+      rv[c][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vh + (size_t)(t0 + t) * M + cu * 8));
     }
+    // Keep the keys' and values' loads in chunk order, so that phase 1 waits
+    // for each chunk while the later ones are still in flight (the compiler
+    // issues the queries' loads ahead of them all).
+    __builtin_amdgcn_sched_barrier(0);
   }
   // Queries of this wave's rows 16 w + n of every chunk (raw bits; phi is
   // applied in phase 3).
   constexpr int QV = D / 32;
   u32x4 rq[NCH][QV];
+  const bf16_t* qsrc = o ? qh : kh;
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
-    const int i = c * CH + 16 * w + n;
+    const int i = o ? min(c * CH + 16 * w + n, ntok - 1) : 0;
 #pragma unroll
     for (int s = 0; s < QV; ++s)
-      rq[c][s] = (o && i < ntok) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qh + (size_t)(t0 + i) * D + 32 * s + 8 * g))
-                                 : u32x4{0u, 0u, 0u, 0u};
+      rq[c][s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qsrc + (size_t)(t0 + i) * D + 32 * s + 8 * g));
   }
 
   // ---------------- phase 1: block increment and local prefixes ----------------
@@ -452,10 +461,11 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
     // phi(K): head into the resident tile, tail (EXACT) into the staging tile.
 #pragma unroll
     for (int i = 0; i < KV; ++i) {
+      const bool ok = c * CH + (tid + NT * i) / GG::UK < ntok;
       u32x4 hv, lv;
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
-        const uint32_t wd = rk[c][i][h];
+        const uint32_t wd = ok ? rk[c][i][h] : NEG_INF2;
         const float a = phi(lo_of(wd)), bb = phi(hi_of(wd));
         const uint32_t hp = cvt_pk(a, bb);
         hv[h] = hp;
@@ -466,7 +476,8 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
     }
 #pragma unroll
     for (int i = 0; i < VV; ++i)
-      *reinterpret_cast<u32x4*>(tile_at<GG::UV>(sm.V, l_vst, c * CH + i * (NT / GG::UV), 0)) = rv[c][i];
+      *reinterpret_cast<u32x4*>(tile_at<GG::UV>(sm.V, l_vst, c * CH + i * (NT / GG::UV), 0)) =
+          c * CH + (tid + NT * i) / GG::UV < ntok ? rv[c][i] : u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
     // L += phi(K_c)^T V_c, z += colsum phi(K_c).
 #pragma unroll
