@@ -94,16 +94,26 @@ __device__ __forceinline__ float dpfp_feat(const float* x, int t, int base_g, in
 }
 
 // Rows [0, nv) of a row-major [.][W] tensor starting at src, widened to float
-// into LDS (row stride DS floats); rows nv..63 become zeros.
+// into LDS (row stride DS floats); rows nv..63 become zeros.  The loads carry
+// no condition (rows past nv re-read row nv - 1 and are replaced by zeros): a
+// conditional load becomes a branch at which the compiler waits for every load
+// in flight, which would turn the loads into one round trip each.
 template <typename T, int W, int DS>
 __device__ __forceinline__ void load_rows(float* dst, const T* src, int nv, int tid) {
   constexpr int G = CH * W / 4;  // groups of four elements
   static_assert(G % NT == 0, "whole groups per thread");
+  float4 x[G / NT];
+  if (nv > 0) {
+#pragma unroll
+    for (int u = 0; u < G / NT; ++u) {
+      const int e = (u * NT + tid) * 4, r = e / W, c = e % W;
+      x[u] = load4<T>(src + (size_t)min(r, nv - 1) * W + c);
+    }
+  }
 #pragma unroll
   for (int u = 0; u < G / NT; ++u) {
     const int e = (u * NT + tid) * 4, r = e / W, c = e % W;
-    const float4 x = r < nv ? load4<T>(src + (size_t)r * W + c) : float4{0.f, 0.f, 0.f, 0.f};
-    *reinterpret_cast<float4*>(dst + r * DS + c) = x;
+    *reinterpret_cast<float4*>(dst + r * DS + c) = r < nv ? x[u] : float4{0.f, 0.f, 0.f, 0.f};
   }
 }
 
@@ -263,7 +273,7 @@ __global__ __launch_bounds__(NT) void fm_out_kernel(const T* __restrict__ q, con
   f32x4 pf[PF];
 #pragma unroll
   for (int u = 0; u < PF; ++u) pf[u] = *reinterpret_cast<const f32x4*>(Sb + (u * NT + tid) * 4);
-  float pz = tid < FS ? zb[tid] : 0.f;
+  float pz = zb[min(tid, FS - 1)];  // lanes tid >= FS never store theirs
   load_rows<T, D, XS>(sm.Qr, qh + (size_t)q0 * D, nq, tid);
   if (intra_dpfp) load_rows<T, D, XS>(sm.Kr, kh + (size_t)q0 * D, nq, tid);  // the block is this chunk
   f32x4 num[TM];  // num^T tiles: lane (n, g) holds values 16 vb + 4g + i of query 16w + n
@@ -287,11 +297,12 @@ __global__ __launch_bounds__(NT) void fm_out_kernel(const T* __restrict__ q, con
         *reinterpret_cast<f32x4*>(&sm.Ss[f * M + ss_col<M>(f, c)]) = pf[u];
       }
       if (tid < FS) sm.zs[tid] = pz;
-      if (s + 1 < NS) {  // next slice in flight during this one
+      {  // next slice in flight during this one (the last slice re-reads itself; unconditional loads, as in load_rows)
+        const int sn = min(s + 1, NS - 1);
 #pragma unroll
         for (int u = 0; u < PF; ++u)
-          pf[u] = *reinterpret_cast<const f32x4*>(Sb + (size_t)(s + 1) * sstride + (u * NT + tid) * 4);
-        if (tid < FS) pz = zb[(size_t)(s + 1) * npre * FS + tid];
+          pf[u] = *reinterpret_cast<const f32x4*>(Sb + (size_t)sn * sstride + (u * NT + tid) * 4);
+        pz = zb[(size_t)sn * npre * FS + min(tid, FS - 1)];
       }
       __syncthreads();
       // Inter-block part: num^T += S_s^T phi_s(Q)^T, den += phi_s(Q) z_s; for DPFP
