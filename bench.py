@@ -17,11 +17,14 @@ synth module), copied to the GPU before the timed region.  Timing: W untimed
 warm-up steps, then K timed steps launched back to back and bracketed by a
 device synchronisation; HIP events at both ends of the timed region are recorded
 on the stream the library launches on (torch's current stream, passed to the C
-ABI), and the average launch duration is the region over its launches.  The default
-warm-up is long enough (>= 50 ms of back-to-back launches) for the GPU's clocks
-to settle: the first ~100 launches of the causal kernel after idle run up to 15%
-slower than the steady state.  The CPU baseline is
-the oracle timed on the host cores on a bounded sample of the same workload.
+ABI), and the average launch duration is the region over its launches.  Between
+the W warm-up steps and the timed region, untimed steps run back to back for at
+least --settle-ms (default 200 ms) whatever W is: the GPU's clocks ramp up under
+sustained load, and the first ~100 launches of the causal kernel after idle run
+up to 17% slower than the steady state.  The record states the settle phase
+("settle"), and the median, minimum and maximum of individually timed launches
+beside the mean ("launch_us").  The CPU baseline is the oracle timed on the host
+cores on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -87,6 +90,45 @@ def traffic_from_profiles(workload: str):
     if not m_hash or not m_bytes or m_hash.group(1) != source_hash(workload):
         return None
     return float(m_bytes.group(1))
+
+
+def mfma_from_profiles(workload: str):
+    """MFMA busy fraction from a committed SQ counter summary, if it matches the
+    current kernel sources (else None)."""
+    path = os.path.join(PROFILE_DIR, f"{workload}_sq_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"source_hash:\s*([0-9a-f]+)", text)
+    m_busy = re.search(r"mfma_busy_frac:\s*([0-9.eE+-]+)", text)
+    if not m_hash or not m_busy or m_hash.group(1) != source_hash(workload):
+        return None
+    return float(m_busy.group(1))
+
+
+def runtime_info(torch) -> dict:
+    """ROCm/HIP runtime and driver versions, the device and the host CPU."""
+    import ctypes
+    info = {"torch": torch.__version__, "torch_hip": getattr(torch.version, "hip", None),
+            "device": torch.cuda.get_device_name(0), "cpu_model": cpu_model(),
+            "host_cores": len(os.sched_getaffinity(0))}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        for key, fn in (("hip_runtime_version", "hipRuntimeGetVersion"), ("hip_driver_version", "hipDriverGetVersion")):
+            val = ctypes.c_int(0)
+            if getattr(hip, fn)(ctypes.byref(val)) == 0:
+                info[key] = val.value
+    except OSError:
+        pass
+    try:
+        info["rocm"] = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        pass
+    try:
+        info["amdgpu_driver"] = open("/sys/module/amdgpu/version").read().strip()
+    except OSError:
+        pass
+    return info
 
 
 def cpu_model() -> str:
@@ -235,6 +277,9 @@ def main():
                     help="cold caches: write a 1 GiB buffer before every launch and time each launch with its own "
                          "events (the default times back-to-back launches)")
     ap.add_argument("--oracle-budget", type=float, default=20.0)
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="untimed back-to-back steps after the warm-up, at least this long, so that the timed "
+                         "region runs at settled clocks whatever --warmup is")
     args = ap.parse_args()
 
     long_steps = {"decode": (20, 5), "deltanet_decode": (20, 5), "softmax_decode": (5, 2), "copy": (20, 5)}
@@ -435,6 +480,19 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    # Clock settle: untimed steps back to back for at least --settle-ms of wall
+    # time (synchronising every few steps keeps the host close to the device).
+    settle_steps = 0
+    settle0 = time.perf_counter()
+    if not args.flush:
+        while (time.perf_counter() - settle0) * 1e3 < args.settle_ms:
+            step()
+            settle_steps += 1
+            if settle_steps % 8 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+    settle_ms = (time.perf_counter() - settle0) * 1e3
+
     # Timed region: K steps launched back to back on the library's stream, HIP
     # events at both ends.  The average launch duration is the region's time over
     # the launches in it (the launches queue without host gaps, so this matches
@@ -468,6 +526,25 @@ def main():
         wall = time.perf_counter() - wall0
         total_ms = t_start.elapsed_time(t_end)
     launch_ms = total_ms / (K * launches_per_step)
+
+    # Individually timed launches (after the timed region, same settled state):
+    # each launch between its own pair of events, for the median, min and max
+    # beside the mean of the back-to-back region.
+    n_single = min(K * launches_per_step, 512)
+    singles = []
+    for i in range(n_single):
+        a, b = events(2)
+        if args.flush:
+            flush_buf.fill_(1.0)
+        a.record(stream)
+        launch(i % launches_per_step)
+        b.record(stream)
+        singles.append((a, b))
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(b) * 1e3 for a, b in singles)
+    launch_us = {"mean_back_to_back": round(launch_ms * 1e3, 2), "median": round(us[len(us) // 2], 2),
+                 "min": round(us[0], 2), "max": round(us[-1], 2), "n": len(us),
+                 "note": "median/min/max of launches timed one by one with their own events"}
 
     ms_per_step = total_ms / K
     value = units * K / (total_ms / 1e3)
@@ -546,6 +623,11 @@ def main():
         "timing": ("cold: 1 GiB written before every launch, per-launch events summed" if args.flush
                    else "back-to-back launches between two events"),
         "cpu_baseline": cpu,
+        "launch_us": launch_us,
+        "settle": {"steps": settle_steps, "ms": round(settle_ms, 1),
+                   "note": "untimed back-to-back steps between the warm-up and the timed region"},
+        "mfma_busy_frac": mfma_from_profiles(args.workload),
+        "env": runtime_info(torch),
         "wall_s": round(wall, 4),
         "source_hash": source_hash(args.workload),
     }

@@ -34,7 +34,8 @@
  * bf16 inputs are read exactly; accumulation and state are float32; a bf16
  * output is rounded to nearest even once, from float32.
  * (D, M) must be one of {32, 64} x {32, 64}.  B, H, N may be 0 (nothing to
- * compute); negative sizes are rejected.
+ * compute); negative sizes are rejected, and so are N (or Lmax) above 2^30 and
+ * B*H above 2^30.
  * stream: a hipStream_t passed as void* (NULL = the default stream).  All work
  * is enqueued on it asynchronously; the library never synchronises, never
  * allocates device memory and keeps no pointer after returning.

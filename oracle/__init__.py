@@ -49,8 +49,12 @@ def _load():
     global _lib
     with _lock:
         if _lib is None:
-            build()
-            lib = ctypes.CDLL(_SO)
+            # LINATTN_ORACLE_LIB names another build of the same source (the
+            # sanitizer test loads one built with ASan and UBSan).
+            alt = os.environ.get("LINATTN_ORACLE_LIB")
+            if not alt:
+                build()
+            lib = ctypes.CDLL(alt or _SO)
             lib.oracle_phi.restype = ctypes.c_double
             lib.oracle_phi.argtypes = [ctypes.c_double]
             lib.oracle_set_threads.argtypes = [ctypes.c_int]

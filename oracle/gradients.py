@@ -86,3 +86,53 @@ def causal_loss(q, k, v, dO, form: str = "recurrent") -> float:
             for h in range(q.shape[1]):
                 total += float((fwd(q[b, h], k[b, h], v[b, h]) * dO[b, h]).sum())
     return total
+
+
+def dq_term_scale(q, k, v, dO) -> np.ndarray:
+    """Size of the terms dq is formed from, per (b, h, token) row, float64 [B,H,N].
+
+    For the error bound of the query gradient only (test infrastructure).  By
+    the quotient rule on eq.(12), the gradient of L with respect to phi(q_i) is
+    (S_i dO_i - z_i (dO_i . o_i)) / den_i with den_i = phi(q_i)^T z_i: two
+    vectors that can nearly cancel, so that any float32 evaluation of a row
+    carries an error of float32 rounding times their size, however small the
+    row itself is.  Returned: || phi'(q_i) * max(|S_i dO_i|, |z_i (dO_i . o_i)|) / den_i ||_inf,
+    with phi'(x) = 1 (x > 0), exp(x) otherwise.  The formula is pinned against
+    the autograd gradient in the CPU tests.
+    """
+    q, k, v, dO = _t64(q), _t64(k), _t64(v), _t64(dO)
+    B, H, N, D = q.shape
+    out = np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            if N == 0:
+                continue
+            fq, fk = _phi(q[b, h]), _phi(k[b, h])
+            S = torch.cumsum(fk[:, :, None] * v[b, h][:, None, :], dim=0)   # [N, D, M]
+            z = torch.cumsum(fk, dim=0)                                      # [N, D]
+            den = (fq * z).sum(dim=1, keepdim=True)
+            o = torch.einsum("nd,ndm->nm", fq, S) / den
+            t1 = torch.einsum("ndm,nm->nd", S, dO[b, h]).abs()
+            t2 = (z * (dO[b, h] * o).sum(dim=1, keepdim=True)).abs()
+            dphi = torch.where(q[b, h] > 0, torch.ones_like(fq), torch.exp(torch.clamp(q[b, h], max=0.0)))
+            out[b, h] = (dphi * torch.maximum(t1, t2) / den).amax(dim=1).numpy()
+    return out
+
+
+def dq_from_terms(q, k, v, dO) -> np.ndarray:
+    """dq from the quotient-rule form above, float64 [B,H,N,D]; used only by the
+    CPU pin that ties dq_term_scale's formula to the autograd gradient."""
+    q, k, v, dO = _t64(q), _t64(k), _t64(v), _t64(dO)
+    B, H, N, D = q.shape
+    out = np.zeros((B, H, N, D))
+    for b in range(B):
+        for h in range(H):
+            fq, fk = _phi(q[b, h]), _phi(k[b, h])
+            S = torch.cumsum(fk[:, :, None] * v[b, h][:, None, :], dim=0)
+            z = torch.cumsum(fk, dim=0)
+            den = (fq * z).sum(dim=1, keepdim=True)
+            o = torch.einsum("nd,ndm->nm", fq, S) / den
+            g = (torch.einsum("ndm,nm->nd", S, dO[b, h]) - z * (dO[b, h] * o).sum(dim=1, keepdim=True)) / den
+            dphi = torch.where(q[b, h] > 0, torch.ones_like(fq), torch.exp(torch.clamp(q[b, h], max=0.0)))
+            out[b, h] = (dphi * g).numpy()
+    return out

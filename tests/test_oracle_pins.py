@@ -428,6 +428,30 @@ def test_bwd_single_token_passes_values_through():
     assert np.abs(dq).max() < 1e-13 and np.abs(dk).max() < 1e-13
 
 
+def test_bwd_first_query_gradient_vanishes():
+    """o_1 = v_1 for any q_1 and q_1 enters no later output, so dq_1 = 0 at every N
+    (the GPU tests treat that row as identically zero); no other row of dq is."""
+    q, k, v, dO = _bwd_inputs(2, 2, 50, 8, 6, 33)
+    dq, _, _ = oracle.causal_bwd(q, k, v, dO)
+    assert np.abs(dq[:, :, 0]).max() < 1e-14 * np.abs(dq).max()
+    assert np.abs(dq[:, :, 1:]).max(axis=-1).min() > 1e-6 * np.abs(dq).max()
+
+
+def test_bwd_quotient_rule_form_and_term_scale():
+    """The query gradient as the quotient rule writes it, (S_i dO_i - z_i (dO_i . o_i)) / den_i
+    times phi'(q_i), equals the autograd gradient; the term scale the GPU tests use
+    as a floor bounds every row (a difference of two terms is at most twice the
+    larger) and is far above the row where the two terms cancel."""
+    from oracle import gradients
+    q, k, v, dO = _bwd_inputs(2, 2, 60, 8, 5, 35)
+    dq, _, _ = oracle.causal_bwd(q, k, v, dO)
+    assert mat_rel_err(gradients.dq_from_terms(q, k, v, dO), dq) < 1e-12
+    scale = gradients.dq_term_scale(q, k, v, dO)
+    rows = np.abs(dq).max(axis=-1)
+    assert np.all(rows <= 2.0 * scale * (1 + 1e-12))
+    assert np.all(scale[:, :, 0] > 1e6 * rows[:, :, 0])   # the first token: terms cancel exactly
+
+
 def test_bwd_is_causal():
     """dq_i depends on keys and values j <= i only; dk_j, dv_j on output gradients i >= j only."""
     q, k, v, dO = _bwd_inputs(1, 2, 40, 6, 4, 41)

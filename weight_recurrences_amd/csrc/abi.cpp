@@ -33,6 +33,9 @@ int check_shape(int B, int H, int N, int D, int M, int dtype) {
   if (dtype != LINATTN_F32 && dtype != LINATTN_BF16) return LINATTN_ERR_DTYPE;
   if (B < 0 || H < 0 || N < 0 || D <= 0 || M <= 0) return LINATTN_ERR_SHAPE;
   if (!dm_supported(D, M)) return LINATTN_ERR_UNSUPPORTED;
+  // Token indices and block counts are 32-bit in the kernels and their launch
+  // arithmetic (N + block - 1 included): at most 2^30 tokens per sequence.
+  if (N > (1 << 30)) return LINATTN_ERR_SHAPE;
   const long long BH = (long long)B * H;
   if (BH > (1LL << 30)) return LINATTN_ERR_SHAPE;
   const long long rows = BH * N;
@@ -40,7 +43,7 @@ int check_shape(int B, int H, int N, int D, int M, int dtype) {
   if (rows > (1LL << 46) / 64) return LINATTN_ERR_SHAPE;  // bytes of q stay far below 2^63
   if (BH > 0 && N > 0) {
     const int tb = la::causal_block_tokens((int)BH, N);
-    const long long nblk = (N + tb - 1) / tb;
+    const long long nblk = ((long long)N + tb - 1) / tb;
     if (nblk * BH > (long long)INT32_MAX) return LINATTN_ERR_SHAPE;
   }
   return LINATTN_OK;

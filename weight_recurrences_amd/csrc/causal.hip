@@ -826,13 +826,11 @@ hipError_t launch_state_copy(const float* S_init, const float* z_init, float* S_
 }
 
 // bf16 causal calls take the single-pass kernel unless LINATTN_CAUSAL_BF16_PATH=blocked
-// selects the three-kernel path (kept for comparisons).
+// selects the three-kernel path (kept for comparisons).  Read at every call, by
+// the workspace query and by the launch alike.
 static bool bf16_fused() {
-  static const bool fused = [] {
-    const char* e = getenv("LINATTN_CAUSAL_BF16_PATH");
-    return !(e && strcmp(e, "blocked") == 0);
-  }();
-  return fused;
+  const char* e = getenv("LINATTN_CAUSAL_BF16_PATH");
+  return !(e && strcmp(e, "blocked") == 0);
 }
 
 size_t causal_ws_bytes(int BH, int N, int D, int M, int bf16) {

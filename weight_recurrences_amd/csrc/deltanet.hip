@@ -296,14 +296,14 @@ __global__ __launch_bounds__(256) void memory_copy_kernel(const float* W0, float
 }
 
 // Sequences run through the chunk-parallel kernels unless
-// LINATTN_DELTANET_PATH=sequential selects the token-by-token kernel (kept for
-// comparisons; it needs no workspace).
+// LINATTN_DELTANET_PATH=sequential selects the token-by-token kernel (one
+// wavefront-reduction chain per row of W; it needs no workspace).  The variable
+// is read at every call, by the workspace query and by the launch alike, so a
+// call made with a workspace sized for the other path is still validated
+// against the path it takes.
 static bool deltanet_chunked() {
-  static const bool chunked = [] {
-    const char* e = getenv("LINATTN_DELTANET_PATH");
-    return !(e && strcmp(e, "sequential") == 0);
-  }();
-  return chunked;
+  const char* e = getenv("LINATTN_DELTANET_PATH");
+  return !(e && strcmp(e, "sequential") == 0);
 }
 
 size_t deltanet_ws_bytes(int BH, int N, int D, int M) {
