@@ -65,7 +65,12 @@
 extern "C" {
 #endif
 
-#define LINATTN_ABI_VERSION 3  /* 2: deltanet_fwd takes a workspace; 3: the feature-map and softmax decode entry points */
+#define LINATTN_ABI_VERSION 4  /* 2: deltanet_fwd takes a workspace; 3: the feature-map and softmax decode entry points;
+                                  4: linattn_noncausal_fwd_noalloc */
+
+/* Size of the library-owned device scratch behind linattn_noncausal_fwd_noalloc
+ * (one copy per GPU the library runs on, held until the process ends). */
+#define LINATTN_NOALLOC_SCRATCH_BYTES (32u << 20)
 
 typedef enum { LINATTN_F32 = 0, LINATTN_BF16 = 1 } linattn_dtype_t;
 
@@ -132,6 +137,25 @@ size_t linattn_noncausal_workspace_bytes(int B, int H, int N, int D, int M, int 
 int linattn_noncausal_fwd(const void* q, const void* k, const void* v, void* o,
                           int B, int H, int N, int D, int M, int dtype,
                           void* ws, size_t ws_bytes, void* stream);
+
+/* linattn_noncausal_fwd for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, with the workspace taken from a
+ * static device array of LINATTN_NOALLOC_SCRATCH_BYTES owned by the library,
+ * so the caller passes only inputs and outputs.  The call allocates nothing
+ * (no hipMalloc, no allocating library routine).
+ * Limit: the problem must fit the scratch, i.e.
+ *   linattn_noncausal_workspace_bytes(B, H, N, D, M, dtype) <= LINATTN_NOALLOC_SCRATCH_BYTES
+ * (at D = M = 64 that holds for B*H up to about 1000 heads at any N);
+ * a larger problem returns LINATTN_ERR_WORKSPACE before anything is enqueued.
+ * Every call on one GPU shares that GPU's scratch: calls that overlap in time
+ * on one GPU (concurrent streams, or several host threads) race and must be
+ * serialised by the caller.  The scratch keeps whatever the last call left;
+ * this path writes every part of it before reading it.  The first call on a
+ * device looks up that device's copy (hipGetSymbolAddress); a failure there
+ * returns LINATTN_ERR_HIP.  Other errors as linattn_noncausal_fwd. */
+int linattn_noncausal_fwd_noalloc(const void* q, const void* k, const void* v, void* o,
+                                  int B, int H, int N, int D, int M, int dtype, void* stream);
 
 /* One autoregressive step of the RNN form, eq.(18)-(20), for B*H independent
  * states, in place:

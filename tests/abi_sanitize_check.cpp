@@ -71,6 +71,7 @@ hipError_t launch_deltanet_step(const void*, const void*, const void*, const voi
                                 int, hipStream_t) {
   return record(BH, 1);
 }
+void* noalloc_scratch() { return (void*)(uintptr_t)((uint64_t)63 << 36); }
 }  // namespace la
 
 // ----------------------------------------------------------------- cases
@@ -160,6 +161,22 @@ int main() {
   CHECK_NOLAUNCH("noncausal ws aliases q",
                  linattn_noncausal_fwd(P(0), P(1), P(2), P(3), 2, 16, 4096, 64, 64, 1, P(0), BIG, nullptr),
                  LINATTN_ERR_ALIAS);
+
+  // ---- non-causal without allocation (static scratch)
+  CHECK("noncausal noalloc ok", linattn_noncausal_fwd_noalloc(P(0), P(1), P(2), P(3), 2, 16, 32768, 64, 64, 1, nullptr),
+        LINATTN_OK);
+  CHECK_NOLAUNCH("noncausal noalloc too big",
+                 linattn_noncausal_fwd_noalloc(P(0), P(1), P(2), P(3), 64, 64, 4096, 64, 64, 1, nullptr),
+                 LINATTN_ERR_WORKSPACE);
+  CHECK_NOLAUNCH("noncausal noalloc alias",
+                 linattn_noncausal_fwd_noalloc(P(0), P(1), P(2), P(1), 2, 16, 4096, 64, 64, 1, nullptr),
+                 LINATTN_ERR_ALIAS);
+  CHECK_NOLAUNCH("noncausal noalloc null", linattn_noncausal_fwd_noalloc(P(0), nullptr, P(2), P(3), 2, 16, 4096, 64,
+                                                                         64, 1, nullptr),
+                 LINATTN_ERR_NULL);
+  CHECK_NOLAUNCH("noncausal noalloc empty", linattn_noncausal_fwd_noalloc(nullptr, nullptr, nullptr, nullptr, 2, 16,
+                                                                          0, 64, 64, 1, nullptr),
+                 LINATTN_OK);
 
   // ---- backward
   CHECK("bwd ok", linattn_causal_bwd(P(0), P(1), P(2), P(3), P(4), P(5), P(6), 2, 16, 32768, 64, 64, 1, P(9), BIG,

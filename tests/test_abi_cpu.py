@@ -37,7 +37,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.linattn_abi_version() == 3
+    assert lib.linattn_abi_version() == 4
     for code, name in _lib.STATUS.items():
         assert lib.linattn_status_str(code).decode() == name
     assert lib.linattn_status_str(99).decode() == "LINATTN_ERR_UNKNOWN"
@@ -130,6 +130,30 @@ def test_noncausal_validation(lib):
     assert f(*bad) == ALIAS
     bad = list(args); bad[0] = Q + 2
     assert f(*bad) == ALIGN
+
+
+@no_gpu
+def test_noncausal_noalloc_validation(lib):
+    """The allocation-free variant validates like linattn_noncausal_fwd and refuses,
+    before any HIP call, a problem whose workspace exceeds the static scratch."""
+    f = lib.linattn_noncausal_fwd_noalloc
+    limit = 32 << 20
+    assert lib.linattn_noncausal_workspace_bytes(2, 16, 32768, 64, 64, 1) <= limit
+    args = [Q, K, V, O, 2, 16, 32768, 64, 64, 1, None]
+    bad = list(args); bad[3] = None
+    assert f(*bad) == NULL
+    bad = list(args); bad[9] = 7
+    assert f(*bad) == DTYPE
+    bad = list(args); bad[7] = 48
+    assert f(*bad) == UNSUP
+    bad = list(args); bad[3] = K
+    assert f(*bad) == ALIAS
+    bad = list(args); bad[0] = Q + 2
+    assert f(*bad) == ALIGN
+    assert lib.linattn_noncausal_workspace_bytes(64, 64, 4096, 64, 64, 1) > limit
+    big = list(args); big[4], big[5], big[6] = 64, 64, 4096
+    assert f(*big) == WS
+    assert f(None, None, None, None, 2, 16, 0, 64, 64, 1, None) == OK
 
 
 @no_gpu

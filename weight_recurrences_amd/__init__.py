@@ -17,7 +17,7 @@ import torch
 
 from ._lib import BF16, F32, FMAP_DPFP, FMAP_POLY2, LinAttnError, check, load
 
-__all__ = ["causal", "causal_bwd", "fmap", "fmap_dim", "fmap_workspace_bytes", "FMAP_DPFP", "FMAP_POLY2", "causal_bwd_workspace_bytes", "noncausal", "decode_step", "deltanet", "deltanet_decode_step", "causal_workspace_bytes",
+__all__ = ["causal", "causal_bwd", "fmap", "fmap_dim", "fmap_workspace_bytes", "FMAP_DPFP", "FMAP_POLY2", "causal_bwd_workspace_bytes", "noncausal", "noncausal_noalloc", "decode_step", "deltanet", "deltanet_decode_step", "causal_workspace_bytes",
            "noncausal_workspace_bytes", "deltanet_workspace_bytes", "LinAttnError", "abi_version"]
 
 _DT = {torch.float32: F32, torch.bfloat16: BF16}
@@ -209,6 +209,24 @@ def noncausal(q, k, v, *, out=None, workspace=None):
     rc = lib.linattn_noncausal_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, D, M, dt, _ptr(ws), need,
                                    _stream(dev))
     check(rc, "linattn_noncausal_fwd")
+    return o
+
+
+def noncausal_noalloc(q, k, v, *, out=None):
+    """Non-causal linear attention through ``linattn_noncausal_fwd_noalloc``: no
+    workspace argument and no device allocation inside the call (the library's
+    static per-GPU scratch; calls that overlap on one GPU race).  Returns o."""
+    lib = load()
+    dev = _dev(q, k, v)
+    B, H, N, D = q.shape
+    M = v.shape[-1]
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v shapes/dtypes disagree")
+    dt = _dtype_code(q)
+    o = out if out is not None else torch.empty((B, H, N, M), dtype=q.dtype, device=dev)
+    _dev(q, o)
+    rc = lib.linattn_noncausal_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, D, M, dt, _stream(dev))
+    check(rc, "linattn_noncausal_fwd_noalloc")
     return o
 
 

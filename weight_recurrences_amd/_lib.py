@@ -37,6 +37,7 @@ SIGNATURES = {
     "linattn_causal_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
     "linattn_noncausal_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "linattn_noncausal_fwd": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
+    "linattn_noncausal_fwd_noalloc": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
     "linattn_decode_step": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
     "deltanet_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "deltanet_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),

@@ -158,6 +158,29 @@ int linattn_noncausal_fwd(const void* q, const void* k, const void* v, void* o, 
       la::launch_noncausal(q, k, v, o, (int)BH, N, D, M, dtype == LINATTN_BF16, ws, (hipStream_t)stream));
 }
 
+int linattn_noncausal_fwd_noalloc(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int D,
+                                  int M, int dtype, void* stream) {
+  int st = check_shape(B, H, N, D, M, dtype);
+  if (st) return st;
+  const long long BH = (long long)B * H, es = esize(dtype);
+  if (BH * N == 0) return LINATTN_OK;
+  if (!q || !k || !v || !o) return LINATTN_ERR_NULL;
+  if ((st = check_align({q, k, v, o}))) return st;
+  // The same kernels and partition as linattn_noncausal_fwd; their workspace
+  // (per-block state shares and per-head totals, all written before they are
+  // read, so nothing needs clearing) must fit the static scratch.
+  const size_t need = la::noncausal_ws_bytes((int)BH, N, D, M, dtype == LINATTN_BF16);
+  if (need > (size_t)LINATTN_NOALLOC_SCRATCH_BYTES) return LINATTN_ERR_WORKSPACE;
+  const long long nq = BH * N * D * es, nv = BH * N * M * es;
+  const Span sq(q, nq), sk(k, nq), sv(v, nv), so(o, nv);
+  for (const Span& x : {sq, sk, sv})
+    if (so.overlaps(x)) return LINATTN_ERR_ALIAS;
+  void* ws = la::noalloc_scratch();
+  if (!ws) return LINATTN_ERR_HIP;
+  return hip_status(
+      la::launch_noncausal(q, k, v, o, (int)BH, N, D, M, dtype == LINATTN_BF16, ws, (hipStream_t)stream));
+}
+
 int linattn_decode_step(const void* q, const void* k, const void* v, void* o, float* S, float* z, int B, int H,
                         int D, int M, int dtype, void* stream) {
   int st = check_shape(B, H, 1, D, M, dtype);

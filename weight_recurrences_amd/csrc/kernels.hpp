@@ -83,6 +83,9 @@ hipError_t launch_deltanet_chunked(const void* q, const void* k, const void* v, 
                                    int N, int D, int M, int bf16, const float* W0, float* W_out, void* ws,
                                    hipStream_t stream);
 size_t deltanet_ws_bytes(int BH, int N, int D, int M);
+// Device address of the current GPU's copy of the library-owned scratch array
+// (LINATTN_NOALLOC_SCRATCH_BYTES bytes), or NULL if it cannot be obtained.
+void* noalloc_scratch();
 hipError_t launch_deltanet_step(const void* q, const void* k, const void* v, const void* beta, void* o, float* W,
                                 int BH, int D, int M, int bf16, hipStream_t stream);
 
