@@ -29,8 +29,16 @@ __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) { return f2bf(l
 
 // phi(x) = elu(x) + 1 with alpha = 1 ("Transformers are RNNs", §3.2.1 eq.(7)):
 // x + 1 for x > 0, exp(x) otherwise (the exp form keeps relative accuracy for
-// very negative x).
-__device__ __forceinline__ float phi(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+// very negative x).  Evaluated branch-free as max(min(exp(x), 1), x + 1): since
+// exp(x) >= 1 + x with equality only at 0, this is x + 1 for x > 0 and exp(x)
+// for x <= 0 (up to one rounding of exp near 0, where the two agree within an
+// ulp); -inf maps to 0 and NaN propagates.  The min is the clamp modifier of
+// v_exp_f32 and the max one v_maximum3_f32 (IEEE maximum, NaN-propagating): five
+// VALU instructions with the unpack, and no compare and select.
+__device__ __forceinline__ float phi(float x) {
+  const float e = __builtin_amdgcn_fmed3f(__expf(x), 0.f, 1.f);
+  return __builtin_elementwise_maximum(e, x + 1.f);
+}
 
 template <typename T> __device__ __forceinline__ float ld_scalar(const T* p);
 template <> __device__ __forceinline__ float ld_scalar<float>(const float* p) { return *p; }
