@@ -273,9 +273,11 @@ def main():
                              "softmax_decode", *FMAPS,
                              "causal_mid", "causal_small", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--flush", action="store_true",
-                    help="cold caches: write a 1 GiB buffer before every launch and time each launch with its own "
-                         "events (the default times back-to-back launches)")
+    ap.add_argument("--flush", nargs="?", const="read", choices=["read", "write"], default=None,
+                    help="cold caches: before every launch, read (default) or write a 1 GiB buffer, and time each "
+                         "launch with its own events (the default times back-to-back launches).  A read evicts the "
+                         "L2s and the Infinity Cache without leaving dirty lines; after a write, the launch also pays "
+                         "the write-back of the lines it evicts")
     ap.add_argument("--oracle-budget", type=float, default=20.0)
     ap.add_argument("--settle-ms", type=float, default=200.0,
                     help="untimed back-to-back steps after the warm-up, at least this long, so that the timed "
@@ -502,13 +504,25 @@ def main():
     wall0 = time.perf_counter()
     if args.flush:
         # Cold caches: a 1 GiB buffer (4x the Infinity Cache, 32x the L2s) is
-        # written before every launch, outside the launch's own pair of events;
-        # the time is the sum of the launches' intervals.
-        flush_buf = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        # read (summed) before every launch, outside the launch's own pair of
+        # events; the time is the sum of the launches' intervals.  Reading
+        # leaves only clean lines in the caches; "write" fills the buffer
+        # instead, and the next launch then also pays the write-back of the
+        # dirty lines it evicts.
+        flush_buf = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        flush_out = torch.empty((), dtype=torch.float32, device=dev)
+
+        def flush():
+            if args.flush == "write":
+                flush_buf.fill_(1.0)
+            else:
+                torch.sum(flush_buf, dim=0, out=flush_out)
+        flush()
+        torch.cuda.synchronize()
         pairs = []
         for _ in range(K):
             for t in range(launches_per_step):
-                flush_buf.fill_(1.0)
+                flush()
                 a, b = events(2)
                 a.record(stream)
                 launch(t)
@@ -535,7 +549,7 @@ def main():
     for i in range(n_single):
         a, b = events(2)
         if args.flush:
-            flush_buf.fill_(1.0)
+            flush()
         a.record(stream)
         launch(i % launches_per_step)
         b.record(stream)
@@ -620,8 +634,8 @@ def main():
         "config": {"workload": names[args.workload], "B": w.B, "H": w.H, "N": w.N, "D": w.D, "M": w.M,
                    "parallelism": "single GPU"},
         "roofline": roofline,
-        "timing": ("cold: 1 GiB written before every launch, per-launch events summed" if args.flush
-                   else "back-to-back launches between two events"),
+        "timing": (f"cold: 1 GiB {'read' if args.flush == 'read' else 'written'} before every launch, per-launch "
+                   "events summed" if args.flush else "back-to-back launches between two events"),
         "cpu_baseline": cpu,
         "launch_us": launch_us,
         "settle": {"steps": settle_steps, "ms": round(settle_ms, 1),
