@@ -56,13 +56,12 @@ def test_workspace_sizes(lib):
     # a single block per head needs no workspace
     assert lib.linattn_causal_workspace_bytes(1, 1, 256, 32, 32, 0) == 0
     assert lib.linattn_noncausal_workspace_bytes(1, 1, 256, 32, 32, 0) == 2 * (32 * 32 + 32) * 4
-    # delta rule: per chunk of 64 tokens kh, Wc (64 x D), Uc (64 x M), the chunk's
-    # affine map A (D x D) and Bc (M x D), and the memory at the chunk start (M x D);
-    # past 16 chunks, per group of 8 chunks (two-level scan) the composed map (A and
-    # Bc) and the memory at the group start
-    assert lib.deltanet_workspace_bytes(4, 8, 4096, 64, 64, 0) == (32 * 64 * 6 + 32 * 8 * 3) * 64 * 64 * 4
-    assert lib.deltanet_workspace_bytes(1, 2, 1024, 64, 64, 0) == 2 * 16 * 6 * 64 * 64 * 4
-    assert lib.deltanet_workspace_bytes(1, 1, 65, 32, 64, 1) == 2 * (2 * 64 * 32 + 64 * 64 + 32 * 32 + 2 * 64 * 32) * 4
+    # delta rule, per chunk of 64 tokens: kh as bf16 head and tail (64 x D x 4 bytes) and
+    # T as bf16 head and tail in six 64-lane operand blocks of 32 bytes per lane
+    rec64, rec32 = 64 * 64 * 4 + 6 * 64 * 32, 64 * 32 * 4 + 6 * 64 * 32
+    assert lib.deltanet_workspace_bytes(4, 8, 4096, 64, 64, 0) == 32 * 64 * rec64
+    assert lib.deltanet_workspace_bytes(1, 2, 1024, 64, 64, 0) == 2 * 16 * rec64
+    assert lib.deltanet_workspace_bytes(1, 1, 65, 32, 64, 1) == 2 * rec32
     assert lib.deltanet_workspace_bytes(4, 8, 0, 64, 64, 0) == 0
     for bad in [(1, 1, 256, 48, 32, 0), (1, 1, 256, 32, 32, 5), (-1, 1, 4, 32, 32, 0)]:
         assert lib.linattn_causal_workspace_bytes(*bad) == 0

@@ -355,12 +355,11 @@ def test_deltanet_ragged(dtype, D, M, N):
 
 @pytest.mark.parametrize("D,M", [(32, 64), (64, 32), (64, 64)])
 @pytest.mark.parametrize("N", [1025, 1088, 1470, 2113])
-def test_deltanet_two_level_scan(D, M, N):
-    """Past 16 chunks the memory scan composes groups of 8 chunk maps: group counts
-    of 3 to 5 with a partial last group (1 to 7 chunks), from an initial memory,
-    with the final memory written over it."""
+def test_deltanet_many_chunks(D, M, N):
+    """17 to 34 chunks of 64 tokens with a partial last chunk (1 to 63 tokens),
+    from an initial memory, with the final memory written over it."""
     dtype = torch.float32
-    say("deltanet two-level", D, M, N)
+    say("deltanet many chunks", D, M, N)
     q, k, v, beta = synth.qkv_beta(1, 3, N, D, M, dtype=dtype, seed=N + 7 * D + M)
     W0 = torch.randn(1, 3, M, D, generator=torch.Generator().manual_seed(N)) * 0.1
     qg, kg, vg, bg = gpu(q, k, v, beta)
@@ -494,8 +493,11 @@ def test_deltanet_decode_steps_small(dtype, D, M):
 
 
 def test_deltanet_decode_equals_sequence():
-    """N decode steps from W0 give the sequence kernel's outputs and memory (both
-    fp32, one rounding order apart)."""
+    """N decode steps from W0 give the sequence path's outputs and memory.  The
+    decode step is plain fp32; the chunked sequence path forms its products from
+    bf16 head + tail operands (about 2^-17 relative per operand, the tail x tail
+    term dropped), so the two agree to the bound both are held to against the
+    oracle."""
     B, H, N, D, M = 2, 4, 70, 64, 64
     say("deltanet decode vs sequence")
     q, k, v, beta = synth.qkv_beta(B, H, N, D, M, seed=77)
@@ -506,8 +508,8 @@ def test_deltanet_decode_equals_sequence():
     outs = [la.deltanet_decode_step(gq[:, :, t].contiguous(), gk[:, :, t].contiguous(), gv[:, :, t].contiguous(),
                                     gb[:, :, t].contiguous(), W) for t in range(N)]
     o_dec = torch.stack(outs, dim=2)
-    assert row_rel_err(host(o_dec), host(o_seq).double()) < 1e-5
-    assert mat_rel_err(host(W), host(W_seq).double()) < 1e-5
+    assert row_rel_err(host(o_dec), host(o_seq).double()) < 1e-4
+    assert mat_rel_err(host(W), host(W_seq).double()) < 1e-4
 
 
 def test_deltanet_decode_workload_all_heads():

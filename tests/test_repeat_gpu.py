@@ -90,10 +90,10 @@ def test_decode_chain_repeatable():
     assert same(o1, o2) and same(S1, S2) and same(z1, z2)
 
 
-@pytest.mark.parametrize("N", [1000, 4096], ids=["one_level_scan", "two_level_scan"])
+@pytest.mark.parametrize("N", [1000, 4096], ids=["16_chunks", "64_chunks"])
 def test_deltanet_repeatable(N):
-    """16 chunks (one-level memory scan) and 64 chunks (groups of 8 composed
-    first), from an initial memory, outputs and final memory."""
+    """16 chunks (the last one partial) and 64 chunks, from an initial memory,
+    outputs and final memory."""
     w = synth.WORKLOADS["deltanet"]
     say("repeat deltanet", N)
     q, k, v, beta = gpu(*synth.qkv_beta(w.B, w.H, N, w.D, w.M, seed=w.seed + N))

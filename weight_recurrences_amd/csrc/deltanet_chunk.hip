@@ -5,479 +5,560 @@
 // normalisation: per token, kh = phi(k)/sum phi(k), qh likewise,
 // vbar = W kh, W += beta (v - vbar) kh^T, o = W qh (the updated memory).
 //
-// The same recurrence, regrouped by chunks of C = 64 tokens.  With W0 the memory
-// at the chunk start and u_t = beta_t (v_t - W_{t-1} kh_t) the value actually
-// written at token t, W_t = W0 + sum_{s<=t} u_s kh_s^T, so
-//   u_t = beta_t (v_t - W0 kh_t - sum_{s<t} (kh_s . kh_t) u_s).
-// This is a unit lower-triangular system in the rows u_t: with G = Kh Kh^T,
-// L its strictly lower part and B = diag(beta), (I + B L) U = B (V - Kh W0^T),
-// i.e. U = Uc - Wc W0^T with the memory-independent Wc = T Kh and Uc = T V,
-// T = (I + B L)^{-1} B.  Then
-//   W_end = W0 + U^T Kh = W0 A + Bc,  A = I - Wc^T Kh,  Bc = Uc^T Kh,
-//   o_t = W0 qh_t + sum_{s<=t} (qh_t . kh_s) u_s.
-// A chunk maps the memory by an affine map (A, Bc) that does not depend on it,
-// so the only sequential work is one M x D by D x D product per chunk.
+// The same recurrence, regrouped by chunks of C = 64 tokens (exact up to
+// rounding).  With W0 the memory at the chunk start, the values actually written,
+// u_t = beta_t (v_t - W_{t-1} kh_t), satisfy
+//   u_t + beta_t sum_{s<t} (kh_t . kh_s) u_s = beta_t (v_t - W0 kh_t),
+// a unit lower-triangular system.  With G = Kh Kh^T, L its strictly lower part
+// and B = diag(beta): U = T (V - Kh W0^T), T = (I + B L)^{-1} B, and
+//   o_t = W0 qh_t + sum_{s<=t} (qh_t . kh_s) u_s,   W_end = W0 + U^T Kh.
+// T depends on the keys and beta only, so every chunk's T is formed in parallel.
 //
-// Three kernels (fp32 arithmetic throughout, 16x16x4 f32 MFMA tiles):
-//   dn_prep_kernel  per (head, chunk), in parallel: kh, G on MFMA, Wc and Uc by
-//                   forward substitution (one thread per column of [Kh | V]),
-//                   then A and Bc on MFMA; writes Kh, Wc, Uc, A, Bc.
-//   dn_scan_kernel  per head: W <- W A + Bc over the chunks, each wave a
-//                   16-row slice of W; writes the memory at every chunk start.
-//                   Long sequences take two levels: dn_compose_kernel composes
-//                   the maps of groups of 8 chunks in parallel, the scan runs
-//                   over the composed maps, then over each group's chunks.
-//   dn_out_kernel   per (head, chunk), in parallel: U = Uc - Wc W0^T, then
-//                   o = Qh W0^T + (Qh Kh^T, j <= i) U.
+// The update of row m of W involves only row m (and the shared kh, beta), so a
+// head's memory splits into slices of 16 rows that evolve independently.
 //
-// MFMA 16x16x4 f32 layouts (lane l = 16 g + n): operand a = A[n][g], b = B[g][n];
-// the accumulator holds D[4g + r][n] in element r.  The k index of a product may
-// be any permutation shared by both operands; the scan uses k = (tile dt, r) ->
-// d = 16 dt + 4 g + r so that the transposed memory tiles it keeps in registers
-// (its own accumulator layout) are directly the B operand of the next chunk.
+// Two kernels:
+//   dn_prep_kernel   per (head, chunk), all in parallel: kh, G and T in fp32
+//                    (16x16x4 MFMA): the four diagonal 16x16 blocks of T by
+//                    substitution, the blocks below them by doubling,
+//                    T_ab = -T_aa G_ab T_bb for 16-row blocks, then the same for
+//                    the 32-row halves.  Writes kh and T as bf16 head and tail
+//                    (below), laid out as the chain kernel uses them.
+//   dn_chain_kernel  per (head, 16-row slice of W): the chunks in order, the
+//                    slice in registers.  Per chunk: R = V - Kh W^T, U = T R,
+//                    o = Qh W^T + tril(Qh Kh^T) U, W^T += Kh^T U.
+// The chain's products are bf16 MFMA (16x16x32) on operands split into a bf16
+// head and tail (x = h + l to about 2^-17 relative), as h h + h l + l h with fp32
+// accumulation (the tail x tail term, about 2^-16 of a product, is dropped); the
+// memory itself stays fp32 in the accumulators across the chunks.  A wave64
+// VALU instruction takes four cycles, so the sequential kernel keeps its VALU
+// work small: kh arrives already split and in its LDS layout (a plain copy), T
+// already split in MFMA operand order; only qh is formed there.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "lds_tiles.hpp"
 
 namespace la {
 namespace dnc {
 
-constexpr int NT = 256;  // threads per workgroup (4 wavefronts)
-constexpr int C = 64;    // tokens per chunk
+constexpr int NT = 256;    // threads per workgroup (4 wavefronts)
+constexpr int C = 64;      // tokens per chunk
+constexpr int FS = C + 4;  // row stride (floats) of the fp32 C x C tiles in LDS
 
-template <int D, int M>
-struct G {
-  static constexpr int TD = D / 16, TM = M / 16;
-  static constexpr int KS = D + 4;   // row stride of kh / qh tiles in LDS (floats)
-  static constexpr int VS = M + 4;   // row stride of v tiles
-  static constexpr int GS = C + 4;   // row stride of the C x C tiles
-  // Per-chunk records in the workspace (floats).
-  static constexpr size_t KH = (size_t)C * D, WC = (size_t)C * D, UC = (size_t)C * M, AA = (size_t)D * D,
-                          BB = (size_t)M * D, WS = (size_t)M * D;
-};
-
-template <typename T> __device__ __forceinline__ float4 ld4(const T* p) { return load4<T>(p); }
-
-// Loads ROWS rows of a [*, W] tensor (W = D or M) into an fp32 LDS tile with row
-// stride S; with NORM, each row becomes phi(row) / sum(phi(row)).  Rows at or past
-// nt are zero.  Thread p handles units of 4 elements.
-template <typename T, int W, int S, bool NORM, int ROWS = C>
-__device__ __forceinline__ void load_rows(float* tile, const T* src, int nt, int tid) {
-  constexpr int UPR = W / 4;  // 4-element units per row
-  constexpr int NU = ROWS * UPR;
+// ---- bf16 head/tail operands ------------------------------------------------
+// Four floats -> {head01, head23, tail01, tail23} (round to nearest even).
+__device__ __forceinline__ u32x4 split4(f32x4 x) {
+  const uint32_t h0 = cvt_pk(x[0], x[1]), h1 = cvt_pk(x[2], x[3]);
+  return u32x4{h0, h1, cvt_pk(x[0] - lo_of(h0), x[1] - hi_of(h0)), cvt_pk(x[2] - lo_of(h1), x[3] - hi_of(h1))};
+}
+// Eight floats -> eight-element head and tail operands.
+__device__ __forceinline__ void split8(const float (&x)[8], u32x4& h, u32x4& l) {
 #pragma unroll
-  for (int i = 0; i < (NU + NT - 1) / NT; ++i) {
-    const int u = tid + NT * i;
-    if (NU % NT == 0 || u < NU) {  // uniform per group of UPR lanes
-      const int row = u / UPR, c4 = (u % UPR) * 4;
-      const bool ok = row < nt;
-      float4 x = ok ? ld4<T>(src + (size_t)row * W + c4) : float4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (NORM) {
-        x = float4{phi(x.x), phi(x.y), phi(x.z), phi(x.w)};
-        float s = (x.x + x.y) + (x.z + x.w);
-        if constexpr (UPR == 16) s = sum16(s);
-        else s = sum8(s);
-        const float inv = ok ? 1.f / s : 0.f;
-        x = float4{x.x * inv, x.y * inv, x.z * inv, x.w * inv};
-      }
-      *reinterpret_cast<float4*>(&tile[row * S + c4]) = x;
-    }
+  for (int i = 0; i < 4; ++i) {
+    h[i] = cvt_pk(x[2 * i], x[2 * i + 1]);
+    l[i] = cvt_pk(x[2 * i] - lo_of(h[i]), x[2 * i + 1] - hi_of(h[i]));
   }
+}
+// Raw buffer resource over [p, p + bytes): stores at offsets past the end are
+// discarded by the hardware (the third-word flags are the 32-bit data format).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, bytes, 0x00020000);
+}
+template <typename T> __device__ __forceinline__ void store_elem(__amdgpu_buffer_rsrc_t r, int off, float x);
+template <> __device__ __forceinline__ void store_elem<float>(__amdgpu_buffer_rsrc_t r, int off, float x) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, 0, 0);
+}
+template <> __device__ __forceinline__ void store_elem<bf16_t>(__amdgpu_buffer_rsrc_t r, int off, float x) {
+  __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f2bf(x), r, off, 0, 0);
+}
+
+// c + a b with a = ah + al, b = bh + bl: three bf16 products.
+__device__ __forceinline__ f32x4 mma3(u32x4 ah, u32x4 al, u32x4 bh, u32x4 bl, f32x4 c) {
+  c = mma(as_bf16x8(ah), as_bf16x8(bh), c);
+  c = mma(as_bf16x8(ah), as_bf16x8(bl), c);
+  return mma(as_bf16x8(al), as_bf16x8(bh), c);
 }
 
 // ----------------------------------------------------------------------------
-// Prep: grid BH * nch, blockIdx.x = bh * nch + c.
-template <typename T, int D, int M>
-__global__ __launch_bounds__(NT) void dn_prep_kernel(const T* __restrict__ k, const T* __restrict__ v,
-                                                     const T* __restrict__ beta, int N, int nch,
-                                                     float* __restrict__ kh_ws, float* __restrict__ wc_ws,
-                                                     float* __restrict__ uc_ws, float* __restrict__ a_ws,
-                                                     float* __restrict__ b_ws) {
-  using GG = G<D, M>;
-  constexpr int W2 = D + M;       // columns of Y = [Kh | V] and of X = [Wc | Uc]
-  constexpr int XS = W2 + 16;     // X row stride: rows read by k-slot g step 16 banks
-  __shared__ __attribute__((aligned(16))) float Ks[C * GG::KS];  // Kh
-  __shared__ __attribute__((aligned(16))) float Gs[C * GG::GS];  // G = Kh Kh^T
-  __shared__ __attribute__((aligned(16))) float Xs[C * XS];      // Y, overwritten block by block by X
+// Per-chunk record in the workspace (16-byte units), for chunk (bh, c) at unit
+// (bh * nch + c) * Rec<D>::UNITS:
+//   [0, KI)         kh as the chain kernel's two bf16 LDS tiles (head, then
+//                   tail): row-major [t][d], 16-byte units swizzled (lds_tiles.hpp);
+//   [KI, KI + 768)  T in operand order: for block b = (w, sg) of the six
+//                   (token tile w, slab sg <= w / 2) pairs, lane l = 16 g + n
+//                   holds T[16 w + n][32 sg + 16 h + 4 g + r] (e = 4 h + r) as a
+//                   head unit then a tail unit at 128 b + 2 l.
+template <int D>
+struct Rec {
+  static constexpr int U8 = D / 8;          // 16-byte units per bf16 row
+  static constexpr int KI = 2 * C * U8;     // kh image units (head and tail)
+  static constexpr int UNITS = KI + 6 * 128;
+};
+__host__ __device__ constexpr int t_block(int w, int sg) { return w < 2 ? w : 2 * w - 2 + sg; }
+
+// ----------------------------------------------------------------------------
+// Grid BH * nch, blockIdx.x = bh * nch + c.
+// MFMA 16x16x4 f32 (lane l = 16 g + n): a = A[n][k], b = B[k][n] for the k-slot
+// g; the accumulator holds D[4 g + r][n] in element r.
+template <typename T, int D>
+__global__ __launch_bounds__(NT) void dn_prep_kernel(const T* __restrict__ k, const T* __restrict__ beta, int N,
+                                                     int nch, u32x4* __restrict__ ws) {
+  using RR = Rec<D>;
+  constexpr int KS = D + 4;  // kh row stride: 16 rows x 4 k-slots hit 64 distinct banks
+  constexpr int UPR = D / 4;
+  constexpr int U8 = RR::U8;
+  __shared__ __attribute__((aligned(16))) float Ks[C * KS];
+  __shared__ __attribute__((aligned(16))) float Gs[C * FS];
+  __shared__ __attribute__((aligned(16))) float Ts[C * FS];
   __shared__ float Bs[C];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
   const int bh = blockIdx.x / nch, c = blockIdx.x % nch;
   const int t0 = c * C, nt = min(C, N - t0);
-  load_rows<T, D, GG::KS, true>(Ks, k + ((size_t)bh * N + t0) * D, nt, tid);
-  load_rows<T, M, XS, false>(Xs + D, v + ((size_t)bh * N + t0) * M, nt, tid);
-  if (tid < C) Bs[tid] = tid < nt ? ld_scalar<T>(beta + (size_t)bh * N + t0 + tid) : 0.f;
+  u32x4* rec = ws + ((size_t)bh * nch + c) * RR::UNITS;
+
+  // kh = phi(k) / sum phi(k); rows at or past nt are zero (their beta is zero too).
+  {
+    float4 raw[C * UPR / NT];
+    const T* src = k + ((size_t)bh * N + t0) * D;
+#pragma unroll
+    for (int i = 0; i < C * UPR / NT; ++i) {
+      const int u = tid + NT * i, row = u / UPR;
+      raw[i] = load4<T>(src + (size_t)min(row, nt - 1) * D + (u % UPR) * 4);
+    }
+    const float bt = ld_scalar<T>(beta + (size_t)bh * N + t0 + min(tid & (C - 1), nt - 1));
+    if (tid < C) Bs[tid] = tid < nt ? bt : 0.f;
+#pragma unroll
+    for (int i = 0; i < C * UPR / NT; ++i) {
+      const int u = tid + NT * i, row = u / UPR, c4 = (u % UPR) * 4;
+      float4 x = float4{phi(raw[i].x), phi(raw[i].y), phi(raw[i].z), phi(raw[i].w)};
+      float s = (x.x + x.y) + (x.z + x.w);
+      s = UPR == 16 ? sum16(s) : sum8(s);
+      const float inv = row < nt ? __builtin_amdgcn_rcpf(s) : 0.f;  // 1 ulp
+      x = float4{x.x * inv, x.y * inv, x.z * inv, x.w * inv};
+      *reinterpret_cast<float4*>(&Ks[row * KS + c4]) = x;
+    }
+  }
   __syncthreads();
-  for (int u = tid; u < C * D / 4; u += NT) {  // Y's Kh columns
-    const int row = u / (D / 4), c4 = (u % (D / 4)) * 4;
-    *reinterpret_cast<float4*>(&Xs[row * XS + c4]) = *reinterpret_cast<const float4*>(&Ks[row * GG::KS + c4]);
+
+  // kh image for the chain kernel: head and tail tiles, swizzled.
+#pragma unroll
+  for (int i = 0; i < C * U8 / NT; ++i) {
+    const int u = tid + NT * i, row = u / U8, c8 = (u % U8) * 8;
+    const float4 a = *reinterpret_cast<const float4*>(&Ks[row * KS + c8]);
+    const float4 b = *reinterpret_cast<const float4*>(&Ks[row * KS + c8 + 4]);
+    const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    u32x4 h, l;
+    split8(x, h, l);
+    const int unit = swz<U8>(row, c8) >> 3;
+    rec[unit] = h;
+    rec[C * U8 + unit] = l;
   }
 
-  // G = Kh Kh^T: wave w computes the row tile w against every column tile.
+  // G blocks on and below the diagonal: tile p = i (i + 1) / 2 + j for block (i, j),
+  // j <= i; wave w takes p = w, w + 4, w + 8.
 #pragma unroll
-  for (int jt = 0; jt < C / 16; ++jt) {
+  for (int it = 0; it < 3; ++it) {
+    const int p = w + 4 * it;
+    const int i = p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3;
+    const int j = min(p, 9) - i * (i + 1) / 2;
     f32x4 acc{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < D / 4; ++kk)
-      acc = mma(Ks[(16 * w + n) * GG::KS + 4 * kk + g], Ks[(16 * jt + n) * GG::KS + 4 * kk + g], acc);
+      acc = mma(Ks[(16 * i + n) * KS + 4 * kk + g], Ks[(16 * j + n) * KS + 4 * kk + g], acc);
+    if (p < 10) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) Gs[(16 * w + 4 * g + r) * GG::GS + 16 * jt + n] = acc[r];
+      for (int r = 0; r < 4; ++r) Gs[(16 * i + 4 * g + r) * FS + 16 * j + n] = acc[r];
+    }
   }
   __syncthreads();
 
-  // [Wc | Uc] = T [Kh | V], x_t = beta_t (y_t - sum_{s<t} G[t][s] x_s), in four
-  // blocks of 16 tokens.  Block i first takes the earlier blocks at once on MFMA,
-  // z = y - G[block i][blocks < i] X[blocks < i], in place in Xs; then one thread
-  // per column solves the 16 rows of the block, right-looking (G is symmetric, so
-  // column t of G is its row t).
+  // Diagonal blocks T_ii = (I + B_i L_ii)^{-1} B_i: wave 0, lane (n, g) solves
+  // column n of block i = g, x_t = beta_t (e_n - sum_{s<t} G_ts x_s)_t, right-looking.
+  if (w == 0) {
+    const int base = 16 * g;
+    float z[16];
 #pragma unroll
-  for (int bi = 0; bi < C / 16; ++bi) {
-    if (bi > 0) {
-      for (int ct = w; ct < W2 / 16; ct += 4) {
-        f32x4 acc;
+    for (int t = 0; t < 16; ++t) z[t] = t == n ? 1.f : 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] = Xs[(16 * bi + 4 * g + r) * XS + 16 * ct + n];
-        for (int bj = 0; bj < bi; ++bj)
+    for (int t = 0; t < 16; ++t) {
+      const float x = Bs[base + t] * z[t];
+      z[t] = x;
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk)
-            acc = mma(-Gs[(16 * bi + n) * GG::GS + 16 * bj + 4 * kk + g],
-                      Xs[(16 * bj + 4 * kk + g) * XS + 16 * ct + n], acc);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Xs[(16 * bi + 4 * g + r) * XS + 16 * ct + n] = acc[r];
-      }
-      __syncthreads();
-    }
-    if (tid < W2) {
-      float z[16];
-#pragma unroll
-      for (int t = 0; t < 16; ++t) z[t] = Xs[(16 * bi + t) * XS + tid];
-#pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        z[t] *= Bs[16 * bi + t];
-#pragma unroll
-        for (int t2 = t + 1; t2 < 16; ++t2) z[t2] -= Gs[(16 * bi + t) * GG::GS + 16 * bi + t2] * z[t];
-      }
-#pragma unroll
-      for (int t = 0; t < 16; ++t) Xs[(16 * bi + t) * XS + tid] = z[t];
-    }
-    __syncthreads();
-  }
-
-  const size_t rec = (size_t)bh * nch + c;
-  // Wc, Uc and Kh for the output kernel.
-  for (int u = tid; u < C * W2 / 4; u += NT) {
-    const int row = u / (W2 / 4), c4 = (u % (W2 / 4)) * 4;
-    const float4 x = *reinterpret_cast<const float4*>(&Xs[row * XS + c4]);
-    if (c4 < D) *reinterpret_cast<float4*>(&wc_ws[rec * GG::WC + (size_t)row * D + c4]) = x;
-    else *reinterpret_cast<float4*>(&uc_ws[rec * GG::UC + (size_t)row * M + c4 - D]) = x;
-  }
-  float* khd = kh_ws + rec * GG::KH;
-  for (int u = tid; u < C * D / 4; u += NT) {
-    const int row = u / (D / 4), c4 = (u % (D / 4)) * 4;
-    *reinterpret_cast<float4*>(&khd[row * D + c4]) = *reinterpret_cast<const float4*>(&Ks[row * GG::KS + c4]);
-  }
-
-  // The chunk's affine map: A = I - Wc^T Kh (D x D), Bc = Uc^T Kh (M x D).  The
-  // TD * TD + TM * TD output tiles are dealt round robin to the waves; tile
-  // (i0, j0) = sum over tokens of X[t][i0 + i] Kh[t][j0 + j].
-  constexpr int NTA = GG::TD * GG::TD, NTB = GG::TM * GG::TD;
-  for (int tile = w; tile < NTA + NTB; tile += 4) {
-    const bool isa = tile < NTA;
-    const int tt = isa ? tile : tile - NTA;
-    const int it = tt / GG::TD, jt = tt % GG::TD;
-    const int xcol = (isa ? 0 : D) + 16 * it;
-    f32x4 acc{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < C / 4; ++kk)
-      acc = mma(Xs[(4 * kk + g) * XS + xcol + n], Ks[(4 * kk + g) * GG::KS + 16 * jt + n], acc);
-    float* dst = isa ? a_ws + rec * GG::AA : b_ws + rec * GG::BB;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 16 * it + 4 * g + r, j = 16 * jt + n;
-      dst[(size_t)i * D + j] = isa ? (i == j ? 1.f : 0.f) - acc[r] : acc[r];
-    }
-  }
-}
-
-// ----------------------------------------------------------------------------
-// Scan: one workgroup per head; wave w keeps the 16-row slice m0 = 16 w of the
-// memory, transposed, in registers: wt[dt][r] = W^T[16 dt + 4 g + r][m0 + n].
-// Per chunk: W <- W A + Bc, i.e. W^T tile dt <- Bc^T tile dt + sum over k of
-// A[k][16 dt + i] W^T[k][m], with k = 16 dt' + 4 g + r.  A (shared by the
-// waves) is staged in LDS; each wave reads its Bc tiles from global memory.
-// The workgroup covers the chunks [grp * G, min(nch, grp * G + G)) of head bh
-// (blockIdx.x = bh * ng + grp, ng = ceil(nch / G)), starting from its own memory
-// W0 + blockIdx.x * M * D; records are indexed bh * nch + c.  One workgroup per
-// head (G = nch) is the plain scan.
-template <int D, int M>
-__global__ __launch_bounds__(NT) void dn_scan_kernel(const float* __restrict__ a_ws, const float* __restrict__ b_ws,
-                                                     const float* __restrict__ W0, int nch, int G,
-                                                     float* __restrict__ ws_ws, float* __restrict__ W_out) {
-  using GG = dnc::G<D, M>;
-  constexpr int AS = D + 4;  // A row stride: (4g + r) * AS = 16 g mod 64 banks at D = 64 (4 g at D = 32)
-  __shared__ __attribute__((aligned(16))) float As[2][D * AS];
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
-  const int ng = (nch + G - 1) / G, bh = blockIdx.x / ng, grp = blockIdx.x % ng, m0 = 16 * w;
-  const int c0 = grp * G, c1 = min(nch, c0 + G);
-  const bool active = w < GG::TM;  // waves past M/16 only help staging
-
-  f32x4 wt[GG::TD];
-#pragma unroll
-  for (int dt = 0; dt < GG::TD; ++dt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      wt[dt][r] = (W0 && active) ? W0[((size_t)blockIdx.x * M + m0 + n) * D + 16 * dt + 4 * g + r] : 0.f;
-
-  // Register staging: A as float4 units of rows (all threads), this wave's Bc tiles.
-  constexpr int NA4 = D * D / 4 / NT > 0 ? D * D / 4 / NT : 1;
-  float4 ra[NA4];
-  f32x4 rb[GG::TD];
-  auto load_chunk = [&](int c) __attribute__((always_inline)) {
-    const size_t rec = (size_t)bh * nch + c;
-#pragma unroll
-    for (int i = 0; i < NA4; ++i) {
-      const int u = tid + NT * i;
-      ra[i] = u < D * D / 4 ? *reinterpret_cast<const float4*>(a_ws + rec * GG::AA + 4 * u) : float4{0.f, 0.f, 0.f, 0.f};
+      for (int t2 = t + 1; t2 < 16; ++t2) z[t2] -= Gs[(base + t2) * FS + base + t] * x;
     }
 #pragma unroll
-    for (int dt = 0; dt < GG::TD; ++dt)
-      rb[dt] = active ? *reinterpret_cast<const f32x4*>(b_ws + rec * GG::BB + (size_t)(m0 + n) * D + 16 * dt + 4 * g)
-                      : f32x4{0.f, 0.f, 0.f, 0.f};
-  };
-  load_chunk(c0);
-
-  for (int c = c0; c < c1; ++c) {
-    const size_t rec = (size_t)bh * nch + c;
-    float* Ab = As[(c - c0) & 1];
-#pragma unroll
-    for (int i = 0; i < NA4; ++i) {
-      const int u = tid + NT * i;
-      if (u < D * D / 4) *reinterpret_cast<float4*>(&Ab[(u / (D / 4)) * AS + (u % (D / 4)) * 4]) = ra[i];
-    }
-    // the memory at the chunk start, for the output kernel (W layout [m][d])
-    if (active) {
-#pragma unroll
-      for (int dt = 0; dt < GG::TD; ++dt)
-        *reinterpret_cast<f32x4*>(ws_ws + rec * GG::WS + (size_t)(m0 + n) * D + 16 * dt + 4 * g) = wt[dt];
-    }
-    f32x4 acc[GG::TD];
-#pragma unroll
-    for (int dt = 0; dt < GG::TD; ++dt) acc[dt] = rb[dt];
-    // One barrier per chunk: buffer c & 1 is rewritten two chunks later, after
-    // every wave has passed the next chunk's barrier.
-    __syncthreads();
-    if (c + 1 < c1) load_chunk(c + 1);
-#pragma unroll
-    for (int dk = 0; dk < GG::TD; ++dk)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int dt = 0; dt < GG::TD; ++dt)
-          acc[dt] = mma(Ab[(16 * dk + 4 * g + r) * AS + 16 * dt + n], wt[dk][r], acc[dt]);
-#pragma unroll
-    for (int dt = 0; dt < GG::TD; ++dt) wt[dt] = acc[dt];
+    for (int t = 0; t < 16; ++t) Ts[(base + t) * FS + base + n] = z[t];
   }
-  if (W_out && active) {
-#pragma unroll
-    for (int dt = 0; dt < GG::TD; ++dt)
-      *reinterpret_cast<f32x4*>(W_out + ((size_t)blockIdx.x * M + m0 + n) * D + 16 * dt + 4 * g) = wt[dt];
-  }
-}
+  __syncthreads();
 
-// ----------------------------------------------------------------------------
-// Composition of the chunk maps of one group: W -> W A_c + Bc_c for the chunks
-// [grp * G, min(nch, grp * G + G)) of head bh (blockIdx.x = bh * ng + grp) is
-// W -> W Ag + Bg with (Ag, Bg) <- (Ag A_c, Bg A_c + Bc_c) from the group's first
-// map.  Wave w holds rows 16 w.. of Ag (w < D / 16) and of Bg (w < M / 16) in the
-// scan's transposed layout, so every step is the scan's product.  Writes
-// ag [BH * ng][D][D] and bg [BH * ng][M][D].
-template <int D, int M>
-__global__ __launch_bounds__(NT) void dn_compose_kernel(const float* __restrict__ a_ws, const float* __restrict__ b_ws,
-                                                        int nch, int G, float* __restrict__ ag, float* __restrict__ bg) {
-  using GG = dnc::G<D, M>;
-  constexpr int AS = D + 4;
-  __shared__ __attribute__((aligned(16))) float As[2][D * AS];
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
-  const int ng = (nch + G - 1) / G, bh = blockIdx.x / ng, grp = blockIdx.x % ng, r0 = 16 * w;
-  const int c0 = grp * G, c1 = min(nch, c0 + G);
-  const bool act_a = w < GG::TD, act_b = w < GG::TM;
-  f32x4 xa[GG::TD], xb[GG::TD];
+  // Below the diagonal, for a lower-triangular [[T_bb, 0], [X, T_aa]] block pair:
+  // X = -T_aa G_ab T_bb.  First the 16-row pairs (1, 0) and (3, 2) (waves 0, 1;
+  // waves 2, 3 repeat them and discard the result).  The product T_aa Y takes Y
+  // from the accumulator with the k-permutation k = 4 g + r.
   {
-    const size_t rec = (size_t)bh * nch + c0;
+    const int a = 2 * (w & 1) + 1, b = a - 1;
+    f32x4 y{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int dt = 0; dt < GG::TD; ++dt) {
-      xa[dt] = act_a ? *reinterpret_cast<const f32x4*>(a_ws + rec * GG::AA + (size_t)(r0 + n) * D + 16 * dt + 4 * g)
-                     : f32x4{0.f, 0.f, 0.f, 0.f};
-      xb[dt] = act_b ? *reinterpret_cast<const f32x4*>(b_ws + rec * GG::BB + (size_t)(r0 + n) * D + 16 * dt + 4 * g)
-                     : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kk = 0; kk < 4; ++kk)
+      y = mma(Gs[(16 * a + n) * FS + 16 * b + 4 * kk + g], Ts[(16 * b + 4 * kk + g) * FS + 16 * b + n], y);
+    f32x4 x{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x = mma(Ts[(16 * a + n) * FS + 16 * a + 4 * g + r], y[r], x);
+    if (w < 2) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Ts[(16 * a + 4 * g + r) * FS + 16 * b + n] = -x[r];
     }
   }
-  for (int c = c0 + 1; c < c1; ++c) {
-    const size_t rec = (size_t)bh * nch + c;
-    float* Ab = As[(c - c0) & 1];
-    for (int u = tid; u < D * D / 4; u += NT)
-      *reinterpret_cast<float4*>(&Ab[(u / (D / 4)) * AS + (u % (D / 4)) * 4]) =
-          *reinterpret_cast<const float4*>(a_ws + rec * GG::AA + 4 * u);
-    f32x4 acc_a[GG::TD], acc_b[GG::TD];
+  __syncthreads();
+  // Then the 32-row halves: with T_A = T[0:32][0:32], T_B = T[32:64][32:64],
+  // T[32:64][0:32] = -T_B (G[32:64][0:32] T_A).  Wave w forms block (2 + a2, c2),
+  // a2 = w / 2, c2 = w % 2: -sum_{b2 <= a2} T[2 + a2][2 + b2] Y[b2],
+  // Y[b2] = sum_{e >= c2} G[2 + b2][e] T[e][c2] (terms outside the triangles are
+  // masked to zero, so every wave runs the same products).
+  {
+    const int a2 = w >> 1, c2 = w & 1;
+    f32x4 x{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int dt = 0; dt < GG::TD; ++dt) {
-      acc_a[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      acc_b[dt] = act_b ? *reinterpret_cast<const f32x4*>(b_ws + rec * GG::BB + (size_t)(r0 + n) * D + 16 * dt + 4 * g)
-                        : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    // One barrier per chunk: buffer (c - c0) & 1 is rewritten two chunks later.
-    __syncthreads();
+    for (int b2 = 0; b2 < 2; ++b2) {
+      f32x4 y{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int dk = 0; dk < GG::TD; ++dk)
+      for (int e = 0; e < 2; ++e)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int dt = 0; dt < GG::TD; ++dt) {
-          const float a = Ab[(16 * dk + 4 * g + r) * AS + 16 * dt + n];
-          acc_a[dt] = mma(a, xa[dk][r], acc_a[dt]);
-          acc_b[dt] = mma(a, xb[dk][r], acc_b[dt]);
+        for (int kk = 0; kk < 4; ++kk) {
+          // both operands masked: the block T[0][1] was never written
+          const bool on = e >= c2;
+          const float ga = on ? Gs[(16 * (2 + b2) + n) * FS + 16 * e + 4 * kk + g] : 0.f;
+          const float tb = on ? Ts[(16 * e + 4 * kk + g) * FS + 16 * c2 + n] : 0.f;
+          y = mma(ga, tb, y);
         }
 #pragma unroll
-    for (int dt = 0; dt < GG::TD; ++dt) {
-      xa[dt] = acc_a[dt];
-      xb[dt] = acc_b[dt];
+      for (int r = 0; r < 4; ++r) {
+        const float ta = b2 <= a2 ? Ts[(16 * (2 + a2) + n) * FS + 16 * (2 + b2) + 4 * g + r] : 0.f;
+        x = mma(ta, y[r], x);
+      }
     }
-  }
+    // The blocks written here (rows 32.., columns ..31) are read by no wave above.
 #pragma unroll
-  for (int dt = 0; dt < GG::TD; ++dt) {
-    if (act_a)
-      *reinterpret_cast<f32x4*>(ag + ((size_t)blockIdx.x * D + r0 + n) * D + 16 * dt + 4 * g) = xa[dt];
-    if (act_b)
-      *reinterpret_cast<f32x4*>(bg + ((size_t)blockIdx.x * M + r0 + n) * D + 16 * dt + 4 * g) = xb[dt];
+    for (int r = 0; r < 4; ++r) Ts[(16 * (2 + a2) + 4 * g + r) * FS + 16 * c2 + n] = -x[r];
+  }
+  __syncthreads();
+
+  // T in operand order (tiles above the diagonal blocks as zeros).
+  for (int i = tid; i < 6 * 64; i += NT) {
+    const int b = i >> 6, l = i & 63, ln = l & 15, lg = l >> 4;
+    const int bw = b < 2 ? b : 2 + ((b - 2) >> 1), sg = b < 2 ? 0 : (b - 2) & 1;
+    float x[8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const bool ok = 2 * sg + h <= bw;
+      const float4 t4 = *reinterpret_cast<const float4*>(&Ts[(16 * bw + ln) * FS + 32 * sg + 16 * h + 4 * lg]);
+      x[4 * h + 0] = ok ? t4.x : 0.f;
+      x[4 * h + 1] = ok ? t4.y : 0.f;
+      x[4 * h + 2] = ok ? t4.z : 0.f;
+      x[4 * h + 3] = ok ? t4.w : 0.f;
+    }
+    u32x4 h, lo;
+    split8(x, h, lo);
+    rec[RR::KI + 128 * b + 2 * l] = h;
+    rec[RR::KI + 128 * b + 2 * l + 1] = lo;
   }
 }
 
 // ----------------------------------------------------------------------------
-// Outputs: grid BH * nch, blockIdx.x = bh * nch + c.  Wave w owns tokens
-// 16w .. 16w + 15 of the chunk.
-//  1. U rows of the wave: U = Uc - Wc W0^T (in place over Uc in LDS).
-//  2. Score tiles transposed, S^T[s][t] = kh_s . qh_t for the wave's tokens t,
-//     zero where s > t.  Lane (n, g) of tile st holds s = 16 st + 4 g + r and
-//     t = 16 w + n, which with k = (st, r) is exactly the A operand of step 3.
-//  3. o = Qh W0^T + S U.
+// The chain.  One workgroup per (head, 16-row slice of W); the NS = M / 16
+// slices of a head get workgroup indices equal mod 8, so they share an XCD (and
+// its L2) for the q and record reads they have in common.  Grid 8 ceil(BH / 8) NS.
+//
+// MFMA 16x16x32 bf16 layouts (lane l = 16 g + n; lds_tiles.hpp): a d-contraction
+// operand holds d = 32 s + 8 g + e of slab s; a token contraction holds tokens
+// 32 s + 16 h + 4 g + r (e = 4 h + r), the rows an accumulator tile keeps in the
+// lane, so accumulators feed it directly.
+//
+// Eight waves, two per SIMD.  Waves 0-3 run the sequential path only: wave w owns
+// token tile w (rows 16 w ..) for X, R and U, and the 16-wide d tile w of the
+// memory slice (W^T rows 16 w .., fp32 in its accumulator).  Waves 4-7 do the
+// work that does not depend on the memory's next value, alongside: the loads,
+// staging of the next chunk, the score tiles, P and o for token tile w - 4.
+// Per chunk (three barriers):
+//   path:   X = Kh W^T (W^T from the slice tile in LDS), R = V - X -> LDS
+//   others: loads for later chunks, the last chunk's o stored; P = Qh W^T;
+//           score tiles S^T = Kh Qh^T of token tiles 0, 1 (masked to s <= t)
+//   | path:   U = T R (token contraction over R of all token tiles) -> LDS
+//     others: score tiles 2, 3; kh copied and half of qh staged for the next chunk
+//   | path:   W^T += Kh^T U (Kh^T by transposed LDS reads) -> slice tile in LDS
+//     others: o = P + S U; the other half of qh staged
+//   |
+// The products on the sequential path keep their three partial products in
+// separate accumulators, so that they do not wait on each other.
+__device__ __forceinline__ void mma3s(u32x4 ah, u32x4 al, u32x4 bh, u32x4 bl, f32x4 (&c)[3]) {
+  c[0] = mma(as_bf16x8(ah), as_bf16x8(bh), c[0]);
+  c[1] = mma(as_bf16x8(ah), as_bf16x8(bl), c[1]);
+  c[2] = mma(as_bf16x8(al), as_bf16x8(bh), c[2]);
+}
+__device__ __forceinline__ f32x4 sum3(const f32x4 (&c)[3]) {
+  f32x4 x;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) x[r] = c[0][r] + (c[1][r] + c[2][r]);
+  return x;
+}
+
+constexpr int NTC = 2 * NT;  // threads of the chain kernel
+
 template <typename T, int D, int M>
-__global__ __launch_bounds__(NT) void dn_out_kernel(const T* __restrict__ q, const float* __restrict__ kh_ws,
-                                                    const float* __restrict__ wc_ws, const float* __restrict__ uc_ws,
-                                                    const float* __restrict__ ws_ws, int N, int nch,
-                                                    T* __restrict__ o) {
-  using GG = G<D, M>;
-  constexpr int US = M + 4;  // U row stride: (4g + r) rows apart = 16 g mod 64 banks at M = 64
-  __shared__ __attribute__((aligned(16))) float Xs[C * GG::KS];   // Wc rows, then qh rows
-  __shared__ __attribute__((aligned(16))) float Ks[C * GG::KS];   // kh [t][d]
-  __shared__ __attribute__((aligned(16))) float Wss[M * GG::KS];  // W0 [m][d]
-  __shared__ __attribute__((aligned(16))) float Us[C * US];       // Uc, then U [t][m]
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
-  const int bh = blockIdx.x / nch, c = blockIdx.x % nch;
-  const int t0 = c * C, nt = min(C, N - t0);
-  const size_t rec = (size_t)bh * nch + c;
-  load_rows<float, D, GG::KS, false>(Xs, wc_ws + rec * GG::WC, C, tid);
-  load_rows<float, D, GG::KS, false>(Ks, kh_ws + rec * GG::KH, C, tid);
-  load_rows<float, M, US, false>(Us, uc_ws + rec * GG::UC, C, tid);
-  load_rows<float, D, GG::KS, false, M>(Wss, ws_ws + rec * GG::WS, M, tid);
-  __syncthreads();
+__global__ __launch_bounds__(NTC) void dn_chain_kernel(const T* __restrict__ q, const T* __restrict__ v,
+                                                       const u32x4* __restrict__ ws, int BH, int N, int nch,
+                                                       const float* __restrict__ W0, float* __restrict__ W_out,
+                                                       T* __restrict__ o) {
+  using RR = Rec<D>;
+  constexpr int U8 = RR::U8;  // 16-byte units per bf16 row of D (swizzle width)
+  constexpr int TD = D / 16;  // d tiles of the slice
+  constexpr int SL = D / 32;  // slabs of a d-contraction
+  constexpr int NS = M / 16;  // slices per head
+  constexpr int UPR = D / 4;  // 4-element units per row of q
+  constexpr int NU = C * UPR / NT;  // q units per helper thread
+  constexpr int KU = RR::KI / NT;   // kh image units per helper thread
+  __shared__ __attribute__((aligned(16))) bf16_t Kt[2][2][C * D];  // [buffer][head, tail] kh [t][d], swizzled
+  __shared__ __attribute__((aligned(16))) bf16_t Qt[2][2][C * D];  // qh
+  __shared__ __attribute__((aligned(16))) bf16_t Wt[2][16 * D];    // slice [m][d], head and tail
+  __shared__ u32x4 Rx[4][64];                                      // R tiles, per token tile and lane
+  __shared__ u32x4 Ux[4][64];                                      // U tiles
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
+  const bool path = wv < 4;  // wave-uniform role
+  const int w = wv & 3, ht = tid & (NT - 1);
+  const int xcd = blockIdx.x & 7, jx = blockIdx.x >> 3;
+  const int bh = (jx / NS) * 8 + xcd, m0 = 16 * (jx % NS);
+  if (bh >= BH) return;
+  const int dt = w % TD;  // d tile of a path wave (waves past TD repeat and discard)
 
-  // 1. U = Uc - Wc W0^T for tokens 16w .. 16w + 15
+  const T* qb = q + (size_t)bh * N * D;
+  const T* vb = v + (size_t)bh * N * M + m0 + n;
+  const u32x4* recb = ws + (size_t)bh * nch * RR::UNITS;
+
+  // Raw q of a chunk (rows clamped into the chunk; masked when staged) and its
+  // kh image (helper waves).
+  auto load_qk = [&](int c, float4 (&rq)[NU], u32x4 (&rk)[KU]) __attribute__((always_inline)) {
+    const int t0 = c * C, last = min(C, N - t0) - 1;
+    const T* qc = qb + (size_t)t0 * D;
 #pragma unroll
-  for (int mt = 0; mt < GG::TM; ++mt) {
-    f32x4 acc{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < D / 4; ++kk)
-      acc = mma(Xs[(16 * w + n) * GG::KS + 4 * kk + g], Wss[(16 * mt + n) * GG::KS + 4 * kk + g], acc);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float& u = Us[(16 * w + 4 * g + r) * US + 16 * mt + n];
-      u = u - acc[r];
+    for (int i = 0; i < NU; ++i) {
+      const int u = ht + NT * i;
+      rq[i] = load4<T>(qc + min(u / UPR, last) * D + (u % UPR) * 4);
     }
-  }
-  __syncthreads();  // U complete; Wc no longer read
-  load_rows<T, D, GG::KS, true>(Xs, q + ((size_t)bh * N + t0) * D, nt, tid);
-  __syncthreads();
-
-  // 2. transposed, masked score tiles
-  f32x4 st4[C / 16];
+    const u32x4* rc = recb + (size_t)c * RR::UNITS;
 #pragma unroll
-  for (int st = 0; st < C / 16; ++st) {
-    f32x4 acc{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < KU; ++i) rk[i] = rc[ht + NT * i];
+  };
+  auto copy_k = [&](int buf, const u32x4 (&rk)[KU]) __attribute__((always_inline)) {
+    u32x4* kd = reinterpret_cast<u32x4*>(Kt[buf][0]);
 #pragma unroll
-    for (int kk = 0; kk < D / 4; ++kk)
-      acc = mma(Ks[(16 * st + n) * GG::KS + 4 * kk + g], Xs[(16 * w + n) * GG::KS + 4 * kk + g], acc);
+    for (int i = 0; i < KU; ++i) kd[ht + NT * i] = rk[i];
+  };
+  // phi(q) / sum phi(q) per row, split into head and tail tiles: units [i0, i1).
+  auto stage_q = [&](int buf, int c, const float4 (&rq)[NU], int i0, int i1) __attribute__((always_inline)) {
+    const int nt = min(C, N - c * C);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r] = (16 * st + 4 * g + r <= 16 * w + n) ? acc[r] : 0.f;
-    st4[st] = acc;
-  }
-
-  // 3. o = Qh W0^T + S U
-  T* oh = o + ((size_t)bh * N + t0) * M;
+    for (int i = 0; i < NU; ++i) {
+      if (i < i0 || i >= i1) continue;
+      const int u = ht + NT * i, row = u / UPR, c4 = (u % UPR) * 4;
+      const float4 r = rq[i];
+      f32x4 x{phi(r.x), phi(r.y), phi(r.z), phi(r.w)};
+      float s = (x[0] + x[1]) + (x[2] + x[3]);
+      s = UPR == 16 ? sum16(s) : sum8(s);
+      const float inv = row < nt ? __builtin_amdgcn_rcpf(s) : 0.f;  // 1 ulp, as for kh
 #pragma unroll
-  for (int mt = 0; mt < GG::TM; ++mt) {
-    f32x4 acc{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < D / 4; ++kk)
-      acc = mma(Xs[(16 * w + n) * GG::KS + 4 * kk + g], Wss[(16 * mt + n) * GG::KS + 4 * kk + g], acc);
-#pragma unroll
-    for (int st = 0; st < C / 16; ++st)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc = mma(st4[st][r], Us[(16 * st + 4 * g + r) * US + 16 * mt + n], acc);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 16 * w + 4 * g + r;
-      if (t < nt) oh[(size_t)t * M + 16 * mt + n] = to_elem<T>(acc[r]);
+      for (int e = 0; e < 4; ++e) x[e] *= inv;
+      const u32x4 hl = split4(x);
+      unit8<U8>(Qt[buf][0], row, c4) = u32x2{hl[0], hl[1]};
+      unit8<U8>(Qt[buf][1], row, c4) = u32x2{hl[2], hl[3]};
     }
+  };
+  // T of token tile w in operand order (slab 1 of tiles 0 and 1 is zero) and V
+  // in the accumulator layout, rows 16 w + 4 g + r, column m0 + n (path waves).
+  auto load_tv = [&](int c, u32x4 (&tt)[4], float (&rv)[4]) __attribute__((always_inline)) {
+    const u32x4* rc = recb + (size_t)c * RR::UNITS + RR::KI + 2 * lane;
+#pragma unroll
+    for (int sg = 0; sg < 2; ++sg) {
+      const u32x4* p = rc + 128 * t_block(w, w < 2 ? 0 : sg);
+      tt[2 * sg] = p[0];
+      tt[2 * sg + 1] = p[1];
+    }
+    const int t0 = c * C, last = min(C, N - t0) - 1;
+    const T* vc = vb + (size_t)t0 * M;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) rv[r] = ld_scalar<T>(vc + min(16 * w + 4 * g + r, last) * M);
+  };
+
+  // Path wave: the slice's d tile dt, transposed: wm[r] = W[m0 + n][16 dt + 4 g + r].
+  f32x4 wm{0.f, 0.f, 0.f, 0.f};
+  if (W0 && path) {
+    const float4 x = *reinterpret_cast<const float4*>(W0 + ((size_t)bh * M + m0 + n) * D + 16 * dt + 4 * g);
+    wm = f32x4{x.x, x.y, x.z, x.w};
   }
+  auto put_w = [&]() __attribute__((always_inline)) {
+    if (w < TD) {
+      const u32x4 hl = split4(wm);
+      unit8<U8>(Wt[0], n, 16 * dt + 4 * g) = u32x2{hl[0], hl[1]};
+      unit8<U8>(Wt[1], n, 16 * dt + 4 * g) = u32x2{hl[2], hl[3]};
+    }
+  };
+
+  // Helper wave: outputs of a chunk are stored during the next one, after that
+  // chunk's loads are issued (loads and stores share one counter, and a store
+  // issued before a load makes every later wait for the load wait for it too).
+  // Rows past the chunk fall outside the buffer resource and are dropped, with
+  // no branch that would cost the compiler its count of the loads in flight.
+  f32x4 opend{0.f, 0.f, 0.f, 0.f};
+  auto store_o = [&](int c) __attribute__((always_inline)) {  // chunk c < 0: nothing (empty resource)
+    const int cc = max(c, 0), t0 = cc * C;
+    const int bytes = c < 0 ? 0 : min(C, N - t0) * M * (int)sizeof(T);
+    const __amdgpu_buffer_rsrc_t ob = out_rsrc(o + ((size_t)bh * N + t0) * M, bytes);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) store_elem<T>(ob, ((16 * w + 4 * g + r) * M + m0 + n) * (int)sizeof(T), opend[r]);
+  };
+
+  // One chunk.  On entry kh, qh of chunk c are staged in buffer c & 1; helper
+  // (rq, rk) hold chunk c + 1's raw q and kh image, and path (tt, rv) chunk c's T
+  // and V.  Helpers load chunk c + 2's q and kh into (rq2, rk2) and stage chunk
+  // c + 1 into the other buffer; path waves load chunk c + 1's T and V.
+  auto chunk = [&](int c, float4 (&rq)[NU], u32x4 (&rk)[KU], float4 (&rq2)[NU], u32x4 (&rk2)[KU],
+                   const u32x4 (&tt)[4], const float (&rv)[4], u32x4 (&tt2)[4], float (&rv2)[4])
+                   __attribute__((always_inline)) {
+    const int buf = c & 1, nt = min(C, N - c * C);
+    const bool more = c + 1 < nch;
+    const bf16_t *Kh = Kt[buf][0], *Kl = Kt[buf][1], *Qh = Qt[buf][0], *Ql = Qt[buf][1];
+    const f32x4 z4{0.f, 0.f, 0.f, 0.f};
+    f32x4 O3[3] = {z4, z4, z4};
+    u32x4 qh[SL], ql[SL], sh[2], sl[2];
+    // score tiles 2 sg, 2 sg + 1 against the helper's token tile w, as operands
+    auto scores = [&](int sg) __attribute__((always_inline)) {
+      float sv[8];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int jt = 2 * sg + h;
+        f32x4 acc = z4;
+#pragma unroll
+        for (int s = 0; s < SL; ++s)
+          acc = mma3(unit16<U8>(Kh, 16 * jt + n, 32 * s + 8 * g), unit16<U8>(Kl, 16 * jt + n, 32 * s + 8 * g), qh[s],
+                     ql[s], acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sv[4 * h + r] = 16 * jt + 4 * g + r <= 16 * w + n ? acc[r] : 0.f;
+      }
+      split8(sv, sh[sg], sl[sg]);
+    };
+
+    if (path) {
+      load_tv(min(c + 1, nch - 1), tt2, rv2);  // past the end: reloads the last chunk (unused)
+      // X = Kh W^T for token tile w; R = V - X (rows past the chunk are zero).
+      f32x4 X3[3] = {z4, z4, z4};
+#pragma unroll
+      for (int s = 0; s < SL; ++s)
+        mma3s(unit16<U8>(Kh, 16 * w + n, 32 * s + 8 * g), unit16<U8>(Kl, 16 * w + n, 32 * s + 8 * g),
+              unit16<U8>(Wt[0], n, 32 * s + 8 * g), unit16<U8>(Wt[1], n, 32 * s + 8 * g), X3);
+      const f32x4 X = sum3(X3);
+      f32x4 R;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) R[r] = (16 * w + 4 * g + r < nt ? rv[r] : 0.f) - X[r];
+      Rx[w][lane] = split4(R);
+    } else {
+      load_qk(min(c + 2, nch - 1), rq2, rk2);
+      store_o(c - 1);
+      // P = Qh W^T (the slice tile is rewritten only after the second barrier).
+#pragma unroll
+      for (int s = 0; s < SL; ++s) {
+        qh[s] = unit16<U8>(Qh, 16 * w + n, 32 * s + 8 * g);
+        ql[s] = unit16<U8>(Ql, 16 * w + n, 32 * s + 8 * g);
+        mma3s(qh[s], ql[s], unit16<U8>(Wt[0], n, 32 * s + 8 * g), unit16<U8>(Wt[1], n, 32 * s + 8 * g), O3);
+      }
+      scores(0);
+    }
+    __syncthreads();
+
+    if (path) {
+      // U = T R for token tile w.
+      f32x4 U3[3] = {z4, z4, z4};
+#pragma unroll
+      for (int sg = 0; sg < 2; ++sg) {
+        const bool on = sg == 0 || w >= 2;
+        const u32x4 z{0u, 0u, 0u, 0u};
+        const u32x4 a = Rx[2 * sg][lane], b = Rx[2 * sg + 1][lane];
+        mma3s(on ? tt[2 * sg] : z, on ? tt[2 * sg + 1] : z, u32x4{a[0], a[1], b[0], b[1]},
+              u32x4{a[2], a[3], b[2], b[3]}, U3);
+      }
+      Ux[w][lane] = split4(sum3(U3));
+    } else {
+      scores(1);
+      if (more) {
+        copy_k(buf ^ 1, rk);
+        stage_q(buf ^ 1, c + 1, rq, 0, NU / 2);
+      }
+    }
+    __syncthreads();
+
+    u32x4 uh[2], ul[2];
+#pragma unroll
+    for (int sg = 0; sg < 2; ++sg) {
+      const u32x4 a = Ux[2 * sg][lane], b = Ux[2 * sg + 1][lane];
+      uh[sg] = u32x4{a[0], a[1], b[0], b[1]};
+      ul[sg] = u32x4{a[2], a[3], b[2], b[3]};
+    }
+    if (path) {
+      // W^T tile dt += Kh^T U.
+      f32x4 W3[3] = {wm, z4, z4};
+#pragma unroll
+      for (int sg = 0; sg < 2; ++sg) {
+        const bf16x8 ah = jfrag<U8>(Kh, 32 * sg, 16 * dt, g, n), al = jfrag<U8>(Kl, 32 * sg, 16 * dt, g, n);
+        mma3s(__builtin_bit_cast(u32x4, ah), __builtin_bit_cast(u32x4, al), uh[sg], ul[sg], W3);
+      }
+      wm = sum3(W3);
+      put_w();
+    } else {
+      // o = P + S U (stored during the next chunk).
+#pragma unroll
+      for (int sg = 0; sg < 2; ++sg) mma3s(sh[sg], sl[sg], uh[sg], ul[sg], O3);
+      opend = sum3(O3);
+      if (more) stage_q(buf ^ 1, c + 1, rq, NU / 2, NU);
+    }
+    __syncthreads();
+  };
+
+  float4 rqa[NU], rqb[NU];
+  u32x4 rka[KU], rkb[KU];
+  u32x4 tta[4], ttb[4];
+  float rva[4], rvb[4];
+  // Prologue in the loop's own order, so that the count of loads in flight at
+  // the loop head is the same on entry as on the back edge.
+  if (path) {
+    load_tv(0, tta, rva);
+    put_w();
+  } else {
+    load_qk(0, rqb, rkb);
+    load_qk(min(1, nch - 1), rqa, rka);
+    copy_k(0, rkb);
+    stage_q(0, 0, rqb, 0, NU);
+  }
+  __syncthreads();
+  for (int c = 0; c < nch; c += 2) {
+    chunk(c, rqa, rka, rqb, rkb, tta, rva, ttb, rvb);
+    if (c + 1 < nch) chunk(c + 1, rqb, rkb, rqa, rka, ttb, rvb, tta, rva);
+  }
+  if (!path) store_o(nch - 1);
+  if (W_out && path && w < TD)
+    *reinterpret_cast<float4*>(W_out + ((size_t)bh * M + m0 + n) * D + 16 * dt + 4 * g) =
+        float4{wm[0], wm[1], wm[2], wm[3]};
 }
 
 // ----------------------------------------------------------------------------
 // Host side.
-// Chunks per group of the two-level scan (0: one serial scan per head).
-static int scan_group(int nch) { return nch > 16 ? 8 : 0; }
-
-template <int D, int M>
-static size_t ws_floats(int BH, int N) {
-  using GG = G<D, M>;
-  const size_t nch = (size_t)((N + C - 1) / C);
-  const int sg = scan_group((int)nch);
-  const size_t ng = sg ? (nch + sg - 1) / sg : 0;
-  // per chunk records, then per group: composed maps and the memory at the group start
-  return (size_t)BH * nch * (GG::KH + GG::WC + GG::UC + GG::AA + GG::BB + GG::WS) +
-         (size_t)BH * ng * (GG::AA + GG::BB + GG::WS);
-}
-
 template <typename T, int D, int M>
 static hipError_t impl(const void* q, const void* k, const void* v, const void* beta, void* o, int BH, int N,
                        const float* W0, float* W_out, void* ws, hipStream_t stream) {
-  using GG = G<D, M>;
   const int nch = (N + C - 1) / C;
-  const size_t rec = (size_t)BH * nch;
-  float* kh = (float*)ws;
-  float* wc = kh + rec * GG::KH;
-  float* uc = wc + rec * GG::WC;
-  float* aa = uc + rec * GG::UC;
-  float* bb = aa + rec * GG::AA;
-  float* wsb = bb + rec * GG::BB;
-  const dim3 block(NT), grid((unsigned)rec);
-  hipLaunchKernelGGL((dn_prep_kernel<T, D, M>), grid, block, 0, stream, (const T*)k, (const T*)v, (const T*)beta, N,
-                     nch, kh, wc, uc, aa, bb);
-  const int sg = scan_group(nch);
-  if (!sg) {
-    hipLaunchKernelGGL((dn_scan_kernel<D, M>), dim3((unsigned)BH), block, 0, stream, aa, bb, W0, nch, nch, wsb, W_out);
-  } else {
-    // Two-level scan: the maps of each group of sg chunks are composed in
-    // parallel, a short serial scan over the composed maps gives the memory at
-    // every group start (and the final memory), and each group then replays its
-    // own chunks from there in parallel, writing the memory at every chunk start.
-    const int ng = (nch + sg - 1) / sg;
-    float* ag = wsb + rec * GG::WS;
-    float* bg = ag + (size_t)BH * ng * GG::AA;
-    float* wg = bg + (size_t)BH * ng * GG::BB;
-    hipLaunchKernelGGL((dn_compose_kernel<D, M>), dim3((unsigned)(BH * ng)), block, 0, stream, aa, bb, nch, sg, ag, bg);
-    hipLaunchKernelGGL((dn_scan_kernel<D, M>), dim3((unsigned)BH), block, 0, stream, ag, bg, W0, ng, ng, wg, W_out);
-    hipLaunchKernelGGL((dn_scan_kernel<D, M>), dim3((unsigned)(BH * ng)), block, 0, stream, aa, bb, wg, nch, sg, wsb,
-                       nullptr);
-  }
-  hipLaunchKernelGGL((dn_out_kernel<T, D, M>), grid, block, 0, stream, (const T*)q, kh, wc, uc, wsb, N, nch, (T*)o);
+  u32x4* rec = (u32x4*)ws;
+  hipLaunchKernelGGL((dn_prep_kernel<T, D>), dim3((unsigned)((size_t)BH * nch)), dim3(NT), 0, stream, (const T*)k,
+                     (const T*)beta, N, nch, rec);
+  const unsigned grid = (unsigned)(8 * ((BH + 7) / 8) * (M / 16));
+  hipLaunchKernelGGL((dn_chain_kernel<T, D, M>), dim3(grid), dim3(NTC), 0, stream, (const T*)q, (const T*)v,
+                     (const u32x4*)rec, BH, N, nch, W0, W_out, (T*)o);
   return hipGetLastError();
 }
 
@@ -485,13 +566,10 @@ static hipError_t impl(const void* q, const void* k, const void* v, const void* 
 
 size_t deltanet_chunk_ws_bytes(int BH, int N, int D, int M) {
   if (BH <= 0 || N <= 0) return 0;
-  switch (D * 100 + M) {
-    case 3232: return dnc::ws_floats<32, 32>(BH, N) * sizeof(float);
-    case 3264: return dnc::ws_floats<32, 64>(BH, N) * sizeof(float);
-    case 6432: return dnc::ws_floats<64, 32>(BH, N) * sizeof(float);
-    case 6464: return dnc::ws_floats<64, 64>(BH, N) * sizeof(float);
-    default: return 0;
-  }
+  if (!((D == 32 || D == 64) && (M == 32 || M == 64))) return 0;
+  const size_t nch = (size_t)((N + dnc::C - 1) / dnc::C);
+  const size_t units = D == 64 ? dnc::Rec<64>::UNITS : dnc::Rec<32>::UNITS;
+  return (size_t)BH * nch * units * 16;
 }
 
 hipError_t launch_deltanet_chunked(const void* q, const void* k, const void* v, const void* beta, void* o, int BH,
