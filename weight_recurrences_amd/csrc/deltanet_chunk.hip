@@ -18,8 +18,8 @@
 // head's memory splits into slices of 16 rows that evolve independently.
 //
 // Two kernels:
-//   dn_prep_kernel   per (head, chunk), all in parallel: kh, G and T in fp32
-//                    (16x16x4 MFMA): the four diagonal 16x16 blocks of T by
+//   dn_prep_kernel   per (head, chunk), all in parallel: kh, G (split-bf16 MFMA)
+//                    and T in fp32 (16x16x4 MFMA): the four diagonal 16x16 blocks of T by
 //                    substitution, the blocks below them by doubling,
 //                    T_ab = -T_aa G_ab T_bb for 16-row blocks, then the same for
 //                    the 32-row halves.  Writes kh and T as bf16 head and tail
@@ -100,23 +100,31 @@ __host__ __device__ constexpr int t_block(int w, int sg) { return w < 2 ? w : 2 
 // Grid BH * nch, blockIdx.x = bh * nch + c.
 // MFMA 16x16x4 f32 (lane l = 16 g + n): a = A[n][k], b = B[k][n] for the k-slot
 // g; the accumulator holds D[4 g + r][n] in element r.
+// G and T live in LDS as their ten 16x16 blocks on and below the diagonal only,
+// row stride 17 inside a block (lb below).
+__device__ __forceinline__ int lb(int r, int c) {  // (r, c) with c / 16 <= r / 16
+  const int i = r >> 4, j = c >> 4;
+  return (i * (i + 1) / 2 + j) * 272 + (r & 15) * 17 + (c & 15);
+}
+
 template <typename T, int D>
-__global__ __launch_bounds__(NT) void dn_prep_kernel(const T* __restrict__ k, const T* __restrict__ beta, int N,
-                                                     int nch, u32x4* __restrict__ ws) {
+__global__ __launch_bounds__(NT, 4) void dn_prep_kernel(const T* __restrict__ k, const T* __restrict__ beta, int N,
+                                                        int nch, u32x4* __restrict__ ws) {
   using RR = Rec<D>;
-  constexpr int KS = D + 4;  // kh row stride: 16 rows x 4 k-slots hit 64 distinct banks
   constexpr int UPR = D / 4;
   constexpr int U8 = RR::U8;
-  __shared__ __attribute__((aligned(16))) float Ks[C * KS];
-  __shared__ __attribute__((aligned(16))) float Gs[C * FS];
-  __shared__ __attribute__((aligned(16))) float Ts[C * FS];
+  constexpr int SL = D / 32;
+  __shared__ __attribute__((aligned(16))) bf16_t Ki[2][C * D];  // kh head and tail, swizzled (the chain's layout)
+  __shared__ float Gs[10 * 272];
+  __shared__ float Ts[10 * 272];
   __shared__ float Bs[C];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
   const int bh = blockIdx.x / nch, c = blockIdx.x % nch;
   const int t0 = c * C, nt = min(C, N - t0);
   u32x4* rec = ws + ((size_t)bh * nch + c) * RR::UNITS;
 
-  // kh = phi(k) / sum phi(k); rows at or past nt are zero (their beta is zero too).
+  // kh = phi(k) / sum phi(k), split into head and tail, into LDS and the record;
+  // rows at or past nt are zero (their beta is zero too).
   {
     float4 raw[C * UPR / NT];
     const T* src = k + ((size_t)bh * N + t0) * D;
@@ -127,35 +135,28 @@ __global__ __launch_bounds__(NT) void dn_prep_kernel(const T* __restrict__ k, co
     }
     const float bt = ld_scalar<T>(beta + (size_t)bh * N + t0 + min(tid & (C - 1), nt - 1));
     if (tid < C) Bs[tid] = tid < nt ? bt : 0.f;
+    u32x2* rec2 = reinterpret_cast<u32x2*>(rec);
 #pragma unroll
     for (int i = 0; i < C * UPR / NT; ++i) {
       const int u = tid + NT * i, row = u / UPR, c4 = (u % UPR) * 4;
-      float4 x = float4{phi(raw[i].x), phi(raw[i].y), phi(raw[i].z), phi(raw[i].w)};
-      float s = (x.x + x.y) + (x.z + x.w);
+      f32x4 x{phi(raw[i].x), phi(raw[i].y), phi(raw[i].z), phi(raw[i].w)};
+      float s = (x[0] + x[1]) + (x[2] + x[3]);
       s = UPR == 16 ? sum16(s) : sum8(s);
       const float inv = row < nt ? __builtin_amdgcn_rcpf(s) : 0.f;  // 1 ulp
-      x = float4{x.x * inv, x.y * inv, x.z * inv, x.w * inv};
-      *reinterpret_cast<float4*>(&Ks[row * KS + c4]) = x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] *= inv;
+      const u32x4 hl = split4(x);
+      const int e8 = swz<U8>(row, c4) >> 2;  // 8-byte half unit
+      unit8<U8>(Ki[0], row, c4) = u32x2{hl[0], hl[1]};
+      unit8<U8>(Ki[1], row, c4) = u32x2{hl[2], hl[3]};
+      rec2[e8] = u32x2{hl[0], hl[1]};
+      rec2[2 * C * U8 + e8] = u32x2{hl[2], hl[3]};
     }
   }
   __syncthreads();
 
-  // kh image for the chain kernel: head and tail tiles, swizzled.
-#pragma unroll
-  for (int i = 0; i < C * U8 / NT; ++i) {
-    const int u = tid + NT * i, row = u / U8, c8 = (u % U8) * 8;
-    const float4 a = *reinterpret_cast<const float4*>(&Ks[row * KS + c8]);
-    const float4 b = *reinterpret_cast<const float4*>(&Ks[row * KS + c8 + 4]);
-    const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    u32x4 h, l;
-    split8(x, h, l);
-    const int unit = swz<U8>(row, c8) >> 3;
-    rec[unit] = h;
-    rec[C * U8 + unit] = l;
-  }
-
-  // G blocks on and below the diagonal: tile p = i (i + 1) / 2 + j for block (i, j),
-  // j <= i; wave w takes p = w, w + 4, w + 8.
+  // G blocks on and below the diagonal (d-contraction on split-bf16 MFMA):
+  // tile p = i (i + 1) / 2 + j for block (i, j), j <= i; wave w takes p = w, w + 4, w + 8.
 #pragma unroll
   for (int it = 0; it < 3; ++it) {
     const int p = w + 4 * it;
@@ -163,11 +164,12 @@ __global__ __launch_bounds__(NT) void dn_prep_kernel(const T* __restrict__ k, co
     const int j = min(p, 9) - i * (i + 1) / 2;
     f32x4 acc{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < D / 4; ++kk)
-      acc = mma(Ks[(16 * i + n) * KS + 4 * kk + g], Ks[(16 * j + n) * KS + 4 * kk + g], acc);
+    for (int s = 0; s < SL; ++s)
+      acc = mma3(unit16<U8>(Ki[0], 16 * i + n, 32 * s + 8 * g), unit16<U8>(Ki[1], 16 * i + n, 32 * s + 8 * g),
+                 unit16<U8>(Ki[0], 16 * j + n, 32 * s + 8 * g), unit16<U8>(Ki[1], 16 * j + n, 32 * s + 8 * g), acc);
     if (p < 10) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Gs[(16 * i + 4 * g + r) * FS + 16 * j + n] = acc[r];
+      for (int r = 0; r < 4; ++r) Gs[lb(16 * i + 4 * g + r, 16 * j + n)] = acc[r];
     }
   }
   __syncthreads();
@@ -184,10 +186,10 @@ __global__ __launch_bounds__(NT) void dn_prep_kernel(const T* __restrict__ k, co
       const float x = Bs[base + t] * z[t];
       z[t] = x;
 #pragma unroll
-      for (int t2 = t + 1; t2 < 16; ++t2) z[t2] -= Gs[(base + t2) * FS + base + t] * x;
+      for (int t2 = t + 1; t2 < 16; ++t2) z[t2] -= Gs[lb(base + t2, base + t)] * x;
     }
 #pragma unroll
-    for (int t = 0; t < 16; ++t) Ts[(base + t) * FS + base + n] = z[t];
+    for (int t = 0; t < 16; ++t) Ts[lb(base + t, base + n)] = z[t];
   }
   __syncthreads();
 
@@ -200,13 +202,13 @@ __global__ __launch_bounds__(NT) void dn_prep_kernel(const T* __restrict__ k, co
     f32x4 y{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
-      y = mma(Gs[(16 * a + n) * FS + 16 * b + 4 * kk + g], Ts[(16 * b + 4 * kk + g) * FS + 16 * b + n], y);
+      y = mma(Gs[lb(16 * a + n, 16 * b + 4 * kk + g)], Ts[lb(16 * b + 4 * kk + g, 16 * b + n)], y);
     f32x4 x{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) x = mma(Ts[(16 * a + n) * FS + 16 * a + 4 * g + r], y[r], x);
+    for (int r = 0; r < 4; ++r) x = mma(Ts[lb(16 * a + n, 16 * a + 4 * g + r)], y[r], x);
     if (w < 2) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Ts[(16 * a + 4 * g + r) * FS + 16 * b + n] = -x[r];
+      for (int r = 0; r < 4; ++r) Ts[lb(16 * a + 4 * g + r, 16 * b + n)] = -x[r];
     }
   }
   __syncthreads();
@@ -214,7 +216,8 @@ __global__ __launch_bounds__(NT) void dn_prep_kernel(const T* __restrict__ k, co
   // T[32:64][0:32] = -T_B (G[32:64][0:32] T_A).  Wave w forms block (2 + a2, c2),
   // a2 = w / 2, c2 = w % 2: -sum_{b2 <= a2} T[2 + a2][2 + b2] Y[b2],
   // Y[b2] = sum_{e >= c2} G[2 + b2][e] T[e][c2] (terms outside the triangles are
-  // masked to zero, so every wave runs the same products).
+  // masked to zero, so every wave runs the same products; a masked term reads a
+  // block inside the triangle instead of one outside it).
   {
     const int a2 = w >> 1, c2 = w & 1;
     f32x4 x{0.f, 0.f, 0.f, 0.f};
@@ -225,21 +228,21 @@ __global__ __launch_bounds__(NT) void dn_prep_kernel(const T* __restrict__ k, co
       for (int e = 0; e < 2; ++e)
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          // both operands masked: the block T[0][1] was never written
           const bool on = e >= c2;
-          const float ga = on ? Gs[(16 * (2 + b2) + n) * FS + 16 * e + 4 * kk + g] : 0.f;
-          const float tb = on ? Ts[(16 * e + 4 * kk + g) * FS + 16 * c2 + n] : 0.f;
+          const float ga = on ? Gs[lb(16 * (2 + b2) + n, 16 * e + 4 * kk + g)] : 0.f;
+          const float tb = on ? Ts[lb(16 * e + 4 * kk + g, 16 * (on ? c2 : 0) + n)] : 0.f;
           y = mma(ga, tb, y);
         }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float ta = b2 <= a2 ? Ts[(16 * (2 + a2) + n) * FS + 16 * (2 + b2) + 4 * g + r] : 0.f;
+        const bool on = b2 <= a2;
+        const float ta = on ? Ts[lb(16 * (2 + a2) + n, 16 * (2 + (on ? b2 : 0)) + 4 * g + r)] : 0.f;
         x = mma(ta, y[r], x);
       }
     }
     // The blocks written here (rows 32.., columns ..31) are read by no wave above.
 #pragma unroll
-    for (int r = 0; r < 4; ++r) Ts[(16 * (2 + a2) + 4 * g + r) * FS + 16 * c2 + n] = -x[r];
+    for (int r = 0; r < 4; ++r) Ts[lb(16 * (2 + a2) + 4 * g + r, 16 * c2 + n)] = -x[r];
   }
   __syncthreads();
 
@@ -251,11 +254,9 @@ __global__ __launch_bounds__(NT) void dn_prep_kernel(const T* __restrict__ k, co
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const bool ok = 2 * sg + h <= bw;
-      const float4 t4 = *reinterpret_cast<const float4*>(&Ts[(16 * bw + ln) * FS + 32 * sg + 16 * h + 4 * lg]);
-      x[4 * h + 0] = ok ? t4.x : 0.f;
-      x[4 * h + 1] = ok ? t4.y : 0.f;
-      x[4 * h + 2] = ok ? t4.z : 0.f;
-      x[4 * h + 3] = ok ? t4.w : 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        x[4 * h + r] = ok ? Ts[lb(16 * bw + ln, ok ? 32 * sg + 16 * h + 4 * lg + r : 0)] : 0.f;
     }
     u32x4 h, lo;
     split8(x, h, lo);
