@@ -45,8 +45,11 @@
 // reads free of bank conflicts.
 #include <stdlib.h>
 
+#include <algorithm>
 #include <atomic>
 #include <chrono>
+#include <map>
+#include <mutex>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -374,7 +377,8 @@ template <int D, int M, bool LOCAL, bool EXACT>
 __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, bf16_t* __restrict__ o,
     int N, int nblk, int BH, const float* S0, const float* z0, float* S_out, float* z_out,
-    unsigned long long* flags, char* agg_ws, char* incl_ws, unsigned long long epoch, unsigned long long spin_ticks) {
+    unsigned long long* flags, char* agg_ws, char* incl_ws, unsigned long long epoch, unsigned long long spin_ticks,
+    int incl_period) {
   using GG = G<D, M>;
   __shared__ Smem<D, M> sm;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
@@ -501,7 +505,9 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
 
   // The block increment is published now; its stores drain while phase 3a runs.
   const size_t slot = (size_t)bh * nblk + b;
-  if (b > 0) agg_store<D, M, LOCAL, EXACT>(agg_ws + slot * GG::SLOT, L, w, lane, n, g);
+  // (Block 0 publishes its increment too when it publishes no inclusive prefix.)
+  const bool agg0 = b == 0 && incl_period > 1 && nblk > 1;
+  if (b > 0 || agg0) agg_store<D, M, LOCAL, EXACT>(agg_ws + slot * GG::SLOT, L, w, lane, n, g);
 
   // ---------------- phase 3a: outputs relative to the block start ----------------
   // For query i of chunk c: num_i = phi(q_i)^T (P + S_c) + sum_{j in c, j<=i} A_ij v_j,
@@ -586,6 +592,12 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
   // publishes nothing within the spin bound) computes increments differently.
   Tiles<D, M> P;
   tiles_zero<D, M>(P);
+  if (agg0) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's stores are complete
+    __syncthreads();
+    if (tid == 0)
+      __hip_atomic_store(&flags[slot], flag_word(epoch, xcc, 1ull), __ATOMIC_RELAXED, FLAG_SCOPE);
+  }
   if (b > 0) {
     __builtin_amdgcn_s_waitcnt(0);  // this wave's stores are complete
     __syncthreads();
@@ -597,7 +609,9 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
     if (w == 0) {
       const int W = b < 64 ? b : 64;
       const unsigned long long inwin = W >= 64 ? ~0ull : ((1ull << W) - 1);
-      int pstar = -4;  // -4: timeout, -3: no inclusive prefix within the window
+      // -4: timeout; -3: no inclusive prefix within the window; -1: none at all,
+      // every predecessor back to block 0 has its increment (fold from S0)
+      int pstar = -4;
       const unsigned long long start = rt_clock();
       for (int it = 0; it < (1 << 20); ++it) {
         int st = 0;
@@ -611,7 +625,7 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
         const int first = incl ? __builtin_ctzll(incl) : W;
         const unsigned long long need = first >= 64 ? inwin : ((1ull << first) - 1);
         if ((ready & need) == need) {
-          pstar = first < W ? b - 1 - first : -3;
+          pstar = first < W ? b - 1 - first : W == b ? -1 : -3;
           break;
         }
         if (rt_clock() - start > spin_ticks) break;
@@ -621,8 +635,9 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
     }
     __syncthreads();
     const int pstar = sm.status;
-    if (pstar >= 0) {
-      slot_load<D, M, LOCAL>(P, incl_ws + ((size_t)bh * nblk + pstar) * GG::SLOT, w, lane, g);
+    if (pstar >= -1) {
+      if (pstar >= 0) slot_load<D, M, LOCAL>(P, incl_ws + ((size_t)bh * nblk + pstar) * GG::SLOT, w, lane, g);
+      else if (S0) tiles_add_from_state<D, M>(P, S0 + (size_t)bh * D * M, z0 + (size_t)bh * D, w, n, g);
       int j = pstar + 1;
       for (; j + 2 <= b; j += 2) {  // two loads in flight, added in order
         Tiles<D, M> a0, a1;
@@ -679,7 +694,12 @@ __global__ __launch_bounds__(NT, 2) void causal_fused_kernel(
     tiles_add_from_state<D, M>(P, S0 + (size_t)bh * D * M, z0 + (size_t)bh * D, w, n, g);
   }
 
-  {
+  // Inclusive prefixes are published by every incl_period-th block only (the
+  // last one of each group of that many consecutive blocks of a head, which is
+  // all of a head that is resident at once); the blocks after it fold the
+  // increments from there.  Every published prefix is the same left fold, so
+  // the results do not depend on which one a block finds.
+  if (b == nblk - 1 || b % incl_period == incl_period - 1) {
     Tiles<D, M> inc = L;
     round_increment<D, M, EXACT>(inc);  // the increment as the successors fold it
 #pragma unroll
@@ -771,6 +791,22 @@ static unsigned long long next_epoch() {
   return (g_epoch.fetch_add(1) + 1) & EPOCH_MASK;
 }
 
+// Workgroups of a kernel resident at once on the current device (cached).
+static int resident_wgs(const void* kernel) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 512;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_pair(dev, kernel);
+  const auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int cus = 0, per = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, NT, 0) != hipSuccess || per <= 0) per = 1;
+  return cache[key] = cus * per;
+}
+
 __global__ __launch_bounds__(256) void copy_state_kernel(const float* S, const float* z, float* S2, float* z2,
                                                         long long nS, long long nz) {
   const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
@@ -810,10 +846,19 @@ static hipError_t fused_impl(const void* q, const void* k, const void* v, void* 
   // states are exchanged through its L2.
   const dim3 grid((unsigned)nblk * (unsigned)BH), block(NT);
   const bool exact = S_out != nullptr || o == nullptr;
-#define LA_FUSED_LAUNCH(LOC, EX)                                                                                  \
-  hipLaunchKernelGGL((causal_fused_kernel<D, M, LOC, EX>), grid, block, 0, stream, (const bf16_t*)q, (const bf16_t*)k, \
-                     (const bf16_t*)v, (bf16_t*)o, N, nblk, BH, S0, z0, S_out, z_out, flags, agg, incl, next_epoch(),  \
-                     spin_ticks)
+  // Inclusive prefixes every second block of a head (every block when a head
+  // has at most one block resident at a time).  A block mostly finds a recent
+  // predecessor's prefix within its own round, so sparser prefixes deepen the
+  // folds: on the long bf16 workload every 2nd block gave 145.5 us per call,
+  // every block 147.4, every 4th 147.0, every 8th 154.7, every 16th 165.4.
+#define LA_FUSED_LAUNCH(LOC, EX)                                                                                    \
+  do {                                                                                                            \
+    const void* fn = (const void*)causal_fused_kernel<D, M, LOC, EX>;                                              \
+    const int period = std::min(2, std::max(1, resident_wgs(fn) / std::max(BH, 1)));                             \
+    hipLaunchKernelGGL((causal_fused_kernel<D, M, LOC, EX>), grid, block, 0, stream, (const bf16_t*)q,               \
+                       (const bf16_t*)k, (const bf16_t*)v, (bf16_t*)o, N, nblk, BH, S0, z0, S_out, z_out, flags, agg, \
+                       incl, next_epoch(), spin_ticks, period);                                                     \
+  } while (0)
   if (BH % 8 == 0) {
     if (exact) LA_FUSED_LAUNCH(true, true);
     else LA_FUSED_LAUNCH(true, false);
