@@ -583,12 +583,26 @@ def main():
     if args.workload in FMAPS:
         # The recurrent form's arithmetic with C features: S update 2CM, numerator
         # 2CM, z C, denominator 2C, the map itself C.  fp32 matrix work dominates.
+        # The degree-2 polynomial map is defined with D^2 features, but x_a x_b =
+        # x_b x_a leaves D (D + 1) / 2 distinct ones: `frac` counts those (the
+        # minimal exact map); the kernels carry the pairs a <= b in groups of 16
+        # (16 * 8 (D/16) (D/16 + 1) features), reported beside it with the defined
+        # count.  DPFP's 2 nu D features are all distinct.
         C = la.fmap_dim(fm, nu, w.D)
-        flops = units * (4 * C * w.M + 4 * C)
-        tflops = flops / (launch_ms / 1e3) / 1e12
+        if fm == la.FMAP_POLY2:
+            c_min, c_exec = w.D * (w.D + 1) // 2, 16 * 8 * (w.D // 16) * (w.D // 16 + 1)
+        else:
+            c_min = c_exec = C
+        fl = lambda c: units * (4 * c * w.M + 4 * c)
+        flops = fl(c_min)
+        tfl = lambda c: fl(c) / (launch_ms / 1e3) / 1e12
+        tflops = tfl(c_min)
         roofline = {"bound": "mfma", "achieved": round(tflops, 3), "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(tflops / FP32_PEAK_TFLOPS, 4), "traffic": traffic, "kernel": kernel,
-                    "algorithmic_flops_per_launch": flops, "feature_dim": C, "launch_ms": round(launch_ms, 5),
+                    "algorithmic_flops_per_launch": flops, "feature_dim": c_min, "launch_ms": round(launch_ms, 5),
+                    "feature_dims": {"minimal_exact": c_min, "executed": c_exec, "defined": C},
+                    "frac_executed": round(tfl(c_exec) / FP32_PEAK_TFLOPS, 4),
+                    "frac_defined": round(tfl(C) / FP32_PEAK_TFLOPS, 4),
                     "hbm": {"achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                             "frac": round(achieved / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": alg_bytes}}
     if args.workload == "deltanet":
