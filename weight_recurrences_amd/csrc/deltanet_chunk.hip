@@ -320,11 +320,14 @@ __global__ __launch_bounds__(NTC) void dn_chain_kernel(const T* __restrict__ q, 
   constexpr int KU = RR::KI / NT;   // kh image units per helper thread
   __shared__ __attribute__((aligned(16))) bf16_t Kt[2][2][C * D];  // [buffer][head, tail] kh [t][d], swizzled
   __shared__ __attribute__((aligned(16))) bf16_t Qt[2][2][C * D];  // qh
-  __shared__ __attribute__((aligned(16))) bf16_t Wt[2][16 * D];    // slice [m][d], head and tail
+  // The slice [m][d] (head, tail) at the start of chunks of either parity, and
+  // after token tiles 0, 1, 2 of the current chunk.
+  __shared__ __attribute__((aligned(16))) bf16_t Wt[2][2][16 * D];
+  __shared__ __attribute__((aligned(16))) bf16_t Wp[3][2][16 * D];
   __shared__ u32x4 Rx[4][64];                                      // R tiles, per token tile and lane
   __shared__ u32x4 Ux[4][64];                                      // U tiles
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
-  const bool path = wv < 4;  // wave-uniform role
+  const bool path = __builtin_amdgcn_readfirstlane(wv) < 4;  // the wave's role (a scalar branch)
   const int w = wv & 3, ht = tid & (NT - 1);
   const int xcd = blockIdx.x & 7, jx = blockIdx.x >> 3;
   const int bh = (jx / NS) * 8 + xcd, m0 = 16 * (jx % NS);
@@ -335,16 +338,19 @@ __global__ __launch_bounds__(NTC) void dn_chain_kernel(const T* __restrict__ q, 
   const T* vb = v + (size_t)bh * N * M + m0 + n;
   const u32x4* recb = ws + (size_t)bh * nch * RR::UNITS;
 
-  // Raw q of a chunk (rows clamped into the chunk; masked when staged) and its
-  // kh image (helper waves).
-  auto load_qk = [&](int c, float4 (&rq)[NU], u32x4 (&rk)[KU]) __attribute__((always_inline)) {
+  // Raw q of a chunk, units [i0, i1) (rows clamped into the chunk; masked when
+  // staged), and its kh image (helper waves).
+  auto load_q = [&](int c, float4 (&rq)[NU], int i0, int i1) __attribute__((always_inline)) {
     const int t0 = c * C, last = min(C, N - t0) - 1;
     const T* qc = qb + (size_t)t0 * D;
 #pragma unroll
     for (int i = 0; i < NU; ++i) {
+      if (i < i0 || i >= i1) continue;
       const int u = ht + NT * i;
       rq[i] = load4<T>(qc + min(u / UPR, last) * D + (u % UPR) * 4);
     }
+  };
+  auto load_k = [&](int c, u32x4 (&rk)[KU]) __attribute__((always_inline)) {
     const u32x4* rc = recb + (size_t)c * RR::UNITS;
 #pragma unroll
     for (int i = 0; i < KU; ++i) rk[i] = rc[ht + NT * i];
@@ -390,92 +396,95 @@ __global__ __launch_bounds__(NTC) void dn_chain_kernel(const T* __restrict__ q, 
   };
 
   // Path wave: the slice's d tile dt, transposed: wm[r] = W[m0 + n][16 dt + 4 g + r].
+  // (Every wave loads it and waits for it here: a load left pending on only
+  // some paths into the loop would make the compiler wait for all loads in
+  // flight at its first use inside the loop, on every chunk.)
   f32x4 wm{0.f, 0.f, 0.f, 0.f};
-  if (W0 && path) {
+  if (W0) {
     const float4 x = *reinterpret_cast<const float4*>(W0 + ((size_t)bh * M + m0 + n) * D + 16 * dt + 4 * g);
     wm = f32x4{x.x, x.y, x.z, x.w};
   }
-  auto put_w = [&]() __attribute__((always_inline)) {
+  __builtin_amdgcn_s_waitcnt(0);
+  auto put_w = [&](bf16_t (&dst)[2][16 * D], f32x4 x) __attribute__((always_inline)) {
     if (w < TD) {
-      const u32x4 hl = split4(wm);
-      unit8<U8>(Wt[0], n, 16 * dt + 4 * g) = u32x2{hl[0], hl[1]};
-      unit8<U8>(Wt[1], n, 16 * dt + 4 * g) = u32x2{hl[2], hl[3]};
+      const u32x4 hl = split4(x);
+      unit8<U8>(dst[0], n, 16 * dt + 4 * g) = u32x2{hl[0], hl[1]};
+      unit8<U8>(dst[1], n, 16 * dt + 4 * g) = u32x2{hl[2], hl[3]};
     }
   };
 
-  // Helper wave: outputs of a chunk are stored during the next one, after that
-  // chunk's loads are issued (loads and stores share one counter, and a store
-  // issued before a load makes every later wait for the load wait for it too).
-  // Rows past the chunk fall outside the buffer resource and are dropped, with
-  // no branch that would cost the compiler its count of the loads in flight.
-  f32x4 opend{0.f, 0.f, 0.f, 0.f};
-  auto store_o = [&](int c) __attribute__((always_inline)) {  // chunk c < 0: nothing (empty resource)
-    const int cc = max(c, 0), t0 = cc * C;
+  // Helper wave: outputs of chunk c, formed at the start of chunk c + 1 (after
+  // that chunk's loads are issued: loads and stores share one counter, and a
+  // store issued before a load makes every later wait for the load wait for it
+  // too).  Rows past the chunk fall outside the buffer resource and are
+  // dropped, with no branch that would cost the compiler its count of the loads
+  // in flight.
+  //   o_t = W_{<t} qh_t + sum_{s <= t} (qh_t . kh_s) u_s for t in token tile w
+  //       = Qh_w Wa^T + tril(Qh_w Kh_w^T) U_w,
+  // with Wa the memory after token tiles 0 .. w - 1 of the chunk (its start for
+  // w = 0): the score products with earlier token tiles are folded into Wa,
+  // which the path waves form alongside the memory update.
+  auto outputs = [&](int c) __attribute__((always_inline)) {  // c < 0: nothing stored (empty resource)
+    const int pb = c & 1, t0 = max(c, 0) * C;
+    const bf16_t *Kh = Kt[pb][0], *Kl = Kt[pb][1], *Qh = Qt[pb][0], *Ql = Qt[pb][1];
+    const bf16_t(&Wa)[2][16 * D] = w == 0 ? Wt[pb] : Wp[w - 1];
+    const f32x4 z4{0.f, 0.f, 0.f, 0.f};
+    f32x4 O3[3] = {z4, z4, z4}, sacc = z4;
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+      const u32x4 qh = unit16<U8>(Qh, 16 * w + n, 32 * s + 8 * g), ql = unit16<U8>(Ql, 16 * w + n, 32 * s + 8 * g);
+      mma3s(qh, ql, unit16<U8>(Wa[0], n, 32 * s + 8 * g), unit16<U8>(Wa[1], n, 32 * s + 8 * g), O3);
+      sacc = mma3(unit16<U8>(Kh, 16 * w + n, 32 * s + 8 * g), unit16<U8>(Kl, 16 * w + n, 32 * s + 8 * g), qh, ql,
+                  sacc);
+    }
+    // the diagonal score tile S^T[s][t], s, t in token tile w, masked to s <= t,
+    // in half w % 2 of slab w / 2 of a token contraction (the other half zero)
+    f32x4 sm;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sm[r] = 4 * g + r <= n ? sacc[r] : 0.f;
+    const u32x4 shl = split4(sm);
+    const bool hi = w & 1;
+    const u32x4 sh = hi ? u32x4{0u, 0u, shl[0], shl[1]} : u32x4{shl[0], shl[1], 0u, 0u};
+    const u32x4 sl = hi ? u32x4{0u, 0u, shl[2], shl[3]} : u32x4{shl[2], shl[3], 0u, 0u};
+    const int sg = w >> 1;
+    const u32x4 ua = Ux[2 * sg][lane], ub = Ux[2 * sg + 1][lane];
+    mma3s(sh, sl, u32x4{ua[0], ua[1], ub[0], ub[1]}, u32x4{ua[2], ua[3], ub[2], ub[3]}, O3);
+    const f32x4 oc = sum3(O3);
     const int bytes = c < 0 ? 0 : min(C, N - t0) * M * (int)sizeof(T);
     const __amdgpu_buffer_rsrc_t ob = out_rsrc(o + ((size_t)bh * N + t0) * M, bytes);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) store_elem<T>(ob, ((16 * w + 4 * g + r) * M + m0 + n) * (int)sizeof(T), opend[r]);
+    for (int r = 0; r < 4; ++r) store_elem<T>(ob, ((16 * w + 4 * g + r) * M + m0 + n) * (int)sizeof(T), oc[r]);
   };
 
-  // One chunk.  On entry kh, qh of chunk c are staged in buffer c & 1; helper
-  // (rq, rk) hold chunk c + 1's raw q and kh image, and path (tt, rv) chunk c's T
-  // and V.  Helpers load chunk c + 2's q and kh into (rq2, rk2) and stage chunk
-  // c + 1 into the other buffer; path waves load chunk c + 1's T and V.
-  auto chunk = [&](int c, float4 (&rq)[NU], u32x4 (&rk)[KU], float4 (&rq2)[NU], u32x4 (&rk2)[KU],
-                   const u32x4 (&tt)[4], const float (&rv)[4], u32x4 (&tt2)[4], float (&rv2)[4])
-                   __attribute__((always_inline)) {
+  // The two roles run separate loops with the same three barriers per chunk,
+  // so that the compiler's count of each wave's loads in flight covers only its
+  // own loads (a loop that interleaves both roles' code would make every wait
+  // count the other role's loads and stores as well).
+  //
+  // Path waves.  Chunk c: X and R; U; the memory update.  On entry (tt, rv) hold
+  // chunk c's T and V; chunk c + 1's are loaded into (tt2, rv2).
+  auto path_chunk = [&](int c, const u32x4 (&tt)[4], const float (&rv)[4], u32x4 (&tt2)[4], float (&rv2)[4])
+                        __attribute__((always_inline)) {
     const int buf = c & 1, nt = min(C, N - c * C);
-    const bool more = c + 1 < nch;
-    const bf16_t *Kh = Kt[buf][0], *Kl = Kt[buf][1], *Qh = Qt[buf][0], *Ql = Qt[buf][1];
+    const bf16_t *Kh = Kt[buf][0], *Kl = Kt[buf][1];
     const f32x4 z4{0.f, 0.f, 0.f, 0.f};
-    f32x4 O3[3] = {z4, z4, z4};
-    u32x4 qh[SL], ql[SL], sh[2], sl[2];
-    // score tiles 2 sg, 2 sg + 1 against the helper's token tile w, as operands
-    auto scores = [&](int sg) __attribute__((always_inline)) {
-      float sv[8];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int jt = 2 * sg + h;
-        f32x4 acc = z4;
-#pragma unroll
-        for (int s = 0; s < SL; ++s)
-          acc = mma3(unit16<U8>(Kh, 16 * jt + n, 32 * s + 8 * g), unit16<U8>(Kl, 16 * jt + n, 32 * s + 8 * g), qh[s],
-                     ql[s], acc);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sv[4 * h + r] = 16 * jt + 4 * g + r <= 16 * w + n ? acc[r] : 0.f;
-      }
-      split8(sv, sh[sg], sl[sg]);
-    };
-
-    if (path) {
-      load_tv(min(c + 1, nch - 1), tt2, rv2);  // past the end: reloads the last chunk (unused)
-      // X = Kh W^T for token tile w; R = V - X (rows past the chunk are zero).
+    load_tv(min(c + 1, nch - 1), tt2, rv2);  // past the end: reloads the last chunk (unused)
+    // X = Kh W^T for token tile w; R = V - X (rows past the chunk are zero).
+    {
       f32x4 X3[3] = {z4, z4, z4};
 #pragma unroll
       for (int s = 0; s < SL; ++s)
         mma3s(unit16<U8>(Kh, 16 * w + n, 32 * s + 8 * g), unit16<U8>(Kl, 16 * w + n, 32 * s + 8 * g),
-              unit16<U8>(Wt[0], n, 32 * s + 8 * g), unit16<U8>(Wt[1], n, 32 * s + 8 * g), X3);
+              unit16<U8>(Wt[buf][0], n, 32 * s + 8 * g), unit16<U8>(Wt[buf][1], n, 32 * s + 8 * g), X3);
       const f32x4 X = sum3(X3);
       f32x4 R;
 #pragma unroll
       for (int r = 0; r < 4; ++r) R[r] = (16 * w + 4 * g + r < nt ? rv[r] : 0.f) - X[r];
       Rx[w][lane] = split4(R);
-    } else {
-      load_qk(min(c + 2, nch - 1), rq2, rk2);
-      store_o(c - 1);
-      // P = Qh W^T (the slice tile is rewritten only after the second barrier).
-#pragma unroll
-      for (int s = 0; s < SL; ++s) {
-        qh[s] = unit16<U8>(Qh, 16 * w + n, 32 * s + 8 * g);
-        ql[s] = unit16<U8>(Ql, 16 * w + n, 32 * s + 8 * g);
-        mma3s(qh[s], ql[s], unit16<U8>(Wt[0], n, 32 * s + 8 * g), unit16<U8>(Wt[1], n, 32 * s + 8 * g), O3);
-      }
-      scores(0);
     }
     __syncthreads();
-
-    if (path) {
-      // U = T R for token tile w.
+    // U = T R for token tile w.
+    {
       f32x4 U3[3] = {z4, z4, z4};
 #pragma unroll
       for (int sg = 0; sg < 2; ++sg) {
@@ -486,66 +495,86 @@ __global__ __launch_bounds__(NTC) void dn_chain_kernel(const T* __restrict__ q, 
               u32x4{a[2], a[3], b[2], b[3]}, U3);
       }
       Ux[w][lane] = split4(sum3(U3));
-    } else {
-      scores(1);
-      if (more) {
-        copy_k(buf ^ 1, rk);
-        stage_q(buf ^ 1, c + 1, rq, 0, NU / 2);
-      }
     }
     __syncthreads();
-
-    u32x4 uh[2], ul[2];
-#pragma unroll
-    for (int sg = 0; sg < 2; ++sg) {
-      const u32x4 a = Ux[2 * sg][lane], b = Ux[2 * sg + 1][lane];
-      uh[sg] = u32x4{a[0], a[1], b[0], b[1]};
-      ul[sg] = u32x4{a[2], a[3], b[2], b[3]};
-    }
-    if (path) {
-      // W^T tile dt += Kh^T U.
-      f32x4 W3[3] = {wm, z4, z4};
+    // W^T tile dt += Kh^T U, and the memory after token tiles 0, 1, 2 (for the
+    // outputs): slab 0 (tiles 0, 1), then slab 1 (tiles 2, 3); a tile alone is
+    // the slab with the other tile's tokens zeroed in the Kh^T operand.
+    {
+      u32x4 uh[2], ul[2], ah[2], al[2];
 #pragma unroll
       for (int sg = 0; sg < 2; ++sg) {
-        const bf16x8 ah = jfrag<U8>(Kh, 32 * sg, 16 * dt, g, n), al = jfrag<U8>(Kl, 32 * sg, 16 * dt, g, n);
-        mma3s(__builtin_bit_cast(u32x4, ah), __builtin_bit_cast(u32x4, al), uh[sg], ul[sg], W3);
+        const u32x4 a = Ux[2 * sg][lane], b = Ux[2 * sg + 1][lane];
+        uh[sg] = u32x4{a[0], a[1], b[0], b[1]};
+        ul[sg] = u32x4{a[2], a[3], b[2], b[3]};
+        ah[sg] = __builtin_bit_cast(u32x4, jfrag<U8>(Kh, 32 * sg, 16 * dt, g, n));
+        al[sg] = __builtin_bit_cast(u32x4, jfrag<U8>(Kl, 32 * sg, 16 * dt, g, n));
       }
-      wm = sum3(W3);
-      put_w();
-    } else {
-      // o = P + S U (stored during the next chunk).
-#pragma unroll
-      for (int sg = 0; sg < 2; ++sg) mma3s(sh[sg], sl[sg], uh[sg], ul[sg], O3);
-      opend = sum3(O3);
-      if (more) stage_q(buf ^ 1, c + 1, rq, NU / 2, NU);
+      const u32x4 lo2{0xffffffffu, 0xffffffffu, 0u, 0u};  // the first tile of a slab
+      f32x4 A1[3] = {wm, z4, z4};
+      mma3s(ah[0], al[0], uh[0], ul[0], A1);
+      const f32x4 w1 = sum3(A1);  // after tiles 0, 1
+      f32x4 F3[3] = {w1, z4, z4};
+      mma3s(ah[1], al[1], uh[1], ul[1], F3);
+      const f32x4 w0m = wm;
+      wm = sum3(F3);  // the next chunk's memory
+      put_w(Wt[buf ^ 1], wm);
+      f32x4 A0[3] = {w0m, z4, z4}, A2[3] = {w1, z4, z4};
+      mma3s(ah[0] & lo2, al[0] & lo2, uh[0], ul[0], A0);
+      mma3s(ah[1] & lo2, al[1] & lo2, uh[1], ul[1], A2);
+      put_w(Wp[0], sum3(A0));
+      put_w(Wp[1], w1);
+      put_w(Wp[2], sum3(A2));
     }
     __syncthreads();
   };
 
-  float4 rqa[NU], rqb[NU];
-  u32x4 rka[KU], rkb[KU];
-  u32x4 tta[4], ttb[4];
-  float rva[4], rvb[4];
-  // Prologue in the loop's own order, so that the count of loads in flight at
-  // the loop head is the same on entry as on the back edge.
+  // Helper waves.  Chunk c: the outputs of chunk c - 1; half of chunk c + 1
+  // staged (kh copied, qh formed) and half of the q two chunks ahead loaded;
+  // the other half, and the kh image two chunks ahead.  Past the last chunk the
+  // staging writes zeros (no row is inside the chunk) into a buffer nothing
+  // reads, and the loads re-read the last chunk: no branches.
+  auto helper_chunk = [&](int c, float4 (&rq)[NU], u32x4 (&rk)[KU]) __attribute__((always_inline)) {
+    const int buf = c & 1;
+    const int cn = min(c + 2, nch - 1);
+    outputs(c - 1);  // chunk 0: operands unused, nothing stored
+    __syncthreads();
+    copy_k(buf ^ 1, rk);
+    stage_q(buf ^ 1, c + 1, rq, 0, NU / 2);
+    load_q(cn, rq, 0, NU / 2);
+    __syncthreads();
+    stage_q(buf ^ 1, c + 1, rq, NU / 2, NU);
+    load_q(cn, rq, NU / 2, NU);
+    load_k(cn, rk);
+    __syncthreads();
+  };
+
   if (path) {
+    u32x4 tta[4], ttb[4];
+    float rva[4], rvb[4];
     load_tv(0, tta, rva);
-    put_w();
+    put_w(Wt[0], wm);
+    __syncthreads();
+    for (int c = 0; c < nch; c += 2) {
+      path_chunk(c, tta, rva, ttb, rvb);
+      if (c + 1 < nch) path_chunk(c + 1, ttb, rvb, tta, rva);
+    }
+    if (W_out && w < TD)
+      *reinterpret_cast<float4*>(W_out + ((size_t)bh * M + m0 + n) * D + 16 * dt + 4 * g) =
+          float4{wm[0], wm[1], wm[2], wm[3]};
   } else {
-    load_qk(0, rqb, rkb);
-    load_qk(min(1, nch - 1), rqa, rka);
-    copy_k(0, rkb);
-    stage_q(0, 0, rqb, 0, NU);
+    float4 rq[NU];
+    u32x4 rk[KU];
+    load_q(0, rq, 0, NU);
+    load_k(0, rk);
+    copy_k(0, rk);
+    stage_q(0, 0, rq, 0, NU);
+    load_q(min(1, nch - 1), rq, 0, NU);
+    load_k(min(1, nch - 1), rk);
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) helper_chunk(c, rq, rk);
+    outputs(nch - 1);
   }
-  __syncthreads();
-  for (int c = 0; c < nch; c += 2) {
-    chunk(c, rqa, rka, rqb, rkb, tta, rva, ttb, rvb);
-    if (c + 1 < nch) chunk(c + 1, rqb, rkb, rqa, rka, ttb, rvb, tta, rva);
-  }
-  if (!path) store_o(nch - 1);
-  if (W_out && path && w < TD)
-    *reinterpret_cast<float4*>(W_out + ((size_t)bh * M + m0 + n) * D + 16 * dt + 4 * g) =
-        float4{wm[0], wm[1], wm[2], wm[3]};
 }
 
 // ----------------------------------------------------------------------------
