@@ -65,15 +65,25 @@ WORKLOAD_SOURCES = {
 FMAPS = {"fmap_dpfp1": (1, 1), "fmap_dpfp2": (1, 2), "fmap_dpfp3": (1, 3), "fmap_poly2": (2, 0)}
 
 
+_CODE_TOKENS = re.compile(r'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'', re.S)
+
+
+def code_text(src: str) -> str:
+    """C++ source without its comments, with whitespace runs collapsed to one
+    space (string and character literals kept as written)."""
+    src = _CODE_TOKENS.sub(lambda m: " " if m.group(0)[0] == "/" else m.group(0), src)
+    return " ".join(src.split())
+
+
 def source_hash(workload: str = None) -> str:
-    """Hash of the kernel sources behind a workload (all of them without one):
-    counter figures taken from another source are stale."""
+    """Hash of the kernel sources behind a workload (all of them without one),
+    comments and layout ignored: counter figures taken from other code are stale."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "weight_recurrences_amd", "csrc")
     names = WORKLOAD_SOURCES.get(workload) or [n for n in os.listdir(csrc) if n.endswith((".hip", ".hpp", ".cpp"))]
     for name in sorted(names):
         h.update(name.encode())
-        h.update(open(os.path.join(csrc, name), "rb").read())
+        h.update(code_text(open(os.path.join(csrc, name), encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -235,9 +235,10 @@ int linattn_fmap_fwd(const void* q, const void* k, const void* v, void* o,
  * The sequence runs in chunks of 64 tokens: per chunk the same recurrence is
  * solved exactly as a unit lower-triangular system in the values written,
  * (I + diag(beta) L) U = diag(beta) (V - Kh W0^T), L the strictly lower part of
- * Kh Kh^T, so that only W0 -> W0 + U^T Kh is sequential.  The workspace holds
- * T = (I + diag(beta) L)^{-1} diag(beta) for every chunk (64 x 64 fp32, 16 KiB),
- * formed for all chunks in parallel before the sequential pass.
+ * Kh Kh^T, so that only W0 -> W0 + U^T Kh is sequential.  The workspace holds,
+ * for every chunk, the normalised keys Kh and T = (I + diag(beta) L)^{-1} diag(beta)
+ * (lower triangle), each as a bf16 head and tail (28 KiB per chunk at D = 64,
+ * 20 KiB at D = 32), formed for all chunks in parallel before the sequential pass.
  * o must not overlap q, k, v, beta, W0, W_out or ws. */
 int deltanet_fwd(const void* q, const void* k, const void* v, const void* beta, void* o,
                  int B, int H, int N, int D, int M, int dtype,

@@ -26,7 +26,11 @@
 //                    (below), laid out as the chain kernel uses them.
 //   dn_chain_kernel  per (head, 16-row slice of W): the chunks in order, the
 //                    slice in registers.  Per chunk: R = V - Kh W^T, U = T R,
-//                    o = Qh W^T + tril(Qh Kh^T) U, W^T += Kh^T U.
+//                    W^T += Kh^T U; for token tile w of the chunk,
+//                    o_w = Qh_w W_{<w}^T + tril(Qh_w Kh_w^T) U_w with W_{<w} the
+//                    memory after the chunk's tiles before w (the score terms with
+//                    earlier tiles folded into it: sum_{j<w} (Qh_w Kh_j^T) U_j =
+//                    Qh_w (sum_{j<w} U_j^T Kh_j)).
 // The chain's products are bf16 MFMA (16x16x32) on operands split into a bf16
 // head and tail (x = h + l to about 2^-17 relative), as h h + h l + l h with fp32
 // accumulation (the tail x tail term, about 2^-16 of a product, is dropped); the
