@@ -48,8 +48,8 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 # Kernel sources each workload's launches are built from (the kernels and the
 # headers they include): a counter summary is current while these are unchanged.
 WORKLOAD_SOURCES = {
-    "causal_long": ["causal_fused.hip", "common.hpp", "lds_tiles.hpp"],
-    "causal_mid": ["causal.hip", "common.hpp"],
+    "causal_long": ["causal_fused.hip", "lookback.hpp", "common.hpp", "lds_tiles.hpp"],
+    "causal_mid": ["causal_fused32.hip", "lookback.hpp", "common.hpp", "lds_tiles.hpp"],
     "causal_bwd_long": ["causal_bwd.hip", "causal_bwd_bf16.hip", "causal.hip", "noncausal.hip", "common.hpp", "lds_tiles.hpp"],
     "noncausal_long": ["noncausal.hip", "common.hpp", "lds_tiles.hpp"],
     "decode": ["decode.hip", "common.hpp"],
@@ -361,7 +361,7 @@ def main():
             ws = torch.empty(max(1, la.causal_workspace_bytes(w.B, w.H, w.N, w.D, w.M, w.dtype)),
                              dtype=torch.uint8, device=dev)
             step = lambda: la.causal(q, k, v, out=o, workspace=ws)
-            kernel = ("causal_fused_kernel (single pass)" if w.dtype == torch.bfloat16 else "linattn_causal_fwd (block_state + state_scan + causal_sweep)")
+            kernel = ("causal_fused_kernel (single pass)" if w.dtype == torch.bfloat16 else "causal_fused32_kernel (single pass)")
         units = w.B * w.H * w.N                      # tokens per step
         es = torch.tensor([], dtype=w.dtype).element_size()
         alg_bytes = units * (2 * w.D + 2 * w.M) * es  # read q, k, v; write o

@@ -43,6 +43,17 @@ def test_version_and_status_strings(lib):
     assert lib.linattn_status_str(99).decode() == "LINATTN_ERR_UNKNOWN"
 
 
+def _single_pass_ws(BH, N, D, M, tblk):
+    """Workspace of the single-pass causal kernels: one 8-byte flag per block,
+    two published states per block (the register image of S, then z, in floats,
+    rounded up to 256 bytes), and room for a private copy of the initial state."""
+    up = lambda x: (x + 255) // 256 * 256
+    nblk = (N + tblk - 1) // tblk
+    tmw = (M // 16) // (4 // (D // 16))
+    slot = up((4 * tmw * 4 * 64 + D) * 4)
+    return up(BH * nblk * 8) + 2 * BH * nblk * slot + up(BH * (D * M + D) * 4)
+
+
 def test_workspace_sizes(lib):
     # long bf16 workload, single-pass kernel: 32 heads x 128 blocks of 256 tokens; one
     # 8-byte flag per block, two published states of (64*64 + 64) floats per block,
@@ -51,10 +62,11 @@ def test_workspace_sizes(lib):
     slot = (64 * 64 + 64) * 4
     init = 32 * (64 * 64 + 64) * 4
     assert lib.linattn_causal_workspace_bytes(2, 16, 32768, 64, 64, 1) == flags + 2 * 32 * 128 * slot + init
-    # float32 causal: blocked kernels, (64*64 + 64) floats per block of 1024 tokens
-    assert lib.linattn_causal_workspace_bytes(2, 16, 32768, 64, 64, 0) == 32 * 32 * (64 * 64 + 64) * 4
-    # a single block per head needs no workspace
-    assert lib.linattn_causal_workspace_bytes(1, 1, 256, 32, 32, 0) == 0
+    assert lib.linattn_causal_workspace_bytes(2, 16, 32768, 64, 64, 1) == _single_pass_ws(32, 32768, 64, 64, 256)
+    # float32 causal, single-pass kernel with blocks of 256 tokens
+    assert lib.linattn_causal_workspace_bytes(2, 16, 32768, 64, 64, 0) == _single_pass_ws(32, 32768, 64, 64, 256)
+    assert lib.linattn_causal_workspace_bytes(1, 1, 256, 32, 32, 0) == _single_pass_ws(1, 256, 32, 32, 256)
+    assert lib.linattn_causal_workspace_bytes(3, 1, 100, 32, 64, 0) == _single_pass_ws(3, 100, 32, 64, 256)
     assert lib.linattn_noncausal_workspace_bytes(1, 1, 256, 32, 32, 0) == 2 * (32 * 32 + 32) * 4
     # delta rule, per chunk of 64 tokens: kh as bf16 head and tail (64 x D x 4 bytes) and
     # T as bf16 head and tail in six 64-lane operand blocks of 32 bytes per lane

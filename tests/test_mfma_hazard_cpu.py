@@ -20,6 +20,7 @@ MIN_DISTANCE = 5
 
 @pytest.mark.skipif(HIPCC is None, reason="hipcc not available")
 @pytest.mark.parametrize("src,pattern", [("causal_fused.hip", "causal_fused_kernel"),
+                                         ("causal_fused32.hip", "causal_fused32_kernel"),
                                          ("noncausal.hip", "nc_"),
                                          ("causal_bwd_bf16.hip", "bf16_kernel"),
                                          ("featmap.hip", "fm_"),

@@ -57,13 +57,14 @@ def test_causal_ragged(dtype, D, M, N):
     assert row_rel_err(host(la.causal(*gpu(q, k, v))), ro) < TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
 @pytest.mark.parametrize("B,H,N", [(1, 1, 40000), (1, 2, 20000), (3, 100, 700), (2, 5, 9000)])
-def test_causal_many_blocks_with_state(B, H, N):
+def test_causal_many_blocks_with_state(dtype, B, H, N):
     """Long sequences over few heads (and many heads over short ones): the
-    single-pass kernel then spreads one head's blocks over several rounds of
-    its persistent grid, which exercises every look-back case."""
-    dtype, D, M = torch.bfloat16, 64, 64
-    say("causal many blocks", B, H, N)
+    single-pass kernels then spread one head's blocks over several rounds of
+    workgroups, which exercises every look-back case."""
+    D, M = 64, 64
+    say("causal many blocks", dtype, B, H, N)
     q, k, v = synth.qkv(B, H, N, D, M, dtype=dtype, seed=B * 1000 + H * 10 + N)
     S0 = torch.randn(B, H, D, M, generator=torch.Generator().manual_seed(N)) * 3
     z0 = torch.rand(B, H, D, generator=torch.Generator().manual_seed(N + 1)) * 5
@@ -76,14 +77,17 @@ def test_causal_many_blocks_with_state(B, H, N):
     assert row_rel_err(host(o2), ro) < TOL[dtype]
 
 
-@pytest.mark.parametrize("B,H,N,exact", [(1, 8, 4096, False), (2, 3, 3000, True), (1, 16, 2304, False)])
-def test_causal_lookback_slow_path(monkeypatch, B, H, N, exact):
+@pytest.mark.parametrize("dtype,B,H,N,exact", [(torch.bfloat16, 1, 8, 4096, False), (torch.bfloat16, 2, 3, 3000, True),
+                                               (torch.bfloat16, 1, 16, 2304, False), (torch.float32, 1, 8, 2000, True),
+                                               (torch.float32, 2, 3, 1500, False)],
+                         ids=["bf16-8h", "bf16-6h-state", "bf16-16h", "f32-8h-state", "f32-6h"])
+def test_causal_lookback_slow_path(monkeypatch, dtype, B, H, N, exact):
     """With a look-back wait bound of 0 every block whose predecessors have not
     published yet takes the slow path and computes their increments directly from
-    K and V; the results must still match the oracle (both variants, B*H a
-    multiple of 8 and not)."""
-    dtype, D, M = torch.bfloat16, 64, 64
-    say("causal look-back slow path", B, H, N, exact)
+    K and V; the results must still match the oracle (bf16 with and without the
+    state, float32, B*H a multiple of 8 and not)."""
+    D, M = 64, 64
+    say("causal look-back slow path", dtype, B, H, N, exact)
     monkeypatch.setenv("LINATTN_LOOKBACK_SPIN_TICKS", "0")
     q, k, v = synth.qkv(B, H, N, D, M, dtype=dtype, seed=N + H)
     S0 = torch.randn(B, H, D, M, generator=torch.Generator().manual_seed(N)) * 2
@@ -98,15 +102,15 @@ def test_causal_lookback_slow_path(monkeypatch, B, H, N, exact):
     assert row_rel_err(host(o), ro) < TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
 @pytest.mark.parametrize("D,M", [(32, 32), (32, 64), (64, 32), (64, 64)])
 @pytest.mark.parametrize("N", [1, 65, 1000, 2500])
-def test_causal_bf16_blocked_path(monkeypatch, D, M, N):
-    """LINATTN_CAUSAL_BF16_PATH=blocked sends bf16 calls through the three-kernel
+def test_causal_blocked_path(monkeypatch, dtype, D, M, N):
+    """LINATTN_CAUSAL_PATH=blocked sends causal calls through the three-kernel
     path (block states, block scan, chunked sweep): outputs, final state from an
     initial state, and outputs only, against the oracle."""
-    monkeypatch.setenv("LINATTN_CAUSAL_BF16_PATH", "blocked")
-    dtype = torch.bfloat16
-    say("causal bf16 blocked", D, M, N)
+    monkeypatch.setenv("LINATTN_CAUSAL_PATH", "blocked")
+    say("causal blocked", dtype, D, M, N)
     q, k, v = synth.qkv(2, 3, N, D, M, dtype=dtype, seed=N * 5 + D + 3 * M)
     S0 = torch.randn(2, 3, D, M, generator=torch.Generator().manual_seed(N)) * 2
     z0 = torch.rand(2, 3, D, generator=torch.Generator().manual_seed(N + 1)) * 4
@@ -119,15 +123,16 @@ def test_causal_bf16_blocked_path(monkeypatch, D, M, N):
     assert row_rel_err(host(la.causal(*gpu(q, k, v))), ro) < TOL[dtype]
 
 
-def test_causal_bf16_blocked_path_long_head(monkeypatch):
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_causal_blocked_path_long_head(monkeypatch, dtype):
     """The blocked path over many blocks of one head (its block scan), the long
     workload's head length."""
-    monkeypatch.setenv("LINATTN_CAUSAL_BF16_PATH", "blocked")
-    q, k, v = synth.qkv(1, 2, 32768, 64, 64, dtype=torch.bfloat16, scale=0.5, seed=77)
-    say("causal bf16 blocked long head")
+    monkeypatch.setenv("LINATTN_CAUSAL_PATH", "blocked")
+    q, k, v = synth.qkv(1, 2, 32768, 64, 64, dtype=dtype, scale=0.5, seed=77)
+    say("causal blocked long head", dtype)
     o = host(la.causal(*gpu(q, k, v)))
     ro, _, _ = oracle.causal(q, k, v)
-    assert row_rel_err(o, ro) < 2e-2
+    assert row_rel_err(o, ro) < (2e-2 if dtype == torch.bfloat16 else 1e-4)
 
 
 def test_causal_small_workload_all_rows_explicit():

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblinattn.so")
-SOURCES = ["abi.cpp", "causal.hip", "causal_fused.hip", "causal_bwd.hip", "causal_bwd_bf16.hip", "noncausal.hip", "decode.hip", "deltanet.hip", "deltanet_chunk.hip", "softmax_decode.hip", "featmap.hip", "scratch.hip"]
+SOURCES = ["abi.cpp", "causal.hip", "causal_fused.hip", "causal_fused32.hip", "causal_bwd.hip", "causal_bwd_bf16.hip", "noncausal.hip", "decode.hip", "deltanet.hip", "deltanet_chunk.hip", "softmax_decode.hip", "featmap.hip", "scratch.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else "hipcc")

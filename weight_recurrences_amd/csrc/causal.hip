@@ -825,17 +825,18 @@ hipError_t launch_state_copy(const float* S_init, const float* z_init, float* S_
   return hipGetLastError();
 }
 
-// bf16 causal calls take the single-pass kernel unless LINATTN_CAUSAL_BF16_PATH=blocked
-// selects the three-kernel path (kept for comparisons).  Read at every call, by
-// the workspace query and by the launch alike.
-static bool bf16_fused() {
-  const char* e = getenv("LINATTN_CAUSAL_BF16_PATH");
+// Causal calls take the single-pass kernels (causal_fused.hip for bf16,
+// causal_fused32.hip for float32) unless LINATTN_CAUSAL_PATH=blocked selects the
+// three-kernel path (kept for comparisons).  Read at every call, by the
+// workspace query and by the launch alike.
+static bool causal_fused_path() {
+  const char* e = getenv("LINATTN_CAUSAL_PATH");
   return !(e && strcmp(e, "blocked") == 0);
 }
 
 size_t causal_ws_bytes(int BH, int N, int D, int M, int bf16) {
   if (BH <= 0 || N <= 0) return 0;
-  if (bf16 && bf16_fused()) return causal_fused_ws_bytes(BH, N, D, M);
+  if (causal_fused_path()) return bf16 ? causal_fused_ws_bytes(BH, N, D, M) : causal_fused32_ws_bytes(BH, N, D, M);
   const int tblk = causal_block_tokens(BH, N);
   const long long nblk = (N + tblk - 1) / tblk;
   if (nblk <= 1) return 0;
@@ -860,8 +861,10 @@ hipError_t launch_causal(const void* q, const void* k, const void* v, void* o, i
     hipLaunchKernelGGL(state_copy_kernel, dim3(nb), dim3(NT), 0, stream, S0, z0, S_out, z_out, nS, nz);
     return hipGetLastError();
   }
-  if (bf16 && bf16_fused())
-    return launch_causal_fused(q, k, v, o, BH, N, D, M, S0, z0, S_out, z_out, ws, stream);
+  if (causal_fused_path()) {
+    if (bf16) return launch_causal_fused(q, k, v, o, BH, N, D, M, S0, z0, S_out, z_out, ws, stream);
+    return launch_causal_fused32(q, k, v, o, BH, N, D, M, S0, z0, S_out, z_out, ws, stream);
+  }
   if (bf16) {
     LA_DISPATCH_DM(causal_impl, bf16_t, q, k, v, o, BH, N, S0, z0, S_out, z_out, ws, stream)
   } else {

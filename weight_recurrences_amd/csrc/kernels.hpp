@@ -30,6 +30,11 @@ size_t causal_fused_ws_bytes(int BH, int N, int D, int M);
 hipError_t launch_causal_fused(const void* q, const void* k, const void* v, void* o, int BH, int N, int D, int M,
                                const float* S0, const float* z0, float* S_out, float* z_out, void* ws,
                                hipStream_t stream);
+// Single-pass float32 causal kernel (causal_fused32.hip).
+size_t causal_fused32_ws_bytes(int BH, int N, int D, int M);
+hipError_t launch_causal_fused32(const void* q, const void* k, const void* v, void* o, int BH, int N, int D, int M,
+                                 const float* S0, const float* z0, float* S_out, float* z_out, void* ws,
+                                 hipStream_t stream);
 hipError_t launch_noncausal(const void* q, const void* k, const void* v, void* o, int BH, int N, int D, int M,
                             int bf16, void* ws, hipStream_t stream);
 // bf16 non-causal path (state, reduce and apply kernels).
