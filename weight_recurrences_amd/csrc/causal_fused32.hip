@@ -157,6 +157,103 @@ __device__ __forceinline__ void chunk_update(Tiles<D, M>& acc, const Smem<D, M>&
   }
 }
 
+// A state (this wave's tiles of S, and z) as the S^T head/tail operand tiles
+// [M][D] and the z head/tail vectors.
+template <int D, int M>
+__device__ __forceinline__ void put_state(Smem<D, M>& sm, const Tiles<D, M>& t, int w, int n, int g, uint32_t l_wr) {
+  using GG = G<D, M>;
+#pragma unroll
+  for (int u = 0; u < GG::TMW; ++u) {
+    int tdd, tm;
+    tile_coords<D, M>(w, u, tdd, tm);
+    const f32x4& x = t.S[u];
+    const uint32_t h0 = cvt_pk(x[0], x[1]), h1 = cvt_pk(x[2], x[3]);
+    *reinterpret_cast<u32x2*>(tile_at<GG::UK>(sm.Sh, l_wr, 16 * tm, 16 * tdd)) = u32x2{h0, h1};
+    *reinterpret_cast<u32x2*>(tile_at<GG::UK>(sm.Sl, l_wr, 16 * tm, 16 * tdd)) =
+        u32x2{cvt_pk(x[0] - lo_of(h0), x[1] - hi_of(h0)), cvt_pk(x[2] - lo_of(h1), x[3] - hi_of(h1))};
+  }
+  if (w < GG::TD && n == 0) {
+    const uint32_t h0 = cvt_pk(t.Z[0], t.Z[1]), h1 = cvt_pk(t.Z[2], t.Z[3]);
+    *reinterpret_cast<u32x2*>(&sm.Zh[16 * w + 4 * g]) = u32x2{h0, h1};
+    *reinterpret_cast<u32x2*>(&sm.Zl[16 * w + 4 * g]) =
+        u32x2{cvt_pk(t.Z[0] - lo_of(h0), t.Z[1] - hi_of(h0)), cvt_pk(t.Z[2] - lo_of(h1), t.Z[3] - hi_of(h1))};
+  }
+}
+
+// num^T += S^T phi(Q)^T and den += z . phi(q) for this wave's 16 query columns,
+// from the operands written by put_state.
+template <int D, int M>
+__device__ __forceinline__ void state_read(f32x4 (&numT)[M / 16], f32x4& den, const Smem<D, M>& sm,
+                                           const bf16x8 (&qfh)[D / 32], const bf16x8 (&qfl)[D / 32], int g,
+                                           uint32_t l_rd) {
+  using GG = G<D, M>;
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s) {
+#pragma unroll
+    for (int tm = 0; tm < GG::TM; ++tm) {
+      const bf16x8 sh = as_bf16x8(*reinterpret_cast<const u32x4*>(tile_at<GG::UK>(sm.Sh, l_rd, 16 * tm, 32 * s)));
+      const bf16x8 sl = as_bf16x8(*reinterpret_cast<const u32x4*>(tile_at<GG::UK>(sm.Sl, l_rd, 16 * tm, 32 * s)));
+      numT[tm] = mma3(sh, sl, qfh[s], qfl[s], numT[tm]);
+    }
+    const bf16x8 zh = as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.Zh[32 * s + 8 * g]));
+    const bf16x8 zl = as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.Zl[32 * s + 8 * g]));
+    den = mma3(zh, zl, qfh[s], qfl[s], den);
+  }
+}
+
+// Within the chunk: num^T += V^T A^T and den += 1^T A^T with the masked scores
+// A^T[j][i] = phi(k_j).phi(q_i), j <= i, for this wave's queries i = 16 w + n.
+template <int D, int M>
+__device__ __forceinline__ void intra_chunk(f32x4 (&numT)[M / 16], f32x4& den, const Smem<D, M>& sm,
+                                            const bf16x8 (&qfh)[D / 32], const bf16x8 (&qfl)[D / 32], int w, int n,
+                                            int g, uint32_t l_rd, uint32_t l_trv) {
+  using GG = G<D, M>;
+  const bf16x8 ones = ones8();
+  f32x4 at[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    at[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (t <= w) {
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) {
+        const bf16x8 kah = as_bf16x8(*reinterpret_cast<const u32x4*>(tile_at<GG::UK>(sm.Kh, l_rd, 16 * t, 32 * s)));
+        const bf16x8 kal = as_bf16x8(*reinterpret_cast<const u32x4*>(tile_at<GG::UK>(sm.Kl, l_rd, 16 * t, 32 * s)));
+        at[t] = mma3(kah, kal, qfh[s], qfl[s], at[t]);
+      }
+      if (t == w) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (4 * g + r > n) at[t][r] = 0.f;
+      }
+    }
+  }
+  // A score tile pair is the B operand of a 32-key slab (lane (n, g) holds
+  // column i = n at the j-slots of group g).
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    if (2 * s <= w) {
+      u32x4 ph, pl;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const f32x4& a = at[2 * s + h];
+        ph[2 * h] = cvt_pk(a[0], a[1]);
+        ph[2 * h + 1] = cvt_pk(a[2], a[3]);
+        pl[2 * h] = cvt_pk(a[0] - lo_of(ph[2 * h]), a[1] - hi_of(ph[2 * h]));
+        pl[2 * h + 1] = cvt_pk(a[2] - lo_of(ph[2 * h + 1]), a[3] - hi_of(ph[2 * h + 1]));
+      }
+      const bf16x8 pfh = as_bf16x8(ph), pfl = as_bf16x8(pl);
+#pragma unroll
+      for (int tm = 0; tm < GG::TM; ++tm) {
+        const bf16x8 avh = jfrag_at<GG::UV>(sm.Vh, l_trv, 32 * s, 16 * tm);
+        const bf16x8 avl = jfrag_at<GG::UV>(sm.Vl, l_trv, 32 * s, 16 * tm);
+        numT[tm] = mma3(avh, avl, pfh, pfl, numT[tm]);
+      }
+      den = mma(ones, pfh, den);
+      den = mma(ones, pfl, den);
+    }
+  }
+}
+
 template <int D, int M, bool LOCAL>
 __global__ __launch_bounds__(NT, 2) void causal_fused32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v, float* __restrict__ o,
@@ -186,35 +283,7 @@ __global__ __launch_bounds__(NT, 2) void causal_fused32_kernel(
   const uint32_t l_rd = lane_off<UK>(n, 8 * g);
   const uint32_t l_wr = lane_off<UK>(n, 4 * g);
 
-  // ---------------- pass 1: the block increment ----------------
-  // All of the block's keys and values are loaded at once, chunk by chunk in
-  // order (ordinary loads, so that pass 2 finds the lines in the caches).
-  Tiles<D, M> L;
-  tiles_zero<D, M>(L);
-  RawKV<D, M> r1[NCH];
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    // Chunks past the end re-read the last row (nothing of them is used).
-    load_kv<D, M, false>(r1[c], kh, vh, t0 + min(c, nch - 1) * CH, ntok - min(c, nch - 1) * CH, tid);
-    __builtin_amdgcn_sched_barrier(0);  // keep the chunks' loads in order
-  }
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    if (c >= nch) break;
-    if (c > 0) __syncthreads();  // the previous chunk's tiles are read
-    stage_kv<D, M>(sm, r1[c], ntok - c * CH, tid, l_kst, l_vst);
-    __syncthreads();
-    chunk_update<D, M>(L, sm, w, l_trk_w, l_trv_w);
-  }
-  // Publish the increment.  (Block 0 publishes its increment too when it
-  // publishes no inclusive prefix.)
-  const bool agg0 = b == 0 && incl_period > 1 && nblk > 1;
-  if (b > 0 || agg0) agg_store<D, M, LOCAL, true>(agg_ws + ((size_t)bh * nblk + b) * GG::SLOT, L, w, lane, n, g);
-
-  // ---------------- phase 2: exclusive prefix of the block ----------------
   // Queries: this wave's rows 16 w + n of a chunk, d-slots 32 s + 8 g .. + 7.
-  RawKV<D, M> r2[NCH];
-  f32x4 rq[NCH][QV][2];
   auto load_q = [&](f32x4 (&dst)[QV][2], int c) {
     const int i = min(c * CH + 16 * w + n, ntok - 1);
 #pragma unroll
@@ -224,143 +293,118 @@ __global__ __launch_bounds__(NT, 2) void causal_fused32_kernel(
       dst[s][1] = __builtin_nontemporal_load(src + 1);
     }
   };
-  // The first chunk of pass 2 is loaded while the look-back waits.
-  Tiles<D, M> R;  // the running prefix of pass 2, from P
-  block_prefix<D, M, LOCAL, true, 4>(R, L, sm.status, kh, vh, N, TB, b, bh, nblk, S0, z0, S_out, z_out, flags, agg_ws,
-                                  incl_ws, epoch, spin_ticks, incl_period, agg0, xcc, tid, w, lane, n, g,
-                                  [&] {
-                                    if (o) {
-                                      load_kv<D, M, true>(r2[0], kh, vh, t0, ntok, tid);
-                                      load_q(rq[0], 0);
-                                      const int c1 = min(1, nch - 1);
-                                      load_kv<D, M, true>(r2[1], kh, vh, t0 + c1 * CH, ntok - c1 * CH, tid);
-                                      load_q(rq[1], c1);
-                                    }
-                                  });
-  if (!o) return;
-
-  // ---------------- pass 2: outputs, chunk by chunk ----------------
-  const bool have_p = b > 0 || S0 != nullptr;
-  float* ob = o + ((size_t)bh * N + t0) * M;
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    if (c >= nch) break;
-    // Every wave has finished reading the previous chunk's tiles (for c = 0,
-    // pass 1's last tiles: the look-back's barriers follow them when b > 0).
-    if (c > 0 || b == 0) __syncthreads();
-    stage_kv<D, M>(sm, r2[c], ntok - c * CH, tid, l_kst, l_vst);
-    // R_c^T as head and tail: each wave writes its tiles (rows m, columns d).
-    const bool have_r = have_p || c > 0;
-    if (have_r) {
-#pragma unroll
-      for (int u = 0; u < GG::TMW; ++u) {
-        int tdd, tm;
-        tile_coords<D, M>(w, u, tdd, tm);
-        const f32x4& x = R.S[u];
-        const uint32_t h0 = cvt_pk(x[0], x[1]), h1 = cvt_pk(x[2], x[3]);
-        *reinterpret_cast<u32x2*>(tile_at<UK>(sm.Sh, l_wr, 16 * tm, 16 * tdd)) = u32x2{h0, h1};
-        *reinterpret_cast<u32x2*>(tile_at<UK>(sm.Sl, l_wr, 16 * tm, 16 * tdd)) =
-            u32x2{cvt_pk(x[0] - lo_of(h0), x[1] - hi_of(h0)), cvt_pk(x[2] - lo_of(h1), x[3] - hi_of(h1))};
-      }
-      if (w < GG::TD && n == 0) {
-        const uint32_t h0 = cvt_pk(R.Z[0], R.Z[1]), h1 = cvt_pk(R.Z[2], R.Z[3]);
-        *reinterpret_cast<u32x2*>(&sm.Zh[16 * w + 4 * g]) = u32x2{h0, h1};
-        *reinterpret_cast<u32x2*>(&sm.Zl[16 * w + 4 * g]) = u32x2{cvt_pk(R.Z[0] - lo_of(h0), R.Z[1] - hi_of(h0)),
-                                                                 cvt_pk(R.Z[2] - lo_of(h1), R.Z[3] - hi_of(h1))};
-      }
-    }
-    // phi(Q_c) as head and tail.
-    bf16x8 qfh[QV], qfl[QV];
+  auto split_q = [&](const f32x4 (&r)[QV][2], bf16x8 (&qh_)[QV], bf16x8 (&ql_)[QV]) {
 #pragma unroll
     for (int s = 0; s < QV; ++s) {
       u32x4 hq, lq;
-      split8(phi4(rq[c][s][0]), phi4(rq[c][s][1]), hq, lq);
-      qfh[s] = as_bf16x8(hq);
-      qfl[s] = as_bf16x8(lq);
+      split8(phi4(r[s][0]), phi4(r[s][1]), hq, lq);
+      qh_[s] = as_bf16x8(hq);
+      ql_[s] = as_bf16x8(lq);
     }
-    if (c + 2 < NCH && c + 2 < nch) {
-      load_kv<D, M, true>(r2[c + 2], kh, vh, t0 + (c + 2) * CH, ntok - (c + 2) * CH, tid);
-      load_q(rq[c + 2], c + 2);
-    }
-    __syncthreads();
-
-    f32x4 numT[GG::TM];  // transposed: row m = 16 tm + 4 g + r, column i = 16 w + n
-#pragma unroll
-    for (int tm = 0; tm < GG::TM; ++tm) numT[tm] = f32x4{0.f, 0.f, 0.f, 0.f};
-    f32x4 den{0.f, 0.f, 0.f, 0.f};
-    const bf16x8 ones = ones8();
-    // Scores A^T[j][i] = phi(k_j).phi(q_i) for key tiles t <= w, masked on the diagonal.
-    f32x4 at[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      at[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (t <= w) {
-#pragma unroll
-        for (int s = 0; s < QV; ++s) {
-          const bf16x8 kah = as_bf16x8(*reinterpret_cast<const u32x4*>(tile_at<UK>((const bf16_t*)sm.Kh, l_rd, 16 * t, 32 * s)));
-          const bf16x8 kal = as_bf16x8(*reinterpret_cast<const u32x4*>(tile_at<UK>((const bf16_t*)sm.Kl, l_rd, 16 * t, 32 * s)));
-          at[t] = mma3(kah, kal, qfh[s], qfl[s], at[t]);
-        }
-        if (t == w) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (4 * g + r > n) at[t][r] = 0.f;
-        }
-      }
-    }
-    // num^T += V^T A^T, den += 1^T A^T: a score tile pair is the B operand of a
-    // 32-key slab (lane (n, g) holds column i = n at the j-slots of group g).
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      if (2 * s <= w) {
-        u32x4 ph, pl;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const f32x4& a = at[2 * s + h];
-          ph[2 * h] = cvt_pk(a[0], a[1]);
-          ph[2 * h + 1] = cvt_pk(a[2], a[3]);
-          pl[2 * h] = cvt_pk(a[0] - lo_of(ph[2 * h]), a[1] - hi_of(ph[2 * h]));
-          pl[2 * h + 1] = cvt_pk(a[2] - lo_of(ph[2 * h + 1]), a[3] - hi_of(ph[2 * h + 1]));
-        }
-        const bf16x8 pfh = as_bf16x8(ph), pfl = as_bf16x8(pl);
-#pragma unroll
-        for (int tm = 0; tm < GG::TM; ++tm) {
-          const bf16x8 avh = jfrag_at<UV>(sm.Vh, l_trv, 32 * s, 16 * tm);
-          const bf16x8 avl = jfrag_at<UV>(sm.Vl, l_trv, 32 * s, 16 * tm);
-          numT[tm] = mma3(avh, avl, pfh, pfl, numT[tm]);
-        }
-        den = mma(ones, pfh, den);
-        den = mma(ones, pfl, den);
-      }
-    }
-    // The prefix before the chunk: num^T += R_c^T phi(Q)^T, den += z . phi(q).
-    if (have_r) {
-#pragma unroll
-      for (int s = 0; s < QV; ++s) {
-#pragma unroll
-        for (int tm = 0; tm < GG::TM; ++tm) {
-          const bf16x8 sh = as_bf16x8(*reinterpret_cast<const u32x4*>(tile_at<UK>((const bf16_t*)sm.Sh, l_rd, 16 * tm, 32 * s)));
-          const bf16x8 sl = as_bf16x8(*reinterpret_cast<const u32x4*>(tile_at<UK>((const bf16_t*)sm.Sl, l_rd, 16 * tm, 32 * s)));
-          numT[tm] = mma3(sh, sl, qfh[s], qfl[s], numT[tm]);
-        }
-        const bf16x8 zh = as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.Zh[32 * s + 8 * g]));
-        const bf16x8 zl = as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.Zl[32 * s + 8 * g]));
-        den = mma3(zh, zl, qfh[s], qfl[s], den);
-      }
-    }
-    // R_{c+1} = R_c + dS_c (not needed after the last chunk).
-    if (c + 1 < nch) chunk_update<D, M>(R, sm, w, l_trk_w, l_trv_w);
-    // o_i = num_i / den_i for query i = 16 w + n: lane (n, g) holds the four
-    // consecutive columns 16 tm + 4 g .. + 3 of every m-tile, one 16-byte store each.
+  };
+  float* ob = o + ((size_t)bh * N + t0) * M;
+  // o_i = num_i / den_i for query i = 16 w + n of chunk c: lane (n, g) holds the
+  // four consecutive columns 16 tm + 4 g .. + 3 of every m-tile, one 16-byte
+  // store each.
+  auto store_out = [&](const f32x4 (&numT)[GG::TM], float den, int c) {
     const int i = c * CH + 16 * w + n;
     if (i < ntok) {
-      const float inv = 1.f / den[0];
+      const float inv = 1.f / den;
       float* dst = ob + (size_t)i * M + 4 * g;
 #pragma unroll
       for (int tm = 0; tm < GG::TM; ++tm)
         *reinterpret_cast<float4*>(dst + 16 * tm) =
             float4{numT[tm][0] * inv, numT[tm][1] * inv, numT[tm][2] * inv, numT[tm][3] * inv};
     }
+  };
+
+  // ---------------- pass 1: the block increment ----------------
+  // All of the block's keys and values are loaded at once (ordinary loads, so
+  // that pass 2 finds the lines in the caches), and the chunks are taken in
+  // the order 1, 2, .., then 0, so that chunk 0's tiles are still in LDS when
+  // the pass ends.  Load slots past the last chunk re-read it (unused).
+  auto chunk_at = [&](int i) { return i + 1 < nch ? i + 1 : 0; };
+  Tiles<D, M> L;
+  tiles_zero<D, M>(L);
+  RawKV<D, M> r1[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = i < nch ? chunk_at(i) : nch - 1;
+    load_kv<D, M, false>(r1[i], kh, vh, t0 + c * CH, ntok - c * CH, tid);
+    __builtin_amdgcn_sched_barrier(0);  // keep the chunks' loads in order
+  }
+  f32x4 rq0[QV][2];
+  if (o) load_q(rq0, 0);
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    if (i >= nch) break;
+    if (i > 0) __syncthreads();  // the previous chunk's tiles are read
+    stage_kv<D, M>(sm, r1[i], ntok - chunk_at(i) * CH, tid, l_kst, l_vst);
+    __syncthreads();
+    chunk_update<D, M>(L, sm, w, l_trk_w, l_trv_w);
+  }
+  // Publish the increment; its stores drain while chunk 0's outputs within the
+  // block are formed.  (Block 0 publishes its increment too when it publishes
+  // no inclusive prefix.)
+  const bool agg0 = b == 0 && incl_period > 1 && nblk > 1;
+  if (b > 0 || agg0) agg_store<D, M, LOCAL, true>(agg_ws + ((size_t)bh * nblk + b) * GG::SLOT, L, w, lane, n, g);
+  f32x4 numT0[GG::TM], den0{0.f, 0.f, 0.f, 0.f};
+  bf16x8 qh0[QV], ql0[QV];
+  if (o) {
+    split_q(rq0, qh0, ql0);
+#pragma unroll
+    for (int tm = 0; tm < GG::TM; ++tm) numT0[tm] = f32x4{0.f, 0.f, 0.f, 0.f};
+    intra_chunk<D, M>(numT0, den0, sm, qh0, ql0, w, n, g, l_rd, l_trv);
+  }
+
+  // ---------------- phase 2: exclusive prefix of the block ----------------
+  // Chunk 1 of pass 2 is loaded while the look-back waits.
+  RawKV<D, M> r2[NCH];
+  f32x4 rq[NCH][QV][2];
+  Tiles<D, M> R;  // the running prefix of pass 2, from P
+  block_prefix<D, M, LOCAL, true, 2>(R, L, sm.status, kh, vh, N, TB, b, bh, nblk, S0, z0, S_out, z_out, flags, agg_ws,
+                                     incl_ws, epoch, spin_ticks, incl_period, agg0, xcc, tid, w, lane, n, g, [&] {
+                                       if (o && nch > 1) {
+                                         load_kv<D, M, true>(r2[1], kh, vh, t0 + CH, ntok - CH, tid);
+                                         load_q(rq[1], 1);
+                                         const int c2 = min(2, nch - 1);
+                                         load_kv<D, M, true>(r2[2], kh, vh, t0 + c2 * CH, ntok - c2 * CH, tid);
+                                         load_q(rq[2], c2);
+                                       }
+                                     });
+  if (!o) return;
+
+  // ---------------- pass 2: outputs, chunk by chunk ----------------
+  const bool have_p = b > 0 || S0 != nullptr;
+  // Chunk 0: its tiles are still in LDS; add the prefix of earlier blocks.
+  if (have_p) {
+    put_state<D, M>(sm, R, w, n, g, l_wr);  // nothing has read the state tiles yet
+    __syncthreads();
+    state_read<D, M>(numT0, den0, sm, qh0, ql0, g, l_rd);
+  }
+  store_out(numT0, den0[0], 0);
+  if (nch > 1) chunk_update<D, M>(R, sm, w, l_trk_w, l_trv_w);  // R_1 = P + dS_0
+#pragma unroll
+  for (int c = 1; c < NCH; ++c) {
+    if (c >= nch) break;
+    __syncthreads();  // every wave has finished reading the previous chunk's tiles
+    stage_kv<D, M>(sm, r2[c], ntok - c * CH, tid, l_kst, l_vst);
+    put_state<D, M>(sm, R, w, n, g, l_wr);
+    bf16x8 qfh[QV], qfl[QV];
+    split_q(rq[c], qfh, qfl);
+    if (c + 2 < NCH && c + 2 < nch) {
+      load_kv<D, M, true>(r2[c + 2], kh, vh, t0 + (c + 2) * CH, ntok - (c + 2) * CH, tid);
+      load_q(rq[c + 2], c + 2);
+    }
+    __syncthreads();
+    f32x4 numT[GG::TM], den{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int tm = 0; tm < GG::TM; ++tm) numT[tm] = f32x4{0.f, 0.f, 0.f, 0.f};
+    intra_chunk<D, M>(numT, den, sm, qfh, qfl, w, n, g, l_rd, l_trv);
+    state_read<D, M>(numT, den, sm, qfh, qfl, g, l_rd);
+    // R_{c+1} = R_c + dS_c (not needed after the last chunk).
+    if (c + 1 < nch) chunk_update<D, M>(R, sm, w, l_trk_w, l_trv_w);
+    store_out(numT, den[0], c);
   }
 }
 

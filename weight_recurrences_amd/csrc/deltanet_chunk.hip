@@ -47,7 +47,6 @@ namespace dnc {
 
 constexpr int NT = 256;    // threads per workgroup (4 wavefronts)
 constexpr int C = 64;      // tokens per chunk
-constexpr int FS = C + 4;  // row stride (floats) of the fp32 C x C tiles in LDS
 
 // ---- bf16 head/tail operands ------------------------------------------------
 // Four floats -> {head01, head23, tail01, tail23} (round to nearest even).
