@@ -7,17 +7,19 @@
 // One workgroup owns a block of TB = 256 tokens (four chunks of 64) of one
 // (batch, head):
 //   pass 1   the block's increment dS = phi(K)^T V, dz = colsum phi(K), chunk by
-//            chunk, published for the later blocks of the head;
+//            chunk in the order 1, 2, 3, 0, published for the later blocks of
+//            the head; chunk 0's tiles are then still in LDS, and its outputs
+//            within the block are formed while the increment's stores drain;
 //   phase 2  decoupled look-back (lookback.hpp): the exclusive prefix P of the
 //            block from the published states of earlier blocks;
-//   pass 2   the outputs, chunk by chunk, from the running prefix R_c (P plus the
-//            chunks of the block before c): for query i of chunk c
+//   pass 2   the outputs from the running prefix R_c (P plus the chunks of the
+//            block before c): for query i of chunk c
 //              num_i = phi(q_i)^T R_c + sum_{j in c, j<=i} (phi(q_i).phi(k_j)) v_j,
-//              den_i likewise with z; o_i = num_i / den_i; then R_{c+1} = R_c + dS_c.
-// Pass 2 reads the block's keys and values a second time; pass 1 reads them
-// with ordinary loads, so the second reads are mostly served by the caches
-// (the Infinity Cache holds a launch's inputs at the sizes where the passes are
-// far apart).  Holding the partial outputs of four chunks across the look-back,
+//              den_i likewise with z; o_i = num_i / den_i; then R_{c+1} = R_c + dS_c
+//            (chunk 0 only adds phi(q_i)^T P to what pass 1 left).
+// Pass 2 reads chunks 1..3 of the block's keys and values a second time; pass 1
+// reads them with ordinary loads, so the second reads are mostly served by the
+// caches (the Infinity Cache holds them between the passes).  Holding the partial outputs of four chunks across the look-back,
 // as the bf16 kernel does, would take 128 more registers here (float32 operands
 // are a head and a tail), and 64-token blocks instead make the look-back fold
 // about ten float32 states per block.
