@@ -250,9 +250,10 @@ def test_state_carry_split_sequence(dtype):
         assert mat_rel_err(host(z1), rz, 1) < STATE_TOL[dtype]
 
 
-def test_state_only_and_empty_sequences():
-    say("state-only / empty")
-    q, k, v = synth.qkv(3, 2, 777, 32, 64, dtype=torch.bfloat16, seed=5)
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_state_only_and_empty_sequences(dtype):
+    say("state-only / empty", dtype)
+    q, k, v = synth.qkv(3, 2, 777, 32, 64, dtype=dtype, seed=5)
     S0 = torch.randn(3, 2, 32, 64, dtype=torch.float64)
     z0 = torch.rand(3, 2, 32, dtype=torch.float64) * 10
     S0f, z0f = S0.float(), z0.float()
@@ -260,8 +261,8 @@ def test_state_only_and_empty_sequences():
     _, rS, rz = oracle.causal(q, k, v, S0=S0f, z0=z0f, want_output=False)
     assert mat_rel_err(host(S), rS) < 1e-4 and mat_rel_err(host(z), rz, 1) < 1e-4
     # N = 0: the final state is the initial state
-    e = torch.empty(3, 2, 0, 32, dtype=torch.bfloat16, device=DEV)
-    ev = torch.empty(3, 2, 0, 64, dtype=torch.bfloat16, device=DEV)
+    e = torch.empty(3, 2, 0, 32, dtype=dtype, device=DEV)
+    ev = torch.empty(3, 2, 0, 64, dtype=dtype, device=DEV)
     o, (S, z) = la.causal(e, e, ev, state=(S0f.to(DEV), z0f.to(DEV)), return_state=True)
     assert o.shape == (3, 2, 0, 64)
     assert torch.equal(host(S), S0f) and torch.equal(host(z), z0f)
