@@ -73,7 +73,8 @@ __device__ __forceinline__ void fetch(u32x4 (&r)[NU], const bf16_t* src, int nt,
 #pragma unroll
   for (int i = 0; i < NU; ++i) {
     const int p = tid + NT * i, row = p / U, cu = p % U;
-    r[i] = row < nt ? *reinterpret_cast<const u32x4*>(src + (size_t)row * W + cu * 8) : u32x4{0u, 0u, 0u, 0u};
+    r[i] = row < nt ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (size_t)row * W + cu * 8))
+                    : u32x4{0u, 0u, 0u, 0u};
   }
 }
 

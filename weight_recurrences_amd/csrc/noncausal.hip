@@ -74,13 +74,13 @@ __global__ __launch_bounds__(NT) void nc_state_kernel(const bf16_t* __restrict__
 #pragma unroll
     for (int i = 0; i < GG::KV; ++i) {
       const int p = tid + NT * i, row = c * CH + p / GG::UK, cu = p % GG::UK;
-      dk[i] = (p < CH * GG::UK && row < ntok) ? *reinterpret_cast<const u32x4*>(kh + (size_t)row * D + cu * 8)
+      dk[i] = (p < CH * GG::UK && row < ntok) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kh + (size_t)row * D + cu * 8))
                                                : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int i = 0; i < GG::VV; ++i) {
       const int p = tid + NT * i, row = c * CH + p / GG::UV, cu = p % GG::UV;
-      dv[i] = (p < CH * GG::UV && row < ntok) ? *reinterpret_cast<const u32x4*>(vh + (size_t)row * M + cu * 8)
+      dv[i] = (p < CH * GG::UV && row < ntok) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vh + (size_t)row * M + cu * 8))
                                                : u32x4{0u, 0u, 0u, 0u};
     }
   };
@@ -199,7 +199,7 @@ __global__ __launch_bounds__(NT) void nc_apply_kernel(const bf16_t* __restrict__
     const int row = CH * c + 16 * w + n;
 #pragma unroll
     for (int s = 0; s < GG::QV; ++s)
-      dq[s] = row < ntok ? *reinterpret_cast<const u32x4*>(qh + (size_t)row * D + 32 * s + 8 * g)
+      dq[s] = row < ntok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qh + (size_t)row * D + 32 * s + 8 * g))
                          : u32x4{0u, 0u, 0u, 0u};
   };
 #pragma unroll
