@@ -35,6 +35,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "lds_tiles.hpp"
 
 namespace la {
 namespace fm {
@@ -117,17 +118,33 @@ __device__ __forceinline__ void load_rows(float* dst, const T* src, int nv, int 
   }
 }
 
+// Eight floats as a bf16 head and tail (x = h + l to about 2^-17 relative).
+__device__ __forceinline__ void split_bf16x8(const float (&x)[8], bf16x8& h, bf16x8& l) {
+  u32x4 hv, lv;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    hv[i] = cvt_pk(x[2 * i], x[2 * i + 1]);
+    lv[i] = cvt_pk(x[2 * i] - lo_of(hv[i]), x[2 * i + 1] - hi_of(hv[i]));
+  }
+  h = as_bf16x8(hv);
+  l = as_bf16x8(lv);
+}
+
 // ---- 1. block state increments ---------------------------------------------
 // grid: BH * nblk * (NS / SG), blockIdx.x = (bh * nblk + blk) * (NS / SG) + sg;
 // the workgroup covers slices sg*SG .. sg*SG + SG - 1 of one block, so the
 // block's keys and values are read once for SG slices.
 // agg [BH * NS][nblk][FS][M], aggz [BH * NS][nblk][FS].
 // Tile: rows = the 16 features 16w.. of the slice, columns = values, k-slot =
-// token; features are formed from the raw key rows as the operand is read, and
-// the lane's operands also give its share of z (tokens 4t + g).
+// token (bf16 16x16x32 MFMA on head/tail operands); features are formed from
+// the raw key rows as the operand is read, and the lane's operands also give
+// its share of z.
+// The largest divisor of NS up to 4: more slices per workgroup read the rows
+// fewer times but hold more accumulators (the polynomial map, 40 slices: 888 us
+// per call with groups of 8, 814 with 4, 901 with 2).
 template <int NS>
-constexpr int slice_group() {  // the largest divisor of NS up to 8
-  int g = NS < 8 ? NS : 8;
+constexpr int slice_group() {
+  int g = NS < 4 ? NS : 4;
   while (NS % g) --g;
   return g;
 }
@@ -171,23 +188,43 @@ __global__ __launch_bounds__(NT) void fm_state_kernel(const T* __restrict__ k, c
     load_rows<T, D, KS>(Kr, kh + (size_t)c0 * D, nv, tid);
     load_rows<T, M, VS>(Vs, vh + (size_t)c0 * M, nv, tid);
     __syncthreads();
-#pragma unroll 2
-    for (int t = 0; t < CH / 4; ++t) {
-      const float* kr = Kr + (4 * t + g) * KS;
-      float bv[TM];
+    // 32-token slabs on bf16 MFMA with head/tail operands (a b = ah bh + ah bl +
+    // al bh, float32 accumulation): k-slot 8g + e of slab s is token 32 s + 4 e + g,
+    // so that the four lane groups read four consecutive rows (distinct banks).
 #pragma unroll
-      for (int vb = 0; vb < TM; ++vb) bv[vb] = Vs[(4 * t + g) * VS + 16 * vb + n];
+    for (int s = 0; s < CH / 32; ++s) {
+      bf16x8 bvh[TM], bvl[TM];
+#pragma unroll
+      for (int vb = 0; vb < TM; ++vb) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = Vs[(32 * s + 4 * e + g) * VS + 16 * vb + n];
+        split_bf16x8(x, bvh[vb], bvl[vb]);
+      }
 #pragma unroll
       for (int j = 0; j < SG; ++j) {
-        float a;
-        if constexpr (FM == POLY2) {
-          a = pw[j] * kr[pa[j]] * kr[pb[j]];
-        } else {
-          a = feature<FM, D>(kr, (sg * SG + j) * FS + 16 * w + n);
-        }
-        zp[j] += a;
+        float a[8];
 #pragma unroll
-        for (int vb = 0; vb < TM; ++vb) acc[j][vb] = mma(a, bv[vb], acc[j][vb]);
+        for (int e = 0; e < 8; ++e) {
+          const float* kr = Kr + (32 * s + 4 * e + g) * KS;
+          if constexpr (FM == POLY2) {
+            a[e] = pw[j] * kr[pa[j]] * kr[pb[j]];
+          } else {
+            a[e] = feature<FM, D>(kr, (sg * SG + j) * FS + 16 * w + n);
+          }
+          zp[j] += a[e];
+        }
+        bf16x8 ah, al;
+        split_bf16x8(a, ah, al);
+#pragma unroll
+        for (int vb = 0; vb < TM; ++vb) {
+          acc[j][vb] = mma(ah, bvh[vb], acc[j][vb]);
+          acc[j][vb] = mma(ah, bvl[vb], acc[j][vb]);
+          acc[j][vb] = mma(al, bvh[vb], acc[j][vb]);
+        }
+        // One slice at a time: the features of later slices are not formed early
+        // (which would keep them all live).
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
