@@ -80,20 +80,6 @@ __device__ __forceinline__ float feature(const float* x, int c) {
   return ri * rj;
 }
 
-// DPFP feature c = s FS + 4t + g of a raw row x (D floats), with the slice's
-// terms hoisted: base = (s FS) mod 2D and gn = g + n, n the order the slice
-// belongs to.  Then i = base + 4t + g and j = i + n (mod 2D); r_i is relu(x) on
-// the first half of r and relu(-x) on the second, so the half is bit D of the
-// index and the component is the index mod D.
-template <int D>
-__device__ __forceinline__ float dpfp_feat(const float* x, int t, int base_g, int base_gn) {
-  const int i = base_g + 4 * t, e = base_gn + 4 * t;
-  const float xi = x[i & (D - 1)], xj = x[e & (D - 1)];
-  const float ri = fmaxf((i & D) ? -xi : xi, 0.f);
-  const float rj = fmaxf((e & D) ? -xj : xj, 0.f);
-  return ri * rj;
-}
-
 // Rows [0, nv) of a row-major [.][W] tensor starting at src, widened to float
 // into LDS (row stride DS floats); rows nv..63 become zeros.  The loads carry
 // no condition (rows past nv re-read row nv - 1 and are replaced by zeros): a
@@ -252,17 +238,21 @@ struct OutSmem {
   float Kr[CH * XS];  // raw keys of the current key chunk
   union {             // the state slices during the slice loop, the values after it
     float Vs[CH * VS];
-    float Ss[FS * M];  // prefix state slice S_s, rows of M floats, swizzled by ss_col
+    struct {
+      bf16_t Sh[FS * M];  // prefix state slice S_s [FS][M] as a bf16 head and tail, row-major swizzled
+      bf16_t Sl[FS * M];
+    } st;
   };
   float zs[FS];  // prefix z slice
 };
 
-// Column of element (f, c) of a state slice in LDS: the 16-float groups are XORed
-// by row so that the four rows a k-slot group g reads (4t + g) fall in four
-// different bank groups (M = 64: by f mod 4; M = 32: by bit 1 of f).
-template <int M>
-__device__ __forceinline__ int ss_col(int f, int c) {
-  return M == 64 ? c ^ ((f & 3) << 4) : c ^ (((f >> 1) & 1) << 4);
+// DPFP feature of a raw row x (D floats) at the indices i and j of r = (relu(x),
+// relu(-x)): r_i r_j (the half of r is bit D of the index, the component the
+// index mod D).
+template <int D>
+__device__ __forceinline__ float dpfp_pair(const float* x, int i, int j) {
+  const float xi = x[i & (D - 1)], xj = x[j & (D - 1)];
+  return fmaxf((i & D) ? -xi : xi, 0.f) * fmaxf((j & D) ? -xj : xj, 0.f);
 }
 
 // grid: BH * nqc, blockIdx.x = bh * nqc + qc (nqc = ceil(N / 64) query chunks).
@@ -331,7 +321,11 @@ __global__ __launch_bounds__(NT) void fm_out_kernel(const T* __restrict__ q, con
 #pragma unroll
       for (int u = 0; u < PF; ++u) {
         const int e = (u * NT + tid) * 4, f = e / M, c = e % M;
-        *reinterpret_cast<f32x4*>(&sm.Ss[f * M + ss_col<M>(f, c)]) = pf[u];
+        const f32x4 x = pf[u];
+        const uint32_t h0 = cvt_pk(x[0], x[1]), h1 = cvt_pk(x[2], x[3]);
+        unit8<M / 8>(sm.st.Sh, f, c) = u32x2{h0, h1};
+        unit8<M / 8>(sm.st.Sl, f, c) =
+            u32x2{cvt_pk(x[0] - lo_of(h0), x[1] - hi_of(h0)), cvt_pk(x[2] - lo_of(h1), x[3] - hi_of(h1))};
       }
       if (tid < FS) sm.zs[tid] = pz;
       {  // next slice in flight during this one (the last slice re-reads itself; unconditional loads, as in load_rows)
@@ -343,10 +337,12 @@ __global__ __launch_bounds__(NT) void fm_out_kernel(const T* __restrict__ q, con
       }
       __syncthreads();
       // Inter-block part: num^T += S_s^T phi_s(Q)^T, den += phi_s(Q) z_s; for DPFP
-      // also the slice's share of the chunk's scores.
+      // also the slice's share of the chunk's scores.  bf16 16x16x32 MFMA on head/
+      // tail operands over 32-feature slabs: k-slot e = 4h + r of lane group g is
+      // feature 32 s2 + 16 h + 4 g + r, the order in which the transposed reads of
+      // the state rows deliver them.
       const int base = (s * FS) & (2 * D - 1), order = (s * FS) / (2 * D) + 1;
-      const int base_g = base + g, base_gn = base + g + order;
-      float pqa[4];  // polynomial: q_a of the slice's four groups, and their first b
+      float pqa[4];  // polynomial: q_a of the slice's four groups, and their b offset 16 h
       int pb0[4];
       if constexpr (FM == POLY2) {
 #pragma unroll
@@ -354,25 +350,50 @@ __global__ __launch_bounds__(NT) void fm_out_kernel(const T* __restrict__ q, con
           int a, h;
           p2_group(4 * s + tg, a, h);
           pqa[tg] = qrow[a];
-          pb0[tg] = 16 * h + g;
+          pb0[tg] = 16 * h;
         }
       }
-#pragma unroll 4
-      for (int t = 0; t < FS / 4; ++t) {
-        float b;
-        if constexpr (FM == POLY2) {
-          b = pqa[t >> 2] * qrow[pb0[t >> 2] + 4 * (t & 3)];
-        } else {
-          b = dpfp_feat<D>(qrow, t, base_g, base_gn);
-        }
-        den += b * sm.zs[4 * t + g];
 #pragma unroll
-        for (int vb = 0; vb < TM; ++vb)
-          num[vb] = mma(sm.Ss[(4 * t + g) * M + ss_col<M>(4 * t + g, 16 * vb + n)], b, num[vb]);
+      for (int s2 = 0; s2 < FS / 32; ++s2) {
+        float qv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int f = 32 * s2 + 16 * (e >> 2) + 4 * g + (e & 3);
+          if constexpr (FM == POLY2) {
+            qv[e] = pqa[f >> 4] * qrow[pb0[f >> 4] + (f & 15)];
+          } else {
+            qv[e] = dpfp_pair<D>(qrow, base + f, base + order + f);
+          }
+          den += qv[e] * sm.zs[f];
+        }
+        bf16x8 qh8, ql8;
+        split_bf16x8(qv, qh8, ql8);
+#pragma unroll
+        for (int vb = 0; vb < TM; ++vb) {
+          const bf16x8 ah = jfrag<M / 8>(sm.st.Sh, 32 * s2, 16 * vb, g, n);
+          const bf16x8 al = jfrag<M / 8>(sm.st.Sl, 32 * s2, 16 * vb, g, n);
+          num[vb] = mma(ah, qh8, num[vb]);
+          num[vb] = mma(ah, ql8, num[vb]);
+          num[vb] = mma(al, qh8, num[vb]);
+        }
         if (intra_dpfp) {
 #pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
-            if (kb <= W) at[kb] = mma(dpfp_feat<D>(sm.Kr + (16 * kb + n) * XS, t, base_g, base_gn), b, at[kb]);
+          for (int kb = 0; kb < 4; ++kb) {
+            if (kb <= W) {
+              const float* krow = sm.Kr + (16 * kb + n) * XS;
+              float kv[8];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const int f = 32 * s2 + 16 * (e >> 2) + 4 * g + (e & 3);
+                kv[e] = dpfp_pair<D>(krow, base + f, base + order + f);
+              }
+              bf16x8 kh8, kl8;
+              split_bf16x8(kv, kh8, kl8);
+              at[kb] = mma(kh8, qh8, at[kb]);
+              at[kb] = mma(kh8, ql8, at[kb]);
+              at[kb] = mma(kl8, qh8, at[kb]);
+            }
+          }
         }
       }
     }
