@@ -41,6 +41,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector / matrix, TFLOP/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "causal linear-attn B·H·N tokens/s at N=32k, D=64; % of HBM/MFMA roofline"
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
@@ -607,12 +608,18 @@ def main():
         flops = fl(c_min)
         tfl = lambda c: fl(c) / (launch_ms / 1e3) / 1e12
         tflops = tfl(c_min)
+        bf16_tflops = 3 * units * 4 * c_exec * w.M / (launch_ms / 1e3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(tflops, 3), "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(tflops / FP32_PEAK_TFLOPS, 4), "traffic": traffic, "kernel": kernel,
                     "algorithmic_flops_per_launch": flops, "feature_dim": c_min, "launch_ms": round(launch_ms, 5),
                     "feature_dims": {"minimal_exact": c_min, "executed": c_exec, "defined": C},
                     "frac_executed": round(tfl(c_exec) / FP32_PEAK_TFLOPS, 4),
                     "frac_defined": round(tfl(C) / FP32_PEAK_TFLOPS, 4),
+                    # The state and output products run as three bf16 MFMAs each
+                    # (head x head, head x tail, tail x head) over the executed
+                    # features: the matrix units' own measure of the same launch.
+                    "bf16_mfma": {"executed_tflops": round(bf16_tflops, 3), "peak": BF16_PEAK_TFLOPS,
+                                  "frac": round(bf16_tflops / BF16_PEAK_TFLOPS, 4)},
                     "hbm": {"achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                             "frac": round(achieved / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": alg_bytes}}
     if args.workload == "deltanet":
