@@ -29,8 +29,12 @@
 //      DPFP: the block is the chunk (tblk = 64) and sim is summed slice by slice
 //      from the features.  POLY2: sim = (q.k)^2 from a D-long dot product, so
 //      blocks hold several chunks and fewer prefix states are written.
-// Products run on fp32 MFMA (v_mfma_f32_16x16x4_f32) with fp32 features; bf16
-// inputs are widened on load and outputs are rounded to the input dtype.
+// Features are formed in fp32 (bf16 inputs are widened on load; outputs are
+// rounded to the input dtype).  The state and output products, and DPFP's
+// scores, take them as a bf16 head and tail on 16x16x32 bf16 MFMA
+// (a.b = ah.bh + ah.bl + al.bh, fp32 accumulation, operands kept to about
+// 2^-17 relative); the value products of the scores and the polynomial map's
+// (q.k)^2 run on fp32 MFMA (v_mfma_f32_16x16x4_f32).
 #include <type_traits>
 
 #include "common.hpp"
