@@ -89,6 +89,23 @@ __device__ __forceinline__ float feature(const float* x, int c) {
 // no condition (rows past nv re-read row nv - 1 and are replaced by zeros): a
 // conditional load becomes a branch at which the compiler waits for every load
 // in flight, which would turn the loads into one round trip each.
+template <typename T, int W>
+__device__ __forceinline__ void fetch_rows(float4 (&x)[CH * W / 4 / NT], const T* src, int nv, int tid) {
+#pragma unroll
+  for (int u = 0; u < CH * W / 4 / NT; ++u) {
+    const int e = (u * NT + tid) * 4, r = e / W, c = e % W;
+    x[u] = load4<T>(src + (size_t)min(r, nv - 1) * W + c);
+  }
+}
+template <int W, int DS>
+__device__ __forceinline__ void put_rows(float* dst, const float4 (&x)[CH * W / 4 / NT], int nv, int tid) {
+#pragma unroll
+  for (int u = 0; u < CH * W / 4 / NT; ++u) {
+    const int e = (u * NT + tid) * 4, r = e / W, c = e % W;
+    *reinterpret_cast<float4*>(dst + r * DS + c) = r < nv ? x[u] : float4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
 template <typename T, int W, int DS>
 __device__ __forceinline__ void load_rows(float* dst, const T* src, int nv, int tid) {
   constexpr int G = CH * W / 4;  // groups of four elements
@@ -235,7 +252,7 @@ __global__ __launch_bounds__(NT) void fm_state_kernel(const T* __restrict__ k, c
 }
 
 // ---- 3. outputs --------------------------------------------------------------
-template <int D, int M>
+template <int D, int M, bool KF>
 struct OutSmem {
   static constexpr int XS = D + 4, VS = M + 4;
   float Qr[CH * XS];  // raw queries of the chunk
@@ -245,6 +262,8 @@ struct OutSmem {
     struct {
       bf16_t Sh[FS * M];  // prefix state slice S_s [FS][M] as a bf16 head and tail, row-major swizzled
       bf16_t Sl[FS * M];
+      bf16_t Kh[KF ? CH * FS : 8];  // DPFP: the slice's key features [key][FS], head and tail, swizzled
+      bf16_t Kl[KF ? CH * FS : 8];
     } st;
   };
   float zs[FS];  // prefix z slice
@@ -270,7 +289,7 @@ __global__ __launch_bounds__(NT) void fm_out_kernel(const T* __restrict__ q, con
                                                     const T* __restrict__ v, T* __restrict__ o, int N, int tblk,
                                                     int nblk, const float* __restrict__ pre,
                                                     const float* __restrict__ prez, int causal, int BHN) {
-  using SM = OutSmem<D, M>;
+  using SM = OutSmem<D, M, FM != POLY2>;
   constexpr int NS = fdim<FM, D>() / FS, TM = M / 16;
   constexpr int XS = SM::XS, VS = SM::VS;
   constexpr int PF = FS * M / 4 / NT;  // float4 groups of a state slice per thread
@@ -307,6 +326,8 @@ __global__ __launch_bounds__(NT) void fm_out_kernel(const T* __restrict__ q, con
   float pz = zb[min(tid, FS - 1)];  // lanes tid >= FS never store theirs
   load_rows<T, D, XS>(sm.Qr, qh + (size_t)q0 * D, nq, tid);
   if (intra_dpfp) load_rows<T, D, XS>(sm.Kr, kh + (size_t)q0 * D, nq, tid);  // the block is this chunk
+  float4 vpre[CH * M / 4 / NT];
+  if constexpr (FM != POLY2) fetch_rows<T, M>(vpre, vh + (size_t)q0 * M, intra_dpfp ? nq : 1, tid);
   f32x4 num[TM];  // num^T tiles: lane (n, g) holds values 16 vb + 4g + i of query 16w + n
 #pragma unroll
   for (int vb = 0; vb < TM; ++vb) num[vb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -332,6 +353,21 @@ __global__ __launch_bounds__(NT) void fm_out_kernel(const T* __restrict__ q, con
             u32x2{cvt_pk(x[0] - lo_of(h0), x[1] - hi_of(h0)), cvt_pk(x[2] - lo_of(h1), x[3] - hi_of(h1))};
       }
       if (tid < FS) sm.zs[tid] = pz;
+      const int base = (s * FS) & (2 * D - 1), order = (s * FS) / (2 * D) + 1;
+      if (FM != POLY2 && intra_dpfp) {  // the slice's features of the chunk's keys, formed once for all waves
+        const int r = tid >> 2, f0 = 16 * (tid & 3);
+        const float* krow = sm.Kr + r * XS;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          float kv[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) kv[e] = dpfp_pair<D>(krow, base + f0 + 8 * hf + e, base + order + f0 + 8 * hf + e);
+          bf16x8 kh8, kl8;
+          split_bf16x8(kv, kh8, kl8);
+          unit16<FS / 8>(sm.st.Kh, r, f0 + 8 * hf) = __builtin_bit_cast(u32x4, kh8);
+          unit16<FS / 8>(sm.st.Kl, r, f0 + 8 * hf) = __builtin_bit_cast(u32x4, kl8);
+        }
+      }
       {  // next slice in flight during this one (the last slice re-reads itself; unconditional loads, as in load_rows)
         const int sn = min(s + 1, NS - 1);
 #pragma unroll
@@ -345,7 +381,6 @@ __global__ __launch_bounds__(NT) void fm_out_kernel(const T* __restrict__ q, con
       // tail operands over 32-feature slabs: k-slot e = 4h + r of lane group g is
       // feature 32 s2 + 16 h + 4 g + r, the order in which the transposed reads of
       // the state rows deliver them.
-      const int base = (s * FS) & (2 * D - 1), order = (s * FS) / (2 * D) + 1;
       float pqa[4];  // polynomial: q_a of the slice's four groups, and their b offset 16 h
       int pb0[4];
       if constexpr (FM == POLY2) {
@@ -383,16 +418,13 @@ __global__ __launch_bounds__(NT) void fm_out_kernel(const T* __restrict__ q, con
         if (intra_dpfp) {
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb) {
-            if (kb <= W) {
-              const float* krow = sm.Kr + (16 * kb + n) * XS;
-              float kv[8];
-#pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                const int f = 32 * s2 + 16 * (e >> 2) + 4 * g + (e & 3);
-                kv[e] = dpfp_pair<D>(krow, base + f, base + order + f);
-              }
-              bf16x8 kh8, kl8;
-              split_bf16x8(kv, kh8, kl8);
+            if (kb <= W) {  // key rows 16 kb + n at the k-slots of the query features
+              const u32x2 h0 = unit8<FS / 8>(sm.st.Kh, 16 * kb + n, 32 * s2 + 4 * g);
+              const u32x2 h1 = unit8<FS / 8>(sm.st.Kh, 16 * kb + n, 32 * s2 + 16 + 4 * g);
+              const u32x2 l0 = unit8<FS / 8>(sm.st.Kl, 16 * kb + n, 32 * s2 + 4 * g);
+              const u32x2 l1 = unit8<FS / 8>(sm.st.Kl, 16 * kb + n, 32 * s2 + 16 + 4 * g);
+              const bf16x8 kh8 = as_bf16x8(u32x4{h0[0], h0[1], h1[0], h1[1]});
+              const bf16x8 kl8 = as_bf16x8(u32x4{l0[0], l0[1], l1[0], l1[1]});
               at[kb] = mma(kh8, qh8, at[kb]);
               at[kb] = mma(kh8, ql8, at[kb]);
               at[kb] = mma(kl8, qh8, at[kb]);
@@ -405,7 +437,7 @@ __global__ __launch_bounds__(NT) void fm_out_kernel(const T* __restrict__ q, con
     if (intra_dpfp) {
       // The values replace the state slices in LDS.
       __syncthreads();
-      load_rows<T, M, VS>(sm.Vs, vh + (size_t)q0 * M, nq, tid);
+      put_rows<M, VS>(sm.Vs, vpre, nq, tid);
       __syncthreads();
       // Keys after the query are masked; num^T += V^T A^T, den += column sums of A^T.
 #pragma unroll
