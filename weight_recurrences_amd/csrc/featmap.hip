@@ -471,25 +471,42 @@ __global__ __launch_bounds__(NT) void fm_out_kernel(const T* __restrict__ q, con
   if constexpr (FM == POLY2) {
     // Intra-block part: sim = (q.k)^2 for the block's keys up to this chunk.
     if (causal) {
+      // Each key chunk's rows are fetched into registers while the previous one
+      // is scored (the last chunk re-reads itself: unconditional loads).
+      float4 kpf[CH * D / 4 / NT], vpf[CH * M / 4 / NT];
+      fetch_rows<T, D>(kpf, kh + (size_t)blk * tblk * D, min(CH, N - blk * tblk), tid);
+      fetch_rows<T, M>(vpf, vh + (size_t)blk * tblk * M, min(CH, N - blk * tblk), tid);
       for (int kc0 = blk * tblk; kc0 <= q0; kc0 += CH) {
         const int nk = min(CH, N - kc0);
         __syncthreads();  // the previous key chunk's readers are done
-        load_rows<T, D, XS>(sm.Kr, kh + (size_t)kc0 * D, nk, tid);
-        load_rows<T, M, VS>(sm.Vs, vh + (size_t)kc0 * M, nk, tid);
+        put_rows<D, XS>(sm.Kr, kpf, nk, tid);
+        put_rows<M, VS>(sm.Vs, vpf, nk, tid);
         __syncthreads();
+        {
+          const int kn = min(kc0 + CH, q0);
+          fetch_rows<T, D>(kpf, kh + (size_t)kn * D, min(CH, N - kn), tid);
+          fetch_rows<T, M>(vpf, vh + (size_t)kn * M, min(CH, N - kn), tid);
+        }
+        // The four key tiles' scores run as four interleaved chains; on the
+        // diagonal chunk the tiles past the wave's queries are masked to zero
+        // (no branch around the products).
         const bool diag = kc0 == q0;
-        const int kbmax = diag ? w : 3;
-        for (int kb = 0; kb <= kbmax; ++kb) {
-          f32x4 a{0.f, 0.f, 0.f, 0.f};
+        f32x4 a4[4];
 #pragma unroll
-          for (int t = 0; t < D / 4; ++t)
-            a = mma(sm.Kr[(16 * kb + n) * XS + 4 * t + g], qrow[4 * t + g], a);
+        for (int kb = 0; kb < 4; ++kb) a4[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) a[i] *= a[i];
-          if (diag && kb == w) {
+        for (int t = 0; t < D / 4; ++t) {
+          const float qx = qrow[4 * t + g];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (4 * g + i > n) a[i] = 0.f;
+          for (int kb = 0; kb < 4; ++kb) a4[kb] = mma(sm.Kr[(16 * kb + n) * XS + 4 * t + g], qx, a4[kb]);
+        }
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          f32x4 a = a4[kb];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            a[i] *= a[i];
+            if (diag && (kb > w || (kb == w && 4 * g + i > n))) a[i] = 0.f;
           }
           den += a[0] + a[1] + a[2] + a[3];
 #pragma unroll
