@@ -656,6 +656,13 @@ def main():
     dtype = {"causal_long": "bf16", "causal_bwd_long": "bf16", "noncausal_long": "bf16", "decode": "bf16", "causal_mid": "f32", "causal_small": "f32",
              "deltanet": "f32", "deltanet_decode": "bf16", "softmax_decode": "bf16",
              **{f: "f32" for f in FMAPS}}[args.workload]
+    if traffic is not None:
+        # The HBM bytes the counters measured, moved in the measured launch time:
+        # how close the path runs to the memory system on the bytes it really
+        # moves (against `achieved`, which counts only the algorithmic ones).
+        tr = traffic / (launch_ms / 1e3) / 1e9
+        roofline["traffic_rate"] = {"achieved": round(tr, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                    "frac": round(tr / HBM_PEAK_GBS, 4)}
     line = {
         "metric": METRIC if args.workload == "causal_long" else f"{args.workload} {unit}",
         "value": value, "unit": unit, "n_gpus": 1, "steps": K, "warmup": Wm,
