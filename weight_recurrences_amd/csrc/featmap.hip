@@ -269,33 +269,23 @@ struct OutSmem {
   float zs[FS];  // prefix z slice
 };
 
-// DPFP feature of a raw row x (D floats) at the indices i and j of r = (relu(x),
-// relu(-x)): r_i r_j (the half of r is bit D of the index, the component the
-// index mod D).
-template <int D>
-__device__ __forceinline__ float dpfp_pair(const float* x, int i, int j) {
-  const float xi = x[i & (D - 1)], xj = x[j & (D - 1)];
-  return fmaxf((i & D) ? -xi : xi, 0.f) * fmaxf((j & D) ? -xj : xj, 0.f);
-}
-
 // Four DPFP features base + f0 + r (r < 4) of a raw row x from two 16-byte LDS
-// reads: r_i r_{i + order} with i = base + f0 + r (base a multiple of D, f0 of 4,
-// order in 1..3).  A lane's four consecutive elements in one read keep the
-// rows' accesses free of bank conflicts (four-byte reads of a column group
-// across rows collide).  Per call against four-byte reads (same-box A/B):
-// DPFP-1 101.4 -> 96.6 us, DPFP-2 169.5 -> 159.3; DPFP-3, whose slices cycle
-// through three orders, keeps the four-byte reads (233.6 against 249.6).
-template <int D>
-__device__ __forceinline__ void dpfp4(const float* x, int base, int order, int f0, float (&out)[4]) {
+// reads: r_i r_{i + ORD} with i = base + f0 + r (base a multiple of D, f0 of 4,
+// ORD in 1..3).  A lane's four consecutive elements in one read keep the rows'
+// accesses free of bank conflicts (four-byte reads of a column group across
+// rows collide).  Per call against four-byte reads (same-box A/B): DPFP-1
+// 101.4 -> 96.6 us, DPFP-2 169.5 -> 159.3 us.
+template <int D, int ORD>
+__device__ __forceinline__ void dpfp4(const float* x, int base, int f0, float (&out)[4]) {
+  static_assert(ORD >= 1 && ORD <= 3, "partner shift 1..3");
   const float4 a = *reinterpret_cast<const float4*>(x + (f0 & (D - 1)));
   const float4 b = *reinterpret_cast<const float4*>(x + ((f0 + 4) & (D - 1)));
   const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
   const bool negi = ((base + f0) & D) != 0;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const float xi = v[r];
-    const float xj = order == 1 ? v[r + 1] : (order == 2 ? v[r + 2] : v[r + 3]);
-    const bool negj = ((base + f0 + r + order) & D) != 0;
+    const float xi = v[r], xj = v[r + ORD];
+    const bool negj = ((base + f0 + r + ORD) & D) != 0;
     out[r] = fmaxf(negi ? -xi : xi, 0.f) * fmaxf(negj ? -xj : xj, 0.f);
   }
 }
@@ -363,7 +353,10 @@ __global__ __launch_bounds__(NT) void fm_out_kernel(const T* __restrict__ q, con
   // scores (kb <= W) are known at compile time and its accumulators stay in place.
   auto slices = [&](auto wc) {
     constexpr int W = decltype(wc)::value;
-    for (int s = 0; s < NS; ++s) {
+    // One slice s of the features.  ORD is a DPFP slice's partner shift (the
+    // order n of its features r_i r_{i+n}), a constant in each copy of the body.
+    auto slice = [&](const int s, auto oc) {
+      constexpr int ORD = decltype(oc)::value;
       __syncthreads();  // raw rows stored; the previous slice's readers are done
 #pragma unroll
       for (int u = 0; u < PF; ++u) {
@@ -375,23 +368,16 @@ __global__ __launch_bounds__(NT) void fm_out_kernel(const T* __restrict__ q, con
             u32x2{cvt_pk(x[0] - lo_of(h0), x[1] - hi_of(h0)), cvt_pk(x[2] - lo_of(h1), x[3] - hi_of(h1))};
       }
       if (tid < FS) sm.zs[tid] = pz;
-      const int base = (s * FS) & (2 * D - 1), order = (s * FS) / (2 * D) + 1;
+      const int base = (s * FS) & (2 * D - 1);
+      constexpr int order = ORD;
       if (FM != POLY2 && intra_dpfp) {  // the slice's features of the chunk's keys, formed once for all waves
         const int r = tid >> 2, f0 = 16 * (tid & 3);
         const float* krow = sm.Kr + r * XS;
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
           float kv[8], k0[4], k1[4];
-          if constexpr (FM <= 2) {
-            dpfp4<D>(krow, base, order, f0 + 8 * hf, k0);
-            dpfp4<D>(krow, base, order, f0 + 8 * hf + 4, k1);
-          } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              k0[r] = dpfp_pair<D>(krow, base + f0 + 8 * hf + r, base + order + f0 + 8 * hf + r);
-              k1[r] = dpfp_pair<D>(krow, base + f0 + 8 * hf + 4 + r, base + order + f0 + 8 * hf + 4 + r);
-            }
-          }
+          dpfp4<D, order>(krow, base, f0 + 8 * hf, k0);
+          dpfp4<D, order>(krow, base, f0 + 8 * hf + 4, k1);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             kv[r] = k0[r];
@@ -441,11 +427,8 @@ __global__ __launch_bounds__(NT) void fm_out_kernel(const T* __restrict__ q, con
             q4[1] = qa * qb.y;
             q4[2] = qa * qb.z;
             q4[3] = qa * qb.w;
-          } else if constexpr (FM <= 2) {
-            dpfp4<D>(qrow, base, order, f0, q4);
-          } else {  // DPFP-3: the selects over three orders cost more than the conflicts they remove
-#pragma unroll
-            for (int r = 0; r < 4; ++r) q4[r] = dpfp_pair<D>(qrow, base + f0 + r, base + order + f0 + r);
+          } else {
+            dpfp4<D, order>(qrow, base, f0, q4);
           }
           const float4 zf = *reinterpret_cast<const float4*>(&sm.zs[f0]);
           den += q4[0] * zf.x + q4[1] * zf.y + q4[2] * zf.z + q4[3] * zf.w;
@@ -479,6 +462,16 @@ __global__ __launch_bounds__(NT) void fm_out_kernel(const T* __restrict__ q, con
           }
         }
       }
+    };
+    if constexpr (FM == POLY2) {
+      for (int s = 0; s < NS; ++s) slice(s, std::integral_constant<int, 1>{});
+    } else {  // slices in feature order, which groups them by shift: NS / FM per shift
+      constexpr int SPO = NS / FM;
+      for (int hs = 0; hs < SPO; ++hs) slice(hs, std::integral_constant<int, 1>{});
+      if constexpr (FM >= 2)
+        for (int hs = 0; hs < SPO; ++hs) slice(SPO + hs, std::integral_constant<int, 2>{});
+      if constexpr (FM >= 3)
+        for (int hs = 0; hs < SPO; ++hs) slice(2 * SPO + hs, std::integral_constant<int, 3>{});
     }
 
     if (intra_dpfp) {
