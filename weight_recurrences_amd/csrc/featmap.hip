@@ -72,18 +72,6 @@ __device__ __forceinline__ void p2_group(int gi, int& a, int& h) {
   a = gi - 8 * h * (h + 1);
 }
 
-// DPFP feature c of a row x of D floats (in LDS), from its definition.
-template <int FM, int D>
-__device__ __forceinline__ float feature(const float* x, int c) {
-  static_assert(FM >= 1 && FM <= 3, "DPFP-nu");
-  constexpr int R = 2 * D;
-  const int n = c / R + 1, i = c % R, j = (i + n) % R;
-  const float xi = x[i < D ? i : i - D], xj = x[j < D ? j : j - D];
-  const float ri = i < D ? (xi > 0.f ? xi : 0.f) : (xi < 0.f ? -xi : 0.f);
-  const float rj = j < D ? (xj > 0.f ? xj : 0.f) : (xj < 0.f ? -xj : 0.f);
-  return ri * rj;
-}
-
 // Rows [0, nv) of a row-major [.][W] tensor starting at src, widened to float
 // into LDS (row stride DS floats); rows nv..63 become zeros.  The loads carry
 // no condition (rows past nv re-read row nv - 1 and are replaced by zeros): a
@@ -125,6 +113,32 @@ __device__ __forceinline__ void load_rows(float* dst, const T* src, int nv, int 
   }
 }
 
+// Rows [0, nv) of a row-major [.][D] tensor as r = (relu(x), relu(-x)) in LDS
+// (row stride DS >= 2 D floats); rows nv..63 become zeros.  A DPFP feature is
+// then the product r_i r_j of two stored values.  Loads as in load_rows.
+template <typename T, int D, int DS>
+__device__ __forceinline__ void load_relu_rows(float* dst, const T* src, int nv, int tid) {
+  constexpr int G = CH * D / 4;
+  static_assert(G % NT == 0, "whole groups per thread");
+  float4 x[G / NT];
+  if (nv > 0) {
+#pragma unroll
+    for (int u = 0; u < G / NT; ++u) {
+      const int e = (u * NT + tid) * 4, r = e / D, c = e % D;
+      x[u] = load4<T>(src + (size_t)min(r, nv - 1) * D + c);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < G / NT; ++u) {
+    const int e = (u * NT + tid) * 4, r = e / D, c = e % D;
+    const float4 p = r < nv ? x[u] : float4{0.f, 0.f, 0.f, 0.f};
+    *reinterpret_cast<float4*>(dst + r * DS + c) =
+        float4{fmaxf(p.x, 0.f), fmaxf(p.y, 0.f), fmaxf(p.z, 0.f), fmaxf(p.w, 0.f)};
+    *reinterpret_cast<float4*>(dst + r * DS + D + c) =
+        float4{fmaxf(-p.x, 0.f), fmaxf(-p.y, 0.f), fmaxf(-p.z, 0.f), fmaxf(-p.w, 0.f)};
+  }
+}
+
 // Eight floats as a bf16 head and tail (x = h + l to about 2^-17 relative).
 __device__ __forceinline__ void split_bf16x8(const float (&x)[8], bf16x8& h, bf16x8& l) {
   u32x4 hv, lv;
@@ -157,15 +171,17 @@ constexpr int slice_group() {
 }
 
 template <typename T, int D, int M, int FM>
-__global__ __launch_bounds__(NT) void fm_state_kernel(const T* __restrict__ k, const T* __restrict__ v, int N,
+__global__ __launch_bounds__(NT, 2) void fm_state_kernel(const T* __restrict__ k, const T* __restrict__ v, int N,
                                                       int tblk, int nblk, float* __restrict__ agg,
                                                       float* __restrict__ aggz) {
   constexpr int NS = fdim<FM, D>() / FS, SG = slice_group<NS>(), TM = M / 16;
   static_assert(NS % SG == 0, "whole slice groups");
   // Row strides of 16 banks: the four k-slot groups g read four different rows.
-  constexpr int KS = D + 16, VS = M + 16;
-  __shared__ float Kr[CH * KS];
-  __shared__ float Vs[CH * VS];
+  // DPFP keeps r = (relu(k), relu(-k)) per key row (2 D floats), the polynomial
+  // map the raw row.
+  constexpr int KS = (FM == POLY2 ? D : 2 * D) + 16, VS = M + 16;
+  __shared__ __attribute__((aligned(16))) float Kr[CH * KS];
+  __shared__ __attribute__((aligned(16))) float Vs[CH * VS];
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform: its tests are scalar branches
   const int sg = blockIdx.x % (NS / SG), rest = blockIdx.x / (NS / SG), blk = rest % nblk, bh = rest / nblk;
@@ -192,7 +208,11 @@ __global__ __launch_bounds__(NT) void fm_state_kernel(const T* __restrict__ k, c
   for (int c0 = t0; c0 < t1; c0 += CH) {
     const int nv = min(CH, t1 - c0);
     __syncthreads();  // the previous chunk's readers are done
-    load_rows<T, D, KS>(Kr, kh + (size_t)c0 * D, nv, tid);
+    if constexpr (FM == POLY2) {
+      load_rows<T, D, KS>(Kr, kh + (size_t)c0 * D, nv, tid);
+    } else {
+      load_relu_rows<T, D, KS>(Kr, kh + (size_t)c0 * D, nv, tid);
+    }
     load_rows<T, M, VS>(Vs, vh + (size_t)c0 * M, nv, tid);
     __syncthreads();
     // 32-token slabs on bf16 MFMA with head/tail operands (a b = ah bh + ah bl +
@@ -216,8 +236,9 @@ __global__ __launch_bounds__(NT) void fm_state_kernel(const T* __restrict__ k, c
           const float* kr = Kr + (32 * s + 4 * e + g) * KS;
           if constexpr (FM == POLY2) {
             a[e] = pw[j] * kr[pa[j]] * kr[pb[j]];
-          } else {
-            a[e] = feature<FM, D>(kr, (sg * SG + j) * FS + 16 * w + n);
+          } else {  // feature c = r_i r_{(i + n) mod 2D}, i = c mod 2D, n = c / 2D + 1
+            const int c = (sg * SG + j) * FS + 16 * w + n, i = c % (2 * D);
+            a[e] = kr[i] * kr[(i + c / (2 * D) + 1) % (2 * D)];
           }
           zp[j] += a[e];
         }
